@@ -1,0 +1,252 @@
+"""Benchmark of the packed Q4_K dequant-matmul on one MI355X.
+
+Headline (``value``): decode weight GB/s at M = 1 on the Llama-3.2-1B-shaped
+decode pass (16 layers of q, k, v, o, gate, up, down plus the 128256 x 2048
+lm_head, all Q4_K, 695.1 MB of packed weights).  One step is one full pass:
+16 batched launches (one per layer, its seven projections) and one lm_head
+launch, on one stream, with every layer's weights in its own HBM buffers
+(the pass is far larger than the 256 MB last-level cache).  Inputs are seeded
+synthetic data generated on the host and uploaded before timing.
+
+Also reported in the same line:
+  * ``roofline``: the dominant kernel (the per-layer batched decode launch):
+    algorithmic bytes per launch / its average duration, timed with HIP events
+    around every such launch on the launch stream, against 8 TB/s;
+  * ``prefill_m1024``: prefill TFLOP/s on the Qwen3-8B-shaped M = 1024 pass
+    (36 layers, one batched launch per layer) against the 2.5 PFLOP/s dense
+    binary16 matrix-core peak;
+  * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the decode
+    workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-prefill] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+FP16_PEAK_TFLOPS = 2500.0  # MI355X dense binary16 matrix cores, published (2.5 PFLOP/s)
+
+METRIC = "Q4_K DequantMatMul: decode weight GB/s (M=1); prefill TFLOP/s (M=1024)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Pass:
+    """Device-resident inputs of one workload at one M, and its launch list."""
+
+    def __init__(self, wl, M, dev):
+        import torch
+        import q4k_inputs as qi
+        from q4k_inputs.workloads import PROJ_ID, X_ROLE
+        self.wl, self.M = wl, M
+        xs_host = {}
+        for _, (name, N, K) in wl.projections():
+            r = X_ROLE[name]
+            if r not in xs_host:
+                xs_host[r] = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, M, 1000 + r))
+        self.x = {r: torch.from_numpy(v).to(dev) for r, v in xs_host.items()}
+        self.y = {}
+        self.layers = []
+        for li in range(wl.layers):
+            probs = []
+            for name, N, K in wl.layer:
+                w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, li, PROJ_ID[name]))
+                wd = torch.from_numpy(w).to(dev)
+                if name not in self.y:
+                    self.y[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
+                probs.append((wd, self.x[X_ROLE[name]], self.y[name]))
+            self.layers.append(probs)
+        self.head = None
+        if wl.lm_head is not None:
+            name, N, K = wl.lm_head
+            w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, -1, PROJ_ID[name]))
+            self.head = (torch.from_numpy(w).to(dev), self.x[X_ROLE[name]],
+                         torch.empty((M, N), dtype=torch.float32, device=dev))
+        self.weight_bytes = wl.weight_bytes()
+        self.flops = 2 * M * wl.weights()
+        layer_w = sum(N * K // 256 * 144 for _, N, K in wl.layer)
+        layer_x = sum(4 * M * k for k in self._distinct_x_k())
+        layer_y = sum(4 * M * N for _, N, _ in wl.layer)
+        self.layer_bytes = layer_w + layer_x + layer_y
+        self.layer_flops = 2 * M * sum(N * K for _, N, K in wl.layer)
+
+    def _distinct_x_k(self):
+        from q4k_inputs.workloads import X_ROLE
+        seen = {}
+        for name, _, K in self.wl.layer:
+            seen[X_ROLE[name]] = K
+        return list(seen.values())
+
+    def run(self, q4k, layer_events=None):
+        for li, probs in enumerate(self.layers):
+            if layer_events is not None:
+                layer_events[li][0].record()
+            q4k.matmul_batched(probs)
+            if layer_events is not None:
+                layer_events[li][1].record()
+        if self.head is not None:
+            q4k.matmul(*self.head)
+
+
+def time_pass(ps, q4k, steps, warmup):
+    """(ms per step, mean ms of one per-layer batched launch)."""
+    import torch
+    for _ in range(warmup):
+        ps.run(q4k)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        ps.run(q4k)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # Second timed region: HIP events around every per-layer launch.
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in ps.layers] for _ in range(steps)]
+    for s in range(steps):
+        ps.run(q4k, evs[s])
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for step in evs for a, b in step]
+    return ms_step, float(np.mean(per))
+
+
+def check_pass(ps, q4k, ncols=64):
+    """Sampled parity of the last pass's outputs against the oracle (lm_head and last layer)."""
+    import oracle
+    import q4k_inputs as qi
+    from q4k_inputs.workloads import PROJ_ID, X_ROLE
+    tol = 1e-5 if ps.M <= 16 else 2e-3
+    worst = 0.0
+    li = ps.wl.layers - 1
+    for (name, N, K), (_, xd, yd) in zip(ps.wl.layer, ps.layers[li]):
+        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, ps.wl.ident, li, PROJ_ID[name]))
+        cols = np.random.default_rng(N).integers(0, N, ncols)
+        y_ref, s = oracle.matmul_cols(w, xd.cpu().numpy(), N, K, cols)
+        err = np.abs(yd.cpu().numpy()[:, cols] - y_ref) / np.maximum(s, 1e-30)
+        worst = max(worst, float(err.max()))
+    if worst > tol:
+        raise AssertionError(f"bench parity check failed: max err/S {worst} > {tol}")
+    return worst
+
+
+def cpu_baseline(ps, budget_s=12.0):
+    """Oracle (as written, OpenMP over output rows) on a bounded sample of the pass."""
+    import oracle
+    import q4k_inputs as qi
+    from q4k_inputs.workloads import PROJ_ID, X_ROLE
+    threads = len(os.sched_getaffinity(0))
+    used = oracle.threads_used(threads)
+    done_bytes, t_total, items = 0, 0.0, []
+    for li, (name, N, K) in [(0, p) for p in ps.wl.layer] + \
+            ([(-1, ps.wl.lm_head)] if ps.wl.lm_head else []) + \
+            [(l, p) for l in range(1, ps.wl.layers) for p in ps.wl.layer]:
+        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, ps.wl.ident, li, PROJ_ID[name]))
+        x = ps.x[X_ROLE[name]].cpu().numpy()
+        t = time.perf_counter()
+        oracle.matmul(w, x, N, K, threads=used)
+        t_total += time.perf_counter() - t
+        done_bytes += w.nbytes
+        items.append(f"{'lm_head' if li < 0 else f'L{li}.{name}'}")
+        if t_total >= budget_s:
+            break
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{len(items)} of {len(ps.wl.projections())} projections of the same pass "
+                      f"({done_bytes / 1e6:.1f} MB packed weights, M={ps.M}) in {t_total:.1f} s: "
+                      f"{items[0]}..{items[-1]}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gguf_q4_dequant_amd as q4k
+    from q4k_inputs.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    q4k.library()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    wl = WORKLOADS["llama3.2-1b_decode_m1"]
+    t = time.time()
+    ps = Pass(wl, 1, dev)
+    torch.cuda.synchronize()
+    log(f"decode inputs ready ({ps.weight_bytes / 1e6:.1f} MB) in {time.time() - t:.1f} s")
+    ms_step, ms_layer = time_pass(ps, q4k, args.steps, args.warmup)
+    parity = check_pass(ps, q4k)
+    value = ps.weight_bytes / (ms_step * 1e-3) / 1e9
+    achieved = ps.layer_bytes / (ms_layer * 1e-3) / 1e9
+    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.1f} GB/s; layer launch {ms_layer * 1e3:.2f} us "
+        f"-> {achieved:.1f} GB/s; parity max err/S {parity:.2e}")
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": 1, "layers": wl.layers,
+                   "launches": "one batched call per layer (q,k,v,o,gate,up,down) + lm_head",
+                   "weight_bytes": ps.weight_bytes, "parity_max_err_over_S": parity},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode per-layer batched launch",
+                     "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(ps)
+        log(f"cpu baseline: {out['cpu_baseline']}")
+    del ps
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        wl3 = WORKLOADS["qwen3-8b_prefill_m1024"]
+        t = time.time()
+        pp = Pass(wl3, 1024, dev)
+        torch.cuda.synchronize()
+        log(f"prefill inputs ready ({pp.weight_bytes / 1e6:.1f} MB) in {time.time() - t:.1f} s")
+        ms_p, ms_pl = time_pass(pp, q4k, args.prefill_steps, 1)
+        parity_p = check_pass(pp, q4k, ncols=16)
+        tflops = pp.flops / (ms_p * 1e-3) / 1e12
+        ach = pp.layer_flops / (ms_pl * 1e-3) / 1e12
+        out["prefill_m1024"] = {
+            "workload": wl3.name, "value": round(tflops, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_p, 4), "steps": args.prefill_steps, "dtype": "f16 operands, f32 accumulate",
+            "parity_max_err_over_S": parity_p,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prefill per-layer batched launch",
+                         "avg_launch_us": round(ms_pl * 1e3, 2)}}
+        log(f"prefill: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
+            f"-> {ach:.1f} TFLOP/s; parity {parity_p:.2e}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

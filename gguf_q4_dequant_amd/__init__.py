@@ -1,0 +1,178 @@
+"""Python binding of libq4k.so: packed GGUF Q4_K dequant-matmul on MI355X.
+
+Argument marshalling only.  Every step of the product runs in the HIP kernels
+of ``libq4k.so``; PyTorch provides device memory and the current stream.  If
+the library has not been built this module raises on first use: there is no
+CPU fallback.
+
+    y = matmul(w_packed, x)           # w_packed: uint8 [N, K/256*144] on cuda
+                                      # x: float32 [M, K] on cuda -> y [M, N]
+    matmul_batched([(w, x, y), ...])  # one launch per kernel family
+
+Names and semantics mirror include/q4k.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libq4k.so")
+
+BLOCK_WEIGHTS = 256
+BLOCK_BYTES = 144
+MAX_BATCH = 32
+
+OK = 0
+ERR_NULL = -1
+ERR_BAD_DIM = -2
+ERR_LAUNCH = -3
+ERR_ALIGN = -4
+ERR_DEVICE = -5
+ERR_ALLOC = -6
+
+PATH_AUTO = 0
+PATH_DECODE = 1
+PATH_PREFILL = 2
+
+# Exported symbols of libq4k.so, as declared in include/q4k.h.
+EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
+            "q4k_select_path", "q4k_strerror", "q4k_version")
+
+
+class Q4KError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} ({code})" if what else f"{strerror(code)} ({code})")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libq4k.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(f"{LIBRARY_PATH} is missing: build it with "
+                          "`python -m gguf_q4_dequant_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.q4k_matmul.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    lib.q4k_matmul.restype = ci
+    lib.q4k_matmul_path.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+    lib.q4k_matmul_path.restype = ci
+    lib.q4k_matmul_batched.argtypes = [ctypes.POINTER(_Problem), ci, ci, vp]
+    lib.q4k_matmul_batched.restype = ci
+    lib.q4k_matmul_batched_path.argtypes = [ctypes.POINTER(_Problem), ci, ci, ci, vp]
+    lib.q4k_matmul_batched_path.restype = ci
+    lib.q4k_select_path.argtypes = [ci, ci, ci]
+    lib.q4k_select_path.restype = ci
+    lib.q4k_strerror.argtypes = [ci]
+    lib.q4k_strerror.restype = ctypes.c_char_p
+    lib.q4k_version.argtypes = []
+    lib.q4k_version.restype = ci
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return library().q4k_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return library().q4k_version()
+
+
+def select_path(M: int, N: int, K: int) -> int:
+    return library().q4k_select_path(M, N, K)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_operands(w, x, y):
+    import torch
+    if w.dtype != torch.uint8 or x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise TypeError("expected w uint8, x float32, y float32")
+    for name, t in (("w", w), ("x", x), ("y", y)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dim() != 2 or y.dim() != 2:
+        raise ValueError("x must be [M, K] and y [M, N]")
+    M, K = x.shape
+    if y.shape[0] != M:
+        raise ValueError("x and y disagree on M")
+    N = y.shape[1]
+    if K % BLOCK_WEIGHTS != 0:
+        raise Q4KError(ERR_BAD_DIM, f"K={K}")
+    if w.numel() != N * (K // BLOCK_WEIGHTS) * BLOCK_BYTES:
+        raise ValueError(f"w has {w.numel()} bytes, expected N*K/256*144 = "
+                         f"{N * (K // BLOCK_WEIGHTS) * BLOCK_BYTES}")
+    return M, N, K
+
+
+def matmul(w, x, y=None, path: int = PATH_AUTO, stream=None):
+    """y[M, N] = x[M, K] . dequant(w)^T, w packed Q4_K bytes of an [N, K] matrix.
+
+    ``y`` is allocated when not given (N taken from w's leading dimension)."""
+    import torch
+    if y is None:
+        if w.dim() != 2:
+            raise ValueError("pass y, or w shaped [N, K/256*144]")
+        y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.float32, device=x.device)
+    M, N, K = _check_operands(w, x, y)
+    rc = library().q4k_matmul_path(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, int(path),
+                                   _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4k_matmul")
+    return y
+
+
+def matmul_batched(problems: Sequence[Tuple], path: int = PATH_AUTO, stream=None):
+    """Run several (w, x, y) products that share M with one launch per kernel family."""
+    problems = list(problems)
+    if not problems:
+        raise Q4KError(ERR_BAD_DIM, "empty batch")
+    arr = (_Problem * len(problems))()
+    M = None
+    for i, (w, x, y) in enumerate(problems):
+        m, n, k = _check_operands(w, x, y)
+        if M is None:
+            M = m
+        elif m != M:
+            raise ValueError("all problems of a batch share M")
+        arr[i] = _Problem(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
+    rc = library().q4k_matmul_batched_path(arr, len(problems), M, int(path), _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4k_matmul_batched")
+    return [p[2] for p in problems]
+
+
+def raw_matmul(w_ptr: int, x_ptr: int, y_ptr: int, M: int, N: int, K: int,
+               path: int = PATH_AUTO, stream: Optional[int] = None) -> int:
+    """Direct C-ABI call with raw device addresses; returns the status code."""
+    return library().q4k_matmul_path(w_ptr, x_ptr, y_ptr, M, N, K, path, stream)
+
+
+def raw_matmul_batched(items: Iterable[Tuple[int, int, int, int, int]], M: int,
+                       path: int = PATH_AUTO, stream: Optional[int] = None) -> int:
+    """Direct C-ABI batched call; items are (w_ptr, x_ptr, y_ptr, N, K); returns the status."""
+    items = list(items)
+    arr = (_Problem * max(len(items), 1))()
+    for i, (w, x, y, n, k) in enumerate(items):
+        arr[i] = _Problem(w, x, y, n, k)
+    return library().q4k_matmul_batched_path(arr, len(items), M, path, stream)

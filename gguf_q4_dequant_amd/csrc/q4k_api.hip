@@ -1,0 +1,128 @@
+// C ABI of libq4k.so: argument checks, the per-shape policy, and the launches.
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/q4k.h"
+#include "q4k_internal.h"
+
+namespace q4k {
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// Largest M for which the fp32 GEMV family is chosen automatically.  Below the
+// cutover the product is bound by streaming W once; above it the matrix cores
+// are needed.
+constexpr int kDecodeMaxM = 16;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device check: the kernels are built for gfx950 only.  Cached per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 ok, -1 bad
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4K_ERR_DEVICE;
+    int st = g_device_ok[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        st = -1;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+            st = 1;
+        g_device_ok[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? Q4K_OK : Q4K_ERR_DEVICE;
+}
+
+int check_problem(const void *w, const float *x, const float *y, int M, int N, int K) {
+    if (M < 0 || N < 0 || K < 0) return Q4K_ERR_BAD_DIM;
+    if (M == 0 || N == 0) return Q4K_OK;
+    if (K == 0 || K % kBlockWeights != 0) return Q4K_ERR_BAD_DIM;
+    if (!w || !x || !y) return Q4K_ERR_NULL;
+    if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return Q4K_ERR_ALIGN;
+    // Byte counts: int sizes keep N*K/256*144, M*K*4 and M*N*4 well inside 63 bits.
+    return Q4K_OK;
+}
+
+int pick_path(int M) { return M <= kDecodeMaxM ? Q4K_PATH_DECODE : Q4K_PATH_PREFILL; }
+
+int run(const q4k_problem *problems, int count, int M, int path, hipStream_t stream) {
+    if (count < 1 || count > kMaxBatch) return Q4K_ERR_BAD_DIM;
+    if (!problems) return Q4K_ERR_NULL;
+    if (path != Q4K_PATH_AUTO && path != Q4K_PATH_DECODE && path != Q4K_PATH_PREFILL)
+        return Q4K_ERR_BAD_DIM;
+    if (M < 0) return Q4K_ERR_BAD_DIM;
+    Batch b;
+    b.count = 0;
+    b.M = M;
+    for (int i = 0; i < count; ++i) {
+        const q4k_problem &q = problems[i];
+        const int rc = check_problem(q.w_packed, q.x, q.y, M, q.N, q.K);
+        if (rc != Q4K_OK) return rc;
+        if (M == 0 || q.N == 0) continue;  // nothing to compute for this one
+        DevProblem &d = b.p[b.count++];
+        d.w = static_cast<const uint8_t *>(q.w_packed);
+        d.x = q.x;
+        d.y = q.y;
+        d.N = q.N;
+        d.K = q.K;
+        d.tile_begin = 0;
+        d.tiles = 0;
+    }
+    if (b.count == 0) return Q4K_OK;
+    const int dev_rc = check_device();
+    if (dev_rc != Q4K_OK) return dev_rc;
+    if (path == Q4K_PATH_AUTO) path = pick_path(M);
+    const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode(b, stream) : launch_prefill(b, stream);
+    return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace q4k
+
+extern "C" {
+
+int q4k_matmul(const void *w_packed, const float *x, float *y, int M, int N, int K, hipStream_t stream) {
+    const q4k_problem p = {w_packed, x, y, N, K};
+    return q4k::run(&p, 1, M, Q4K_PATH_AUTO, stream);
+}
+
+int q4k_matmul_path(const void *w_packed, const float *x, float *y, int M, int N, int K, int path,
+                    hipStream_t stream) {
+    const q4k_problem p = {w_packed, x, y, N, K};
+    return q4k::run(&p, 1, M, path, stream);
+}
+
+int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_t stream) {
+    return q4k::run(problems, count, M, Q4K_PATH_AUTO, stream);
+}
+
+int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int path, hipStream_t stream) {
+    return q4k::run(problems, count, M, path, stream);
+}
+
+int q4k_select_path(int M, int N, int K) {
+    if (M < 0 || N < 0 || K < 0 || (K % q4k::kBlockWeights) != 0) return Q4K_ERR_BAD_DIM;
+    return q4k::pick_path(M);
+}
+
+const char *q4k_strerror(int status) {
+    switch (status) {
+    case Q4K_OK: return "success";
+    case Q4K_ERR_NULL: return "null pointer argument";
+    case Q4K_ERR_BAD_DIM: return "invalid dimension, batch count or path";
+    case Q4K_ERR_LAUNCH: return "kernel launch failed";
+    case Q4K_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case Q4K_ERR_DEVICE: return "no usable gfx950 device";
+    case Q4K_ERR_ALLOC: return "device workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int q4k_version(void) { return q4k::kVersion; }
+
+}  // extern "C"

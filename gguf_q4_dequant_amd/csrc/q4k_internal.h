@@ -1,0 +1,38 @@
+// Internal declarations shared by the C-ABI layer and the kernel files of
+// libq4k.so.  Not installed; the public interface is include/q4k.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+constexpr int kBlockWeights = 256;  // weights per Q4_K super-block
+constexpr int kBlockBytes = 144;    // bytes per Q4_K super-block
+constexpr int kMaxBatch = 32;
+
+// One product of a launch.  tile_begin is the first workgroup index (along
+// grid x) that belongs to this problem; problems are laid out back to back.
+struct DevProblem {
+    const uint8_t *w;
+    const float *x;
+    float *y;
+    int N;
+    int K;
+    int tile_begin;
+    int tiles;
+};
+
+// Passed by value in the kernel-argument segment (well under its 4 KiB limit).
+struct Batch {
+    DevProblem p[kMaxBatch];
+    int count;
+    int M;
+};
+
+// Enqueue the GEMV family / the matrix-core family for every problem of `b`.
+// Return hipSuccess or the launch error.
+hipError_t launch_decode(Batch &b, hipStream_t stream);
+hipError_t launch_prefill(Batch &b, hipStream_t stream);
+
+}  // namespace q4k

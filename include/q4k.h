@@ -1,0 +1,111 @@
+/*
+ * q4k.h -- C ABI of the packed GGUF Q4_K dequant-matmul library (libq4k.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the DequantMatMul that the rlx-qwen3 crate page ("Quick
+ * start") describes: K-quant weight tensors stay packed in device memory and
+ * every matmul over them dequantizes on the fly.  Here
+ *
+ *     y[m, n] = sum_k x[m, k] * w[n, k],   w = dequant(W),   m < M, n < N, k < K
+ *
+ * with W an [N, K] matrix of GGUF Q4_K super-blocks: 256 weights in 144 bytes
+ * (binary16 d and dmin, twelve bytes of 6-bit scales and mins for eight
+ * 32-weight sub-blocks, 128 bytes of 4-bit quants), K/256 consecutive blocks
+ * per row of W, rows back to back; weight w = d*sc_j*q - dmin*m_j.
+ *
+ * Conventions for every entry point:
+ *   - w_packed, x and y are DEVICE pointers on the current HIP device; the
+ *     caller allocates and owns them and the library keeps none of them after
+ *     the call returns.  W is only read, never written.  y must not overlap x
+ *     or W.  x is float32 [M, K] row-major, y is float32 [M, N] row-major and
+ *     is overwritten (no accumulation into existing contents).
+ *   - w_packed, x and y must be 16-byte aligned (the kernels use 16-byte loads).
+ *   - The call enqueues kernels on `stream` (0 = the null stream) and returns
+ *     without synchronizing the host.  Faults inside a kernel surface at the
+ *     caller's next synchronization.
+ *   - M == 0 or N == 0 is a successful no-op.  K must be a positive multiple
+ *     of 256 whenever M and N are positive.
+ *   - Return value: Q4K_OK or a negative Q4K_ERR_* code; on error nothing is
+ *     enqueued.  The integer codes follow the convention of the
+ *     nx_f32_llm_run_v3 source page (0 success, -1 null pointer, -2 bad
+ *     dimension, -3 failure while running the forward), extended with -4..-6.
+ *   - Calls are thread-safe; calls on different streams may run concurrently.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own declaration in hip_runtime_api.h. */
+typedef struct ihipStream_t *hipStream_t;
+
+#define Q4K_BLOCK_WEIGHTS 256
+#define Q4K_BLOCK_BYTES 144
+#define Q4K_MAX_BATCH 32
+
+enum q4k_status {
+    Q4K_OK = 0,
+    Q4K_ERR_NULL = -1,    /* a required pointer is NULL */
+    Q4K_ERR_BAD_DIM = -2, /* M, N or K negative; K not a positive multiple of 256;
+                             batch count outside [1, Q4K_MAX_BATCH]; sizes whose byte
+                             counts overflow 63 bits; unknown path */
+    Q4K_ERR_LAUNCH = -3,  /* the HIP runtime rejected a kernel launch */
+    Q4K_ERR_ALIGN = -4,   /* w_packed, x or y not 16-byte aligned */
+    Q4K_ERR_DEVICE = -5,  /* no usable HIP device, or not a gfx950 device */
+    Q4K_ERR_ALLOC = -6    /* the library could not allocate its device workspace */
+};
+
+/* y = x . dequant(W)^T for one packed weight matrix.
+ * M tokens (rows of x), N output features (rows of W), K input features. */
+int q4k_matmul(const void *w_packed, const float *x, float *y, int M, int N, int K,
+               hipStream_t stream);
+
+/* One problem of a batched call. */
+typedef struct q4k_problem {
+    const void *w_packed; /* device, [N, K/256*144] bytes */
+    const float *x;       /* device, [M, K] */
+    float *y;             /* device, [M, N] */
+    int N;
+    int K;
+} q4k_problem;
+
+/* `count` independent products that share M, run by one launch per kernel
+ * family (for example the q, k, v, o, gate, up and down projections of one
+ * layer).  `problems` is a HOST array that is only read during the call.
+ * Problems may share x; no y may overlap any x, W or another y. */
+int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_t stream);
+
+/* Kernel-family selection for tests and benchmarks. */
+enum q4k_path {
+    Q4K_PATH_AUTO = 0,    /* the library's per-shape policy */
+    Q4K_PATH_DECODE = 1,  /* GEMV family: fp32 arithmetic, meant for M <= 16 */
+    Q4K_PATH_PREFILL = 2  /* matrix-core family: binary16 operands, fp32 accumulation */
+};
+
+/* As q4k_matmul / q4k_matmul_batched with an explicit kernel family.  The
+ * decode family accepts any M; its cost grows with M. */
+int q4k_matmul_path(const void *w_packed, const float *x, float *y, int M, int N, int K,
+                    int path, hipStream_t stream);
+int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int path,
+                            hipStream_t stream);
+
+/* The family Q4K_PATH_AUTO picks for a shape (Q4K_PATH_DECODE or
+ * Q4K_PATH_PREFILL), or a negative error code for an invalid shape. */
+int q4k_select_path(int M, int N, int K);
+
+/* Static text for a status code (never NULL). */
+const char *q4k_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int q4k_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

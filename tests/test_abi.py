@@ -1,0 +1,84 @@
+"""The C-ABI library loads and exports what include/q4k.h declares (no GPU needed).
+
+Only calls that return before touching a device are made here: the status
+strings, the version, the path policy and the argument checks, which reject
+bad arguments before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_q4_dequant_amd as q4k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4k.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q4k_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4k.LIBRARY_PATH):
+        from gguf_q4_dequant_amd import build
+        build.build()
+    return q4k.library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("q4k_matmul", "q4k_matmul_batched", "q4k_strerror"):
+        assert required in names
+    assert set(names) == set(q4k.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert q4k.strerror(code) and q4k.strerror(code) != "unknown status"
+    assert q4k.strerror(-99) == "unknown status"
+    assert q4k.version() >= 100
+
+
+def test_path_policy(lib):
+    assert q4k.select_path(1, 4096, 4096) == q4k.PATH_DECODE
+    assert q4k.select_path(16, 4096, 4096) == q4k.PATH_DECODE
+    assert q4k.select_path(32, 4096, 4096) == q4k.PATH_PREFILL
+    assert q4k.select_path(1024, 4096, 4096) == q4k.PATH_PREFILL
+    assert q4k.select_path(1, 4096, 100) == q4k.ERR_BAD_DIM
+    assert q4k.select_path(-1, 1, 256) == q4k.ERR_BAD_DIM
+
+
+def test_argument_errors_before_any_device_call(lib):
+    A = 1 << 20  # an aligned, never dereferenced stand-in address
+    assert q4k.raw_matmul(A, A, A, -1, 4, 256) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(A, A, A, 1, -4, 256) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(A, A, A, 1, 4, 300) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(A, A, A, 1, 4, 0) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(0, A, A, 1, 4, 256) == q4k.ERR_NULL
+    assert q4k.raw_matmul(A, 0, A, 1, 4, 256) == q4k.ERR_NULL
+    assert q4k.raw_matmul(A, A, 0, 1, 4, 256) == q4k.ERR_NULL
+    assert q4k.raw_matmul(A + 4, A, A, 1, 4, 256) == q4k.ERR_ALIGN
+    assert q4k.raw_matmul(A, A + 8, A, 1, 4, 256) == q4k.ERR_ALIGN
+    assert q4k.raw_matmul(A, A, A + 4, 1, 4, 256) == q4k.ERR_ALIGN
+    assert q4k.raw_matmul(A, A, A, 1, 4, 256, path=7) == q4k.ERR_BAD_DIM
+    # empty products are successful no-ops, even with NULL pointers
+    assert q4k.raw_matmul(0, 0, 0, 0, 4, 256) == q4k.OK
+    assert q4k.raw_matmul(0, 0, 0, 3, 0, 256) == q4k.OK
+    # batch count outside [1, 32]
+    assert q4k.raw_matmul_batched([], 1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul_batched([(A, A, A, 4, 256)] * 33, 1) == q4k.ERR_BAD_DIM
+    # one bad problem rejects the whole batch
+    assert q4k.raw_matmul_batched([(A, A, A, 4, 256), (A, A, A, 4, 100)], 1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul_batched([(0, 0, 0, 0, 256)] * 3, 1) == q4k.OK
+    assert lib.q4k_matmul_batched(None, 1, 1, None) == q4k.ERR_NULL

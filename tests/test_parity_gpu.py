@@ -1,0 +1,165 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Same seeded inputs on both sides.  The fp32 GEMV family must meet
+|y - y_ref| <= 1e-5 * sum|x*w|, the binary16 matrix-core family 2e-3 * sum|x*w|
+(and 2e-5 against the oracle's binary16-operand product).  In the exact regime
+(q4k_inputs.exact_q4k / exact_x) every summation order is exact, so both
+families must equal the oracle bit for bit; one-hot activations must return
+the f32 weight (GEMV) or its binary16 rounding (matrix cores) bit for bit.
+"""
+import numpy as np
+import pytest
+
+import gguf_q4_dequant_amd as q4k
+import oracle
+import q4k_inputs as qi
+from tests.gpu_helpers import (DECODE_TOL, PREFILL_F16_TOL, PREFILL_TOL, check_close, device,
+                               to_dev)
+
+pytestmark = pytest.mark.gpu
+
+DEC, PRE = q4k.PATH_DECODE, q4k.PATH_PREFILL
+
+
+def _run(w, x, N, path):
+    import torch
+    y = q4k.matmul(to_dev(w), to_dev(x), torch.empty((x.shape[0], N), dtype=torch.float32,
+                                                     device=device()), path=path)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _inputs(M, N, K, tag):
+    w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 500, M, N, K, tag))
+    x = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 501, M, N, K, tag))
+    return w, x
+
+
+# Shapes span several workgroup tiles and ragged tails in N, M and K/256.
+DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 130, 5120),
+                 (2, 64, 768), (3, 129, 1280), (4, 200, 3072), (5, 63, 2048), (8, 96, 4096),
+                 (9, 70, 512), (16, 100, 5120), (16, 33, 8192), (1, 40, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+def test_decode_family_matches_oracle(M, N, K):
+    w, x = _inputs(M, N, K, 1)
+    y = _run(w, x, N, DEC)
+    y_ref, s = oracle.matmul(w, x, N, K)
+    check_close(y, y_ref, s, DECODE_TOL, f"decode M={M} N={N} K={K}")
+
+
+PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
+                  (17, 45, 1280), (1, 128, 1024), (256, 129, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
+def test_prefill_family_matches_oracle(M, N, K):
+    w, x = _inputs(M, N, K, 2)
+    y = _run(w, x, N, PRE)
+    y_ref, s = oracle.matmul(w, x, N, K)
+    check_close(y, y_ref, s, PREFILL_TOL, f"prefill M={M} N={N} K={K}")
+    y16, s16 = oracle.matmul_cols(w, x, N, K, np.arange(N), fp16_operands=True)
+    check_close(y, y16, s16, PREFILL_F16_TOL, f"prefill vs f16-operand oracle M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("M,N,K", [(1, 77, 2048), (5, 64, 1024), (40, 150, 768)])
+def test_exact_regime_is_bitwise(path, M, N, K):
+    w = qi.exact_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 600, M, N, K))
+    x = qi.exact_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 601, M, N, K))
+    y = _run(w, x, N, path)
+    y_ref, _ = oracle.matmul(w, x, N, K)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_one_hot_returns_weights(path):
+    N, K = 70, 1024
+    w, _ = _inputs(1, N, K, 3)
+    ks = [0, 1, 31, 32, 33, 63, 64, 100, 255, 256, 511, 700, 1023]
+    x = qi.one_hot_x(len(ks), K, ks)
+    y = _run(w, x, N, path)
+    wf = oracle.dequant(w, K)
+    want = wf[:, ks].T
+    if path == PRE:
+        want = want.astype(np.float16).astype(np.float32)  # binary16 operands, nearest-even
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_golden_blocks_through_gpu(golden_blocks, path):
+    """Closed-form weights of the hand-built blocks come back through the kernels."""
+    rows = np.stack([g.raw for g in golden_blocks])  # N = 5 rows, K = 256
+    ks = list(range(0, 256, 7)) + [255]
+    x = qi.one_hot_x(len(ks), 256, ks)
+    y = _run(rows, x, len(golden_blocks), path)
+    for n, g in enumerate(golden_blocks):
+        want = g.weights_f32()[ks]
+        if path == PRE:
+            want = want.astype(np.float16).astype(np.float32)
+        assert np.array_equal(y[:, n], want), g.name
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_row_split_invariance(path):
+    """An M-row call equals calls on 5+1+3 row chunks (nx runner's mixed-chunk gates)."""
+    M, N, K = 9, 140, 1536
+    w, x = _inputs(M, N, K, 4)
+    y = _run(w, x, N, path)
+    parts = [_run(w, x[a:b], N, path) for a, b in ((0, 5), (5, 6), (6, 9))]
+    assert np.array_equal(np.concatenate(parts), y)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_linearity_determinism_and_weights_untouched(path):
+    import torch
+    M, N, K = 6 if path == DEC else 48, 190, 2048
+    w, x = _inputs(M, N, K, 5)
+    wd, xd = to_dev(w), to_dev(x)
+    y1 = q4k.matmul(wd, xd, path=path)
+    y2 = q4k.matmul(wd, xd, path=path)
+    y3 = q4k.matmul(wd, 2 * xd, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y3, 2 * y1)
+    assert np.array_equal(wd.cpu().numpy(), w)  # W is never written
+
+
+@pytest.mark.parametrize("M", [1, 4, 48])
+def test_batched_equals_single_calls(M):
+    import torch
+    shapes = [(300, 1024), (64, 1024), (64, 1024), (256, 768), (700, 1024), (700, 1024), (1024, 2816)]
+    xs = {K: to_dev(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 700, M, K)))
+          for K in {k for _, k in shapes}}
+    probs = []
+    for i, (N, K) in enumerate(shapes):
+        w = to_dev(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 701, M, i)))
+        probs.append((w, xs[K], torch.empty((M, N), dtype=torch.float32, device=device())))
+    q4k.matmul_batched(probs)
+    singles = [q4k.matmul(w, x) for w, x, _ in probs]
+    torch.cuda.synchronize()
+    for (w, x, y), ys in zip(probs, singles):
+        assert torch.equal(y, ys)
+    # spot-check the batch against the oracle
+    w0 = probs[-1][0].cpu().numpy()
+    x0 = probs[-1][1].cpu().numpy()
+    y_ref, s = oracle.matmul_cols(w0, x0, 1024, 2816, np.arange(0, 1024, 37))
+    tol = DECODE_TOL if M <= 16 else PREFILL_TOL
+    check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
+
+
+def test_empty_shapes_and_misaligned_pointers_leave_y_untouched():
+    import torch
+    dev = device()
+    y = torch.full((3, 0), 7.0, device=dev)
+    q4k.matmul(torch.zeros((0, 144), dtype=torch.uint8, device=dev), torch.zeros((3, 256), device=dev), y)
+    y = torch.full((0, 5), 7.0, device=dev)
+    q4k.matmul(torch.zeros((5, 144), dtype=torch.uint8, device=dev), torch.zeros((0, 256), device=dev), y)
+    w = to_dev(qi.random_q4k(5, 256, 1))
+    x = torch.ones((2, 256), device=dev)
+    y = torch.full((2, 5), 7.0, device=dev)
+    assert q4k.raw_matmul(w.data_ptr() + 4, x.data_ptr(), y.data_ptr(), 2, 5, 256) == q4k.ERR_ALIGN
+    assert q4k.raw_matmul(w.data_ptr(), x.data_ptr(), y.data_ptr(), 2, 5, 200) == q4k.ERR_BAD_DIM
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
