@@ -2,7 +2,9 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/q4k.h"
 #include "q4k_internal.h"
@@ -48,6 +50,70 @@ int check_problem(const void *w, const float *x, const float *y, int M, int N, i
     return Q4K_OK;
 }
 
+// ---- library workspace: per (device, stream) -------------------------------
+struct Buffer {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+struct Scratch {
+    Buffer counters;  // zero outside kernels
+    Buffer partials;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Scratch> g_ws;
+
+// Grow `b` to at least `bytes`; a new buffer is zero-filled when `zero` is set.
+hipError_t grow(Buffer &b, size_t bytes, bool zero, hipStream_t stream) {
+    if (b.bytes >= bytes) return hipSuccess;
+    hipError_t err;
+    if (b.ptr) {
+        // kernels queued on this stream may still use the old buffer
+        err = hipStreamSynchronize(stream);
+        if (err != hipSuccess) return err;
+        (void)hipFree(b.ptr);
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    const size_t want = (bytes + 0xFFFF) & ~static_cast<size_t>(0xFFFF);
+    err = hipMalloc(&b.ptr, want);
+    if (err != hipSuccess) {
+        b.ptr = nullptr;
+        return err;
+    }
+    if (zero) {
+        err = hipMemsetAsync(b.ptr, 0, want, stream);
+        if (err != hipSuccess) return err;
+    }
+    b.bytes = want;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t workspace(hipStream_t stream, size_t counter_bytes, size_t partial_bytes,
+                     unsigned **counters, float **partials) {
+    *counters = nullptr;
+    *partials = nullptr;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Scratch &s = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    if (counter_bytes) {
+        err = grow(s.counters, counter_bytes, true, stream);
+        if (err != hipSuccess) return err;
+        *counters = static_cast<unsigned *>(s.counters.ptr);
+    }
+    if (partial_bytes) {
+        err = grow(s.partials, partial_bytes, false, stream);
+        if (err != hipSuccess) return err;
+        *partials = static_cast<float *>(s.partials.ptr);
+    }
+    return hipSuccess;
+}
+
+namespace {
+
 int pick_path(int M) { return M <= kDecodeMaxM ? Q4K_PATH_DECODE : Q4K_PATH_PREFILL; }
 
 int run(const q4k_problem *problems, int count, int M, int path, hipStream_t stream) {
@@ -70,14 +136,19 @@ int run(const q4k_problem *problems, int count, int M, int path, hipStream_t str
         d.y = q.y;
         d.N = q.N;
         d.K = q.K;
+        d.part = nullptr;
+        d.cnt = nullptr;
         d.tile_begin = 0;
         d.tiles = 0;
+        d.splits = 1;
+        d.pad_ = 0;
     }
     if (b.count == 0) return Q4K_OK;
     const int dev_rc = check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
     if (path == Q4K_PATH_AUTO) path = pick_path(M);
     const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode(b, stream) : launch_prefill(b, stream);
+    if (err == hipErrorOutOfMemory || err == hipErrorMemoryAllocation) return Q4K_ERR_ALLOC;
     return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
 }
 

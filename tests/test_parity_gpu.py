@@ -101,14 +101,25 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
         assert np.array_equal(y[:, n], want), g.name
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
-def test_row_split_invariance(path):
-    """An M-row call equals calls on 5+1+3 row chunks (nx runner's mixed-chunk gates)."""
-    M, N, K = 9, 140, 1536
+@pytest.mark.parametrize("path,M,cuts,bitwise", [
+    (DEC, 4, (2, 3), True),       # every chunk runs the same K split: identical bits
+    (DEC, 9, (5, 6), False),      # 8-row tiles use shorter K chunks: equal within tolerance
+    (PRE, 9, (5, 6), True),
+    (PRE, 200, (130, 131), True),
+])
+def test_row_split_invariance(path, M, cuts, bitwise):
+    """An M-row call equals calls on row chunks (the nx runner's mixed-chunk gates)."""
+    N, K = 140, 1536
     w, x = _inputs(M, N, K, 4)
     y = _run(w, x, N, path)
-    parts = [_run(w, x[a:b], N, path) for a, b in ((0, 5), (5, 6), (6, 9))]
-    assert np.array_equal(np.concatenate(parts), y)
+    bounds = (0,) + cuts + (M,)
+    parts = np.concatenate([_run(w, x[a:b], N, path) for a, b in zip(bounds[:-1], bounds[1:])])
+    if bitwise:
+        assert np.array_equal(parts, y)
+    else:
+        y_ref, s = oracle.matmul(w, x, N, K)
+        check_close(parts, y_ref, s, DECODE_TOL, "row chunks")
+        check_close(y, y_ref, s, DECODE_TOL, "all rows")
 
 
 @pytest.mark.parametrize("path", [DEC, PRE])
@@ -147,6 +158,29 @@ def test_batched_equals_single_calls(M):
     y_ref, s = oracle.matmul_cols(w0, x0, 1024, 2816, np.arange(0, 1024, 37))
     tol = DECODE_TOL if M <= 16 else PREFILL_TOL
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
+
+
+def test_split_k_workspace_reuse_across_layouts():
+    """Consecutive calls whose K-splits lay out the library workspace differently.
+
+    Regression: counters of one call must never start on bytes another call used
+    for partial sums."""
+    import torch
+    seq = [[(300, 8192)], [(700, 5120)] * 5 + [(64, 17408)], [(129, 3072), (64, 1280)], [(300, 8192)]]
+    for M in (1, 3):
+        for si, shapes in enumerate(seq):
+            hosts, probs = [], []
+            for i, (N, K) in enumerate(shapes):
+                w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 800, M, si, i))
+                x = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 801, M, si, i))
+                hosts.append((w, x, N, K))
+                probs.append((to_dev(w), to_dev(x), torch.empty((M, N), dtype=torch.float32, device=device())))
+            q4k.matmul_batched(probs, path=DEC)
+            torch.cuda.synchronize()
+            for (w, x, N, K), (_, _, y) in zip(hosts, probs):
+                cols = np.arange(0, N, 7)
+                y_ref, s = oracle.matmul_cols(w, x, N, K, cols)
+                check_close(y.cpu().numpy()[:, cols], y_ref, s, DECODE_TOL, f"seq {si} M={M} N={N} K={K}")
 
 
 def test_empty_shapes_and_misaligned_pointers_leave_y_untouched():
