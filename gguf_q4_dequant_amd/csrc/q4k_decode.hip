@@ -158,22 +158,59 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
     const int nc = min(n, N - 1);  // rows past N load row N-1 and store nothing
     const uint8_t *wrow = W + (static_cast<size_t>(nc) * KB + b_begin) * kBlockBytes;
 
-    // 1. Issue every weight load of this lane.
-    Block blk[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j)
-        if (wave + kWaves * j < nb) load_block(blk[j], wrow + static_cast<size_t>(wave + kWaves * j) * kBlockBytes);
-
-    // 2. Stage this chunk of x and its sub-block sums in LDS.
+    // 1. Load this chunk of x first (the LDS barrier below waits for it alone),
+    //    then issue every weight load of this lane.
     const int xs_stride = kChunk * 256;
     const int nf4 = nb * 64;  // float4s per activation row in the chunk
-    for (int f = tid; f < mt * nf4; f += kThreads) {
+    constexpr int kXPer = (MT * kChunk * 64 + kThreads - 1) / kThreads;
+    static_assert(kXPer <= 8, "x staging holds at most 8 float4 per thread");
+    // The x loads sit in their own basic block so that the scheduler keeps
+    // them ahead of the weight loads (nb >= 1 always holds): the LDS stores
+    // below then wait for x alone while the weights stay in flight.  Slots past
+    // the chunk re-read a valid float4 and are not stored.
+    float4 xv0, xv1, xv2, xv3, xv4, xv5, xv6, xv7;
+    auto xload = [&](int j) {
+        const int f = min(tid + j * kThreads, mt * nf4 - 1);
         const int m = f / nf4;
         const int r = f - m * nf4;
-        const float4 v = reinterpret_cast<const float4 *>(
+        return reinterpret_cast<const float4 *>(
             X + static_cast<size_t>(m0 + m) * K + static_cast<size_t>(b_begin) * 256)[r];
-        reinterpret_cast<float4 *>(xs + m * xs_stride)[r] = v;
+    };
+    if (nb > 0) {
+        xv0 = xload(0);
+        if constexpr (kXPer > 1) xv1 = xload(1);
+        if constexpr (kXPer > 2) xv2 = xload(2);
+        if constexpr (kXPer > 3) xv3 = xload(3);
+        if constexpr (kXPer > 4) xv4 = xload(4);
+        if constexpr (kXPer > 5) xv5 = xload(5);
+        if constexpr (kXPer > 6) xv6 = xload(6);
+        if constexpr (kXPer > 7) xv7 = xload(7);
     }
+    Block blk[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        // waves without a j-th block re-load their first one (unused)
+        const int bl = wave + kWaves * j < nb ? wave + kWaves * j : wave;
+        load_block(blk[j], wrow + static_cast<size_t>(bl) * kBlockBytes);
+    }
+
+    // 2. Stage x and its sub-block sums in LDS.
+    auto xstore = [&](int j, const float4 &v) {
+        const int f = tid + j * kThreads;
+        if (f < mt * nf4) {
+            const int m = f / nf4;
+            const int r = f - m * nf4;
+            reinterpret_cast<float4 *>(xs + m * xs_stride)[r] = v;
+        }
+    };
+    xstore(0, xv0);
+    if constexpr (kXPer > 1) xstore(1, xv1);
+    if constexpr (kXPer > 2) xstore(2, xv2);
+    if constexpr (kXPer > 3) xstore(3, xv3);
+    if constexpr (kXPer > 4) xstore(4, xv4);
+    if constexpr (kXPer > 5) xstore(5, xv5);
+    if constexpr (kXPer > 6) xstore(6, xv6);
+    if constexpr (kXPer > 7) xstore(7, xv7);
     __syncthreads();
     const int xsum_stride = kChunk * 8;
     for (int e = tid; e < mt * nb * 8; e += kThreads) {
@@ -297,8 +334,12 @@ hipError_t launch_mt(Batch &b, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef Q4K_DECODE_BPW1
+#define Q4K_DECODE_BPW1 1  // blocks per wave for a single activation row
+#endif
+
 hipError_t launch_decode(Batch &b, hipStream_t stream) {
-    if (b.M <= 1) return launch_mt<1, 2>(b, stream);
+    if (b.M <= 1) return launch_mt<1, Q4K_DECODE_BPW1>(b, stream);
     if (b.M <= 2) return launch_mt<2, 2>(b, stream);
     if (b.M <= 4) return launch_mt<4, 2>(b, stream);
     return launch_mt<8, 1>(b, stream);
