@@ -1,20 +1,21 @@
 // Decode family: GEMV-style Q4_K dequant-matmul for few tokens, fp32
 // arithmetic throughout (the path the benchmark's M = 1 decode pass takes).
 //
-// Work item.  A workgroup of four 64-lane waves owns 64 consecutive rows of W
-// (one row per lane, the same rows in every wave) and a chunk of at most
-// 4*BPW consecutive super-blocks of those rows; wave w takes blocks w, w+4, ...
-// of the chunk.  Every lane issues the loads of all its blocks (BPW x 144
-// bytes) before anything else, so a workgroup has its whole chunk in flight at
-// once.  Rows whose K spans several chunks are split across workgroups so that
-// every workgroup streams about the same number of bytes: each writes a
-// partial sum, and the last one to arrive (an atomic counter per output tile)
-// adds the partials in chunk order, so results do not depend on scheduling.
+// Work item ("tile").  A workgroup of four 64-lane waves owns 32 consecutive
+// rows of W and a chunk of at most 8*BPL consecutive super-blocks of those
+// rows.  Eight lanes share a row: lane s of a row takes blocks s, s+8, ... of
+// the chunk, so the eight lanes of a row read 8*144 contiguous bytes per block
+// step and every lane has all its loads (BPL x 144 bytes) in flight at once.
+// The eight partial dot products of a row meet through cross-lane shuffles.
+// Rows whose K spans several chunks are split across workgroups: each writes
+// its partial sums to the library workspace and a second, small kernel adds
+// them in chunk order, so results do not depend on scheduling and no
+// workgroup waits on another.
 //
-// Activations.  All lanes of a wave work on the same block at the same time,
-// so the x values they need are wave-uniform.  The workgroup stages its chunk
-// of x in LDS (coalesced) and reads it back with broadcast loads, together
-// with the 32-element sums X[m, j] of every sub-block j.
+// Activations.  The workgroup stages its chunk of x in LDS (each block padded
+// by four floats so that the eight blocks a wave reads at once sit in
+// different banks), and with it the 32-element sums X[m, j] of every
+// sub-block j, reduced across lanes while staging.
 //
 // Arithmetic (weight w = d*sc_j*q - dmin*m_j on sub-block j):
 //   y[m,n] = sum_j ( d*sc_j * sum_{l in j} x[m,l]*q[l]  -  dmin*m_j * X[m,j] ).
@@ -28,9 +29,12 @@
 namespace q4k {
 namespace {
 
-constexpr int kRows = 64;   // rows of W per workgroup (one per lane)
-constexpr int kWaves = 4;   // waves per workgroup
-constexpr int kThreads = kRows * kWaves;
+constexpr int kWaves = 4;                   // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLanesPerRow = 8;             // lanes sharing one row of W
+constexpr int kRowsPerWave = 64 / kLanesPerRow;
+constexpr int kRows = kRowsPerWave * kWaves;  // rows of W per workgroup
+constexpr int kXBlockStride = 256 + 4;      // floats per staged x block (padded: conflict-free reads)
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
@@ -76,6 +80,12 @@ __device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int
     c[4] = dmin * byte0(mnB); c[5] = dmin * byte1(mnB);
     c[6] = dmin * byte2(mnB); c[7] = dmin * byte3(mnB);
 
+    // The nibble masks come from an opaque scalar move: with the constants in
+    // view the compiler narrows each byte to a 4-bit field extract and loses
+    // the single-instruction byte converts (v_cvt_f32_ubyte1..3).
+    uint32_t lo_mask, hi_mask;
+    asm("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(lo_mask));
+    asm("s_mov_b32 %0, 0xf0f0f0f0" : "=s"(hi_mask));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // 32 quant bytes of group i: low nibbles -> sub-block 2i (x[64i + l]),
@@ -86,8 +96,8 @@ __device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int
         float ql[32], qh[32];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const uint32_t lo = qd[u] & 0x0F0F0F0Fu;
-            const uint32_t hi = qd[u] & 0xF0F0F0F0u;
+            const uint32_t lo = qd[u] & lo_mask;
+            const uint32_t hi = qd[u] & hi_mask;
             ql[4 * u + 0] = byte0(lo); ql[4 * u + 1] = byte1(lo);
             ql[4 * u + 2] = byte2(lo); ql[4 * u + 3] = byte3(lo);
             qh[4 * u + 0] = byte0(hi); qh[4 * u + 1] = byte1(hi);
@@ -123,14 +133,13 @@ __device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int
     }
 }
 
-// MT activation rows per workgroup, BPW blocks per wave (chunk = 4*BPW blocks).
-template <int MT, int BPW>
+// MT activation rows per workgroup, BPL blocks per lane (chunk = 8*BPL blocks).
+template <int MT, int BPL>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
-    constexpr int kChunk = kWaves * BPW;
-    __shared__ __attribute__((aligned(16))) float xs[MT * kChunk * 256];
+    constexpr int kChunk = kLanesPerRow * BPL;
+    constexpr int kXsRow = kChunk * kXBlockStride;  // floats per staged activation row
+    __shared__ __attribute__((aligned(16))) float xs[MT * kXsRow];
     __shared__ float xsum[MT * kChunk * 8];
-    __shared__ float red[kWaves * MT * kRows];
-    __shared__ int is_last;
 
     int p = 0;
     for (int i = 1; i < bt.count; ++i)
@@ -153,80 +162,49 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = rg * kRows + lane;
+    const int wave = tid >> 6;
+    const int s = lane % kLanesPerRow;  // block stream within the row
+    const int n = rg * kRows + wave * kRowsPerWave + lane / kLanesPerRow;
     const int nc = min(n, N - 1);  // rows past N load row N-1 and store nothing
     const uint8_t *wrow = W + (static_cast<size_t>(nc) * KB + b_begin) * kBlockBytes;
 
-    // 1. Load this chunk of x first (the LDS barrier below waits for it alone),
-    //    then issue every weight load of this lane.
-    const int xs_stride = kChunk * 256;
+    // 1. Issue every load of this tile: the lane's blocks, then its share of x.
+    Block blk[BPL];
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+        // lanes without a j-th block re-load their first one (unused)
+        const int bl = s + kLanesPerRow * j < nb ? s + kLanesPerRow * j : (s < nb ? s : 0);
+        load_block(blk[j], wrow + static_cast<size_t>(bl) * kBlockBytes);
+    }
+    constexpr int kXPer = (MT * kChunk * 64 + kThreads - 1) / kThreads;  // float4s per thread
     const int nf4 = nb * 64;  // float4s per activation row in the chunk
-    constexpr int kXPer = (MT * kChunk * 64 + kThreads - 1) / kThreads;
-    static_assert(kXPer <= 8, "x staging holds at most 8 float4 per thread");
-    // The x loads sit in their own basic block so that the scheduler keeps
-    // them ahead of the weight loads (nb >= 1 always holds): the LDS stores
-    // below then wait for x alone while the weights stay in flight.  Slots past
-    // the chunk re-read a valid float4 and are not stored.
-    float4 xv0, xv1, xv2, xv3, xv4, xv5, xv6, xv7;
-    auto xload = [&](int j) {
+    float4 xv[kXPer];
+#pragma unroll
+    for (int j = 0; j < kXPer; ++j) {
+        // slots past the chunk re-read a valid float4 and are not stored
         const int f = min(tid + j * kThreads, mt * nf4 - 1);
         const int m = f / nf4;
         const int r = f - m * nf4;
-        return reinterpret_cast<const float4 *>(
+        xv[j] = reinterpret_cast<const float4 *>(
             X + static_cast<size_t>(m0 + m) * K + static_cast<size_t>(b_begin) * 256)[r];
-    };
-    if (nb > 0) {
-        xv0 = xload(0);
-        if constexpr (kXPer > 1) xv1 = xload(1);
-        if constexpr (kXPer > 2) xv2 = xload(2);
-        if constexpr (kXPer > 3) xv3 = xload(3);
-        if constexpr (kXPer > 4) xv4 = xload(4);
-        if constexpr (kXPer > 5) xv5 = xload(5);
-        if constexpr (kXPer > 6) xv6 = xload(6);
-        if constexpr (kXPer > 7) xv7 = xload(7);
-    }
-    Block blk[BPW];
-#pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        // waves without a j-th block re-load their first one (unused)
-        const int bl = wave + kWaves * j < nb ? wave + kWaves * j : wave;
-        load_block(blk[j], wrow + static_cast<size_t>(bl) * kBlockBytes);
     }
 
-    // 2. Stage x and its sub-block sums in LDS.
-    auto xstore = [&](int j, const float4 &v) {
-        const int f = tid + j * kThreads;
-        if (f < mt * nf4) {
-            const int m = f / nf4;
-            const int r = f - m * nf4;
-            reinterpret_cast<float4 *>(xs + m * xs_stride)[r] = v;
-        }
-    };
-    xstore(0, xv0);
-    if constexpr (kXPer > 1) xstore(1, xv1);
-    if constexpr (kXPer > 2) xstore(2, xv2);
-    if constexpr (kXPer > 3) xstore(3, xv3);
-    if constexpr (kXPer > 4) xstore(4, xv4);
-    if constexpr (kXPer > 5) xstore(5, xv5);
-    if constexpr (kXPer > 6) xstore(6, xv6);
-    if constexpr (kXPer > 7) xstore(7, xv7);
-    __syncthreads();
-    const int xsum_stride = kChunk * 8;
-    for (int e = tid; e < mt * nb * 8; e += kThreads) {
-        const int m = e / (nb * 8);
-        const int sb = e - m * nb * 8;
-        const float4 *src = reinterpret_cast<const float4 *>(xs + m * xs_stride + sb * 32);
-        float s = 0.f;
+    // 2. Stage x and the sub-block sums (8 consecutive float4 = one sub-block,
+    //    held by 8 consecutive lanes, summed with shuffles).
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const float4 t = src[v];
-            s += t.x;
-            s += t.y;
-            s += t.z;
-            s += t.w;
+    for (int j = 0; j < kXPer; ++j) {
+        const int f = tid + j * kThreads;
+        const int m = f / nf4;
+        const int r = f - m * nf4;
+        float t = (xv[j].x + xv[j].y) + (xv[j].z + xv[j].w);
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        if (f < mt * nf4) {
+            const int bl = r >> 6;
+            *reinterpret_cast<float4 *>(xs + m * kXsRow + bl * kXBlockStride + 4 * (r & 63)) = xv[j];
+            if ((r & 7) == 0) xsum[m * kChunk * 8 + (r >> 3)] = t;
         }
-        xsum[m * xsum_stride + sb] = s;
     }
     __syncthreads();
 
@@ -235,114 +213,96 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) yacc[m] = 0.f;
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int bl = wave + kWaves * j;
-        if (bl < nb) block_dot<MT>(blk[j], xs + bl * 256, xs_stride, xsum + bl * 8, xsum_stride, mt, yacc);
+    for (int j = 0; j < BPL; ++j) {
+        const int bl = s + kLanesPerRow * j;
+        if (bl < nb) block_dot<MT>(blk[j], xs + bl * kXBlockStride, kXsRow, xsum + bl * 8, kChunk * 8, mt, yacc);
     }
 
-    // 4. Combine the four waves, then the chunks.
+    // 4. Sum the row's eight lanes; write y, or this chunk's partial sums.
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[(wave * MT + m) * kRows + lane] = yacc[m];
-    __syncthreads();
-    if (splits == 1) {
-        if (wave == 0 && n < N) {
-            for (int m = 0; m < mt; ++m) {
-                float s = red[(0 * MT + m) * kRows + lane];
-                s += red[(1 * MT + m) * kRows + lane];
-                s += red[(2 * MT + m) * kRows + lane];
-                s += red[(3 * MT + m) * kRows + lane];
-                P.y[static_cast<size_t>(m0 + m) * N + n] = s;
-            }
-        }
-        return;
+    for (int m = 0; m < MT; ++m) {
+        float t = yacc[m];
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        yacc[m] = t;
     }
-    // K split across workgroups.  No cache-maintenance fences: partial sums
-    // travel through device-scope atomics, which every XCD performs at the
-    // same memory-side point, and each wave waits for its atomics to complete
-    // before the workgroup bumps the arrival counter.  The last workgroup to
-    // arrive reads the partials back with atomics and adds them in chunk
-    // order, so the result does not depend on arrival order.
-    if (wave == 0 && n < N) {
-        for (int m = 0; m < mt; ++m) {
-            float s = red[(0 * MT + m) * kRows + lane];
-            s += red[(1 * MT + m) * kRows + lane];
-            s += red[(2 * MT + m) * kRows + lane];
-            s += red[(3 * MT + m) * kRows + lane];
-            __hip_atomic_exchange(P.part + (static_cast<size_t>(sidx) * M + m0 + m) * N + n, s,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    unsigned *counter = P.cnt + rg * gridDim.y + blockIdx.y;
-    if (tid == 0)
-        is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  static_cast<unsigned>(splits - 1);
-    __syncthreads();
-    if (!is_last) return;
-    if (wave == 0 && n < N) {
-        for (int m = 0; m < mt; ++m) {
-            float s = 0.f;
-            for (int c = 0; c < splits; ++c)
-                s += __hip_atomic_fetch_add(P.part + (static_cast<size_t>(c) * M + m0 + m) * N + n, 0.f,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            P.y[static_cast<size_t>(m0 + m) * N + n] = s;
-        }
-    }
-    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s != 0 || n >= N) return;
+    float *dst = splits == 1 ? P.y : P.part + static_cast<size_t>(sidx) * M * N;
+    for (int m = 0; m < mt; ++m) dst[static_cast<size_t>(m0 + m) * N + n] = yacc[m];
 }
 
-template <int MT, int BPW>
+// y = sum over chunks of the partial sums, in chunk order, for split problems.
+// One thread per output element; problems laid out back to back in grid x.
+__global__ __launch_bounds__(256) void split_reduce_kernel(Batch bt) {
+    int p = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
+    const DevProblem &P = bt.p[p];
+    const size_t e = static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x;
+    const size_t total = static_cast<size_t>(bt.M) * P.N;
+    if (e >= total) return;
+    float acc = P.part[e];
+    for (int c = 1; c < P.splits; ++c) acc += P.part[static_cast<size_t>(c) * total + e];
+    P.y[e] = acc;
+}
+
+template <int MT, int BPL>
 hipError_t launch_mt(Batch &b, hipStream_t stream) {
-    constexpr int kChunk = kWaves * BPW;
+    constexpr int kChunk = kLanesPerRow * BPL;
     const int m_tiles = (b.M + MT - 1) / MT;
-    // Workspace: one counter per output tile and the partial sums of split problems.
-    size_t n_cnt = 0, n_part = 0;
+    size_t n_part = 0;
     int tiles = 0;
+    Batch red;
+    red.count = 0;
+    red.M = b.M;
+    int red_tiles = 0;
     for (int i = 0; i < b.count; ++i) {
         DevProblem &d = b.p[i];
         const int KB = d.K / kBlockWeights;
-        const int rgs = (d.N + kRows - 1) / kRows;
         d.splits = (KB + kChunk - 1) / kChunk;
         d.tile_begin = tiles;
-        d.tiles = rgs * d.splits;
+        d.tiles = (d.N + kRows - 1) / kRows * d.splits;
         tiles += d.tiles;
-        if (d.splits > 1) {
-            n_cnt += static_cast<size_t>(rgs) * m_tiles;
-            n_part += static_cast<size_t>(d.splits) * b.M * d.N;
-        }
+        if (d.splits > 1) n_part += static_cast<size_t>(d.splits) * b.M * d.N;
     }
     if (n_part) {
-        unsigned *cnt = nullptr;
+        unsigned *unused = nullptr;
         float *part = nullptr;
-        hipError_t err = workspace(stream, n_cnt * sizeof(unsigned), n_part * sizeof(float), &cnt, &part);
+        hipError_t err = workspace(stream, 0, n_part * sizeof(float), &unused, &part);
         if (err != hipSuccess) return err;
         for (int i = 0; i < b.count; ++i) {
             DevProblem &d = b.p[i];
-            if (d.splits > 1) {
-                d.cnt = cnt;
-                d.part = part;
-                cnt += static_cast<size_t>((d.N + kRows - 1) / kRows) * m_tiles;
-                part += static_cast<size_t>(d.splits) * b.M * d.N;
-            }
+            if (d.splits == 1) continue;
+            d.part = part;
+            part += static_cast<size_t>(d.splits) * b.M * d.N;
+            DevProblem &r = red.p[red.count++];
+            r = d;
+            r.tile_begin = red_tiles;
+            r.tiles = static_cast<int>((static_cast<size_t>(b.M) * d.N + 255) / 256);
+            red_tiles += r.tiles;
         }
     }
-    dim3 grid(tiles, m_tiles);
-    hipLaunchKernelGGL((decode_kernel<MT, BPW>), grid, dim3(kThreads), 0, stream, b);
+    hipLaunchKernelGGL((decode_kernel<MT, BPL>), dim3(tiles, m_tiles), dim3(kThreads), 0, stream, b);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || red.count == 0) return err;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(red_tiles), dim3(256), 0, stream, red);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#ifndef Q4K_DECODE_BPW1
-#define Q4K_DECODE_BPW1 1  // blocks per wave for a single activation row
+// Blocks per lane.  Every activation-tile height uses the same value, so the
+// K split (and with it the summation order) of a row does not depend on M.
+#ifndef Q4K_DECODE_BPL
+#define Q4K_DECODE_BPL 1
 #endif
 
 hipError_t launch_decode(Batch &b, hipStream_t stream) {
-    if (b.M <= 1) return launch_mt<1, Q4K_DECODE_BPW1>(b, stream);
-    if (b.M <= 2) return launch_mt<2, 2>(b, stream);
-    if (b.M <= 4) return launch_mt<4, 2>(b, stream);
-    return launch_mt<8, 1>(b, stream);
+    if (b.M <= 1) return launch_mt<1, Q4K_DECODE_BPL>(b, stream);
+    if (b.M <= 2) return launch_mt<2, Q4K_DECODE_BPL>(b, stream);
+    if (b.M <= 4) return launch_mt<4, Q4K_DECODE_BPL>(b, stream);
+    return launch_mt<8, Q4K_DECODE_BPL>(b, stream);
 }
 
 }  // namespace q4k
