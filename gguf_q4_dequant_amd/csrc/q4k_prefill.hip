@@ -1,172 +1,376 @@
 // Prefill family: Q4_K dequant-matmul on the gfx950 matrix cores for many
-// tokens (M >= 32).  Each k-step dequantizes a tile of W to binary16 in LDS
-// (w = d*sc_j*q - dmin*m_j in fp32, then one round-to-nearest-even to
-// binary16), stages the matching tile of x as binary16 (round to nearest
-// even), and feeds v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// tokens (M >= 32).
 //
-// Tile: 128 rows of x by 128 rows of W per workgroup, 64 k per step (one
-// 32-byte quant group of a super-block, i.e. two 32-weight sub-blocks); four
-// waves in a 2x2 grid, each owning a 64x64 output tile (4x4 MFMA tiles).
+//   1. x (fp32) is rounded once to binary16 (nearest even) into the library
+//      workspace by a small pre-pass (each distinct x of a batch once).
+//   2. The GEMM streams 256x64 tiles of x (binary16) and of W into
+//      double-buffered LDS.  W tiles are dequantized on the way in: every
+//      weight is w = d*sc_j*q - dmin*m_j evaluated in fp32 (exact products, one
+//      rounding) and then rounded once to binary16 (nearest even).
+//   3. v_mfma_f32_32x32x16_f16 multiplies them with fp32 accumulation: eight
+//      waves (two per SIMD, so that one wave's matrix-core work hides the
+//      other's loads and dequantization), each owning a 128x64 block of the
+//      256x256 output tile in the accumulation registers.
+// While the matrix cores work on k-step s, the waves already load k-step s+1
+// into registers; after the MFMAs they store it (x as is, W dequantized) into
+// the other LDS buffer.
+//
+// Tile order: workgroup i runs on XCD i % 8, so consecutive tiles are dealt
+// out XCD by XCD: each XCD receives a contiguous run of tiles in which the
+// N tiles of one M tile (same rows of x) are adjacent and share that XCD's L2.
 #include "q4k_internal.h"
 
 namespace q4k {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kLdsStride = kBK + 8;  // halves per LDS row (144 bytes: conflict-free 16-byte reads)
-constexpr int kThreads = 256;
+constexpr int kBM = 256;  // rows of x per tile
+constexpr int kBN = 256;  // rows of W per tile
+constexpr int kBK = 64;   // k per step: one 32-byte quant group = two sub-blocks
+constexpr int kThreads = 512;
+constexpr int kXcds = 8;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_kernel(Batch bt) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[kBM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[kBN * kLdsStride];
+// ---- pre-pass: x (fp32) -> binary16, nearest even --------------------------
+struct CvtSeg {
+    const float *src;
+    _Float16 *dst;
+    size_t n4;      // float4 count
+    int blk_begin;  // first workgroup of this segment
+};
+struct CvtBatch {
+    CvtSeg s[kMaxBatch];
+    int count;
+};
+
+__global__ __launch_bounds__(256) void convert_x_kernel(CvtBatch cb) {
+    int p = 0;
+    for (int i = 1; i < cb.count; ++i)
+        if (static_cast<int>(blockIdx.x) >= cb.s[i].blk_begin) p = i;
+    const CvtSeg &S = cb.s[p];
+    const size_t base = static_cast<size_t>(static_cast<int>(blockIdx.x) - S.blk_begin) * 256 * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const size_t i = base + threadIdx.x + 256 * j;
+        if (i < S.n4) {
+            const float4 v = reinterpret_cast<const float4 *>(S.src)[i];
+            const half2v lo = {(_Float16)v.x, (_Float16)v.y};
+            const half2v hi = {(_Float16)v.z, (_Float16)v.w};
+            uint2 o;
+            o.x = __builtin_bit_cast(uint32_t, lo);
+            o.y = __builtin_bit_cast(uint32_t, hi);
+            reinterpret_cast<uint2 *>(S.dst)[i] = o;
+        }
+    }
+}
+
+// ---- the GEMM --------------------------------------------------------------
+// Problem p reads binary16 activations from xh[p] (rows of K halves).
+struct GemmArgs {
+    const _Float16 *xh[kMaxBatch];
+    // Tiles [xcd_first[c], xcd_first[c+1]) run on XCD c (workgroups c, c+8, ...).
+    int xcd_first[kXcds + 1];
+};
+
+// Decoded scales of one block for one row (this thread's row of the W tile).
+struct RowScales {
+    float d, dmin;
+    uint32_t scA, scB, mnA, mnB;  // sc0..3, sc4..7, m0..3, m4..7: one 6-bit field per byte
+};
+
+__device__ __forceinline__ void decode_header(const uint4 &hd, RowScales &r) {
+    r.d = half_bits_to_float(hd.x & 0xFFFFu);
+    r.dmin = half_bits_to_float(hd.x >> 16);
+    r.scA = hd.y & 0x3F3F3F3Fu;
+    r.mnA = hd.z & 0x3F3F3F3Fu;
+    r.scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    r.mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+}
+
+__device__ __forceinline__ float byte_f(uint32_t v, int e) { return static_cast<float>((v >> (8 * e)) & 0xFFu); }
+
+// f32 weight -> binary16 with two separate roundings (f32, then nearest-even
+// binary16).  The empty asm keeps the compiler from fusing the FMA and the
+// conversion into one mixed-precision FMA, which would round only once.
+__device__ __forceinline__ float opaque(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// LDS tiles hold 256 rows of 64 halves (128 bytes = 8 chunks of 16 bytes) with
+// no padding; chunk c of row r sits in slot c ^ ((r >> 1) & 7).  Sixteen
+// lanes reading chunk c of 16 consecutive rows then touch 16 distinct
+// (row parity, slot) pairs, i.e. all 64 banks once.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(Batch bt, GemmArgs ga) {
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];  // 16-byte slots
+    constexpr int kTileSlots = 256 * 8;  // one 256x64 binary16 tile
+    // buffer b: x tile at lds4 + 2*b*kTileSlots, W tile right after it
+    auto As = [&](int b) { return lds4 + 2 * b * kTileSlots; };
+    auto Bs = [&](int b) { return lds4 + (2 * b + 1) * kTileSlots; };
+
+    // Workgroup i is dispatched to XCD i % 8; each XCD walks its own range of
+    // tiles (the host balances the ranges by work), so that tiles sharing an
+    // x tile or a W tile meet in the same L2.
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+    const int tile = ga.xcd_first[xcd] + static_cast<int>(blockIdx.x) / kXcds;
+    if (tile >= ga.xcd_first[xcd + 1]) return;
 
     int p = 0;
     for (int i = 1; i < bt.count; ++i)
-        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
-    const uint8_t *__restrict__ W = bt.p[p].w;
-    const float *__restrict__ X = bt.p[p].x;
-    float *__restrict__ Y = bt.p[p].y;
-    const int N = bt.p[p].N;
-    const int K = bt.p[p].K;
+        if (tile >= bt.p[i].tile_begin) p = i;
+    const DevProblem &P = bt.p[p];
+    const _Float16 *__restrict__ XH = ga.xh[p];
+    const uint8_t *__restrict__ W = P.w;
+    const int N = P.N;
+    const int K = P.K;
     const int M = bt.M;
     const int KB = K >> 8;
+    const int local = tile - P.tile_begin;
+    // N tiles of one M tile are adjacent: an XCD keeps its x tile in L2 while
+    // it walks along W.
     const int n_tiles = (N + kBN - 1) / kBN;
-    const int local = static_cast<int>(blockIdx.x) - bt.p[p].tile_begin;
-    const int tn0 = (local % n_tiles) * kBN;
     const int tm0 = (local / n_tiles) * kBM;
+    const int tn0 = (local % n_tiles) * kBN;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
 
-    // Loader roles: thread t stages row t/2 (of x and of W), half t%2 of the k-step.
-    const int lr = t >> 1, lh = t & 1;
-    const int xrow = min(tm0 + lr, M - 1);
-    const int wrow_i = min(tn0 + lr, N - 1);
-    const float *xsrc = X + static_cast<size_t>(xrow) * K + 32 * lh;
-    const uint8_t *wsrc = W + static_cast<size_t>(wrow_i) * KB * kBlockBytes;
+    // Loader: thread t moves 16-byte chunks f = t + 512*j (j < 4) of the
+    // 256x64 binary16 x tile (row f/8, chunk f%8; rows past M re-read row M-1,
+    // whose results are never stored), and dequantizes quant chunk t%2 of row
+    // t/2 of the W tile (16 quant bytes: 16 weights of each of the two
+    // sub-blocks of this k-step).
+    const _Float16 *xcol = XH + 8 * (t & 7);
+    const int xr0 = tm0 + (t >> 3);
+    auto x_chunk = [&](int j, int s) {
+        const size_t row = static_cast<size_t>(min(xr0 + 64 * j, M - 1));
+        return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
+    };
+    const int wr = t >> 1, wh = t & 1;
+    const uint8_t *wrow = W + static_cast<size_t>(min(tn0 + wr, N - 1)) * KB * kBlockBytes;
 
-    float4v acc[4][4];
+    const int steps = KB * 4;
+    uint32_t lo_mask, hi_mask;
+    asm("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(lo_mask));
+    asm("s_mov_b32 %0, 0xf0f0f0f0" : "=s"(hi_mask));
+    // Raw data of the next step, loaded while the current one runs on the
+    // matrix cores (named registers: arrays of these end up in scratch).
+    uint4 x0, x1, x2, x3, wq, whd;
+    RowScales rs;
+    auto load_stage = [&](int s) {
+        x0 = x_chunk(0, s);
+        x1 = x_chunk(1, s);
+        x2 = x_chunk(2, s);
+        x3 = x_chunk(3, s);
+        const int kb = s >> 2, g = s & 3;
+        const uint8_t *blk = wrow + static_cast<size_t>(kb) * kBlockBytes;
+        whd = *reinterpret_cast<const uint4 *>(blk);  // used when g == 0
+        wq = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * g + 16 * wh);
+    };
+    auto store_stage = [&](int s, uint4 *A, uint4 *B) {
+        A[swz((t >> 3) + 0, t & 7)] = x0;
+        A[swz((t >> 3) + 64, t & 7)] = x1;
+        A[swz((t >> 3) + 128, t & 7)] = x2;
+        A[swz((t >> 3) + 192, t & 7)] = x3;
+        const int g = s & 3;
+        if (g == 0) decode_header(whd, rs);
+        // sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles, k 32..63);
+        // quant byte l of the group -> k = l and k = 32 + l
+        const uint32_t scw = g < 2 ? rs.scA : rs.scB;
+        const uint32_t mnw = g < 2 ? rs.mnA : rs.mnB;
+        const int sh = (g & 1) * 16;
+        const float a_lo = rs.d * static_cast<float>((scw >> sh) & 0xFFu);
+        const float a_hi = rs.d * 0.0625f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
+        const float c_lo = rs.dmin * static_cast<float>((mnw >> sh) & 0xFFu);
+        const float c_hi = rs.dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
+        auto two_chunks = [&](uint32_t w0, uint32_t w1, int v) {
+            half8 lo, hi;
+            const uint32_t l0 = w0 & lo_mask, h0 = w0 & hi_mask, l1 = w1 & lo_mask, h1 = w1 & hi_mask;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = (_Float16)opaque(__builtin_fmaf(a_lo, byte_f(l0, e), -c_lo));
+                hi[e] = (_Float16)opaque(__builtin_fmaf(a_hi, byte_f(h0, e), -c_hi));
+                lo[4 + e] = (_Float16)opaque(__builtin_fmaf(a_lo, byte_f(l1, e), -c_lo));
+                hi[4 + e] = (_Float16)opaque(__builtin_fmaf(a_hi, byte_f(h1, e), -c_hi));
+            }
+            B[swz(wr, v)] = __builtin_bit_cast(uint4, lo);
+            B[swz(wr, 4 + v)] = __builtin_bit_cast(uint4, hi);
+        };
+        two_chunks(wq.x, wq.y, 2 * wh);
+        two_chunks(wq.z, wq.w, 2 * wh + 1);
+    };
+
+    float16v acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    for (int kb = 0; kb < KB; ++kb) {
-        const uint8_t *blk = wsrc + static_cast<size_t>(kb) * kBlockBytes;
-        const uint4 hd = *reinterpret_cast<const uint4 *>(blk);
-        const float d = half_bits_to_float(hd.x & 0xFFFFu);
-        const float dmin = half_bits_to_float(hd.x >> 16);
-        const uint32_t scA = hd.y & 0x3F3F3F3Fu;
-        const uint32_t mnA = hd.z & 0x3F3F3F3Fu;
-        const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
-        const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
-#pragma unroll 1
-        for (int g = 0; g < 4; ++g) {
-            // ---- stage x (f32 -> binary16) ----
-            const float4 *xs4 = reinterpret_cast<const float4 *>(xsrc + static_cast<size_t>(kb) * 256 + 64 * g);
-            half8 xh[4];
+    auto mma_step = [&](const uint4 *A, const uint4 *B) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float4 u0 = xs4[2 * v], u1 = xs4[2 * v + 1];
-                xh[v] = half8{(_Float16)u0.x, (_Float16)u0.y, (_Float16)u0.z, (_Float16)u0.w,
-                              (_Float16)u1.x, (_Float16)u1.y, (_Float16)u1.z, (_Float16)u1.w};
-            }
-            // ---- stage W (dequantize to binary16) ----
-            // sub-blocks 2g (low nibbles) and 2g+1 (high nibbles) of this block
-            const uint32_t scw = g < 2 ? scA : scB;
-            const uint32_t mnw = g < 2 ? mnA : mnB;
-            const int sh = (g & 1) * 16;
-            const float a_lo = d * static_cast<float>((scw >> sh) & 0xFFu);
-            const float a_hi = d * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
-            const float c_lo = dmin * static_cast<float>((mnw >> sh) & 0xFFu);
-            const float c_hi = dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
-            const uint4 qq = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * g + 16 * lh);
-            const uint32_t qd[4] = {qq.x, qq.y, qq.z, qq.w};
-            half8 wl[2], wh[2];
+        for (int kk = 0; kk < kBK / 8; kk += 2) {  // 16 k per MFMA = 2 chunks
+            half8 af[4], bf[2];
+            const int c = kk + (lane >> 5);
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                _Float16 lo[8], hi[8];
+            for (int a = 0; a < 4; ++a)
+                af[a] = __builtin_bit_cast(half8, A[swz(128 * wm + 32 * a + (lane & 31), c)]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t byte = (qd[2 * v + e / 4] >> (8 * (e & 3))) & 0xFFu;
-                    lo[e] = (_Float16)__builtin_fmaf(a_lo, static_cast<float>(byte & 15u), -c_lo);
-                    hi[e] = (_Float16)__builtin_fmaf(a_hi, static_cast<float>(byte >> 4), -c_hi);
-                }
-                wl[v] = half8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
-                wh[v] = half8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
-            }
-            __syncthreads();  // previous step's MFMA reads are done
-            {
-                half8 *ad = reinterpret_cast<half8 *>(As + lr * kLdsStride + 32 * lh);
+            for (int b = 0; b < 2; ++b)
+                bf[b] = __builtin_bit_cast(half8, B[swz(64 * wn + 32 * b + (lane & 31), c)]);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) ad[v] = xh[v];
-                // quant byte l of the group -> k = l (low nibble) and k = 32 + l (high nibble)
-                half8 *bl = reinterpret_cast<half8 *>(Bs + lr * kLdsStride + 16 * lh);
-                bl[0] = wl[0];
-                bl[1] = wl[1];
-                half8 *bh = reinterpret_cast<half8 *>(Bs + lr * kLdsStride + 32 + 16 * lh);
-                bh[0] = wh[0];
-                bh[1] = wh[1];
-            }
-            __syncthreads();
-            // ---- MFMA ----
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int kk = 0; kk < kBK; kk += 32) {
-                half8 af[4], bf[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    af[a] = *reinterpret_cast<const half8 *>(
-                        As + (64 * wm + 16 * a + (lane & 15)) * kLdsStride + kk + 8 * (lane >> 4));
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    bf[b] = *reinterpret_cast<const half8 *>(
-                        Bs + (64 * wn + 16 * b + (lane & 15)) * kLdsStride + kk + 8 * (lane >> 4));
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-            }
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
         }
+    };
+
+    // Pipeline: LDS buffer s%2 holds step s; the registers hold step s+1,
+    // loaded while step s runs on the matrix cores.
+    load_stage(0);
+    store_stage(0, As(0), Bs(0));
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < steps) load_stage(s + 1);
+        mma_step(As(cur), Bs(cur));
+        if (s + 1 < steps) store_stage(s + 1, As(cur ^ 1), Bs(cur ^ 1));
+        __syncthreads();
     }
 
-    // D layout of a 16x16 MFMA tile: lane l, register r -> row 4*(l/16)+r, column l%16.
+    // D layout of a 32x32 MFMA tile: lane l, register r ->
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int n = tn0 + 64 * wn + 16 * b + (lane & 15);
+        for (int b = 0; b < 2; ++b) {
+            const int n = tn0 + 64 * wn + 32 * b + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = tm0 + 64 * wm + 16 * a + 4 * (lane >> 4) + r;
-                if (m < M && n < N) Y[static_cast<size_t>(m) * N + n] = acc[a][b][r];
+            for (int r = 0; r < 16; ++r) {
+                const int m = tm0 + 128 * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) P.y[static_cast<size_t>(m) * N + n] = acc[a][b][r];
             }
         }
     }
 }
 
+constexpr size_t kLdsBytes = 4 * 256 * 8 * 16;  // two buffers of x and W tiles, 32 KiB each
+
 }  // namespace
 
 hipError_t launch_prefill(Batch &b, hipStream_t stream) {
+    static bool attr_set = false;  // per process; the attribute is a property of the function
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    // Distinct activations, their binary16 copies in the workspace.
+    const float *xs[kMaxBatch];
+    size_t offs[kMaxBatch];
+    int nx = 0;
+    size_t halves = 0;
+    int which[kMaxBatch];
+    for (int i = 0; i < b.count; ++i) {
+        int k = 0;
+        while (k < nx && !(xs[k] == b.p[i].x)) ++k;
+        if (k == nx) {
+            xs[nx] = b.p[i].x;
+            offs[nx] = halves;
+            halves += (static_cast<size_t>(b.M) * b.p[i].K + 127) & ~static_cast<size_t>(127);
+            ++nx;
+        }
+        which[i] = k;
+    }
+    unsigned *unused = nullptr;
+    float *wsp = nullptr;
+    hipError_t err = workspace(stream, 0, halves * sizeof(_Float16), &unused, &wsp);
+    if (err != hipSuccess) return err;
+    _Float16 *xh_base = reinterpret_cast<_Float16 *>(wsp);
+
+    CvtBatch cb;
+    cb.count = 0;
+    int cblocks = 0;
+    for (int k = 0; k < nx; ++k) {
+        int kk = 0;
+        while (b.p[kk].x != xs[k]) ++kk;
+        CvtSeg &sg = cb.s[cb.count++];
+        sg.src = xs[k];
+        sg.dst = xh_base + offs[k];
+        sg.n4 = static_cast<size_t>(b.M) * b.p[kk].K / 4;
+        sg.blk_begin = cblocks;
+        cblocks += static_cast<int>((sg.n4 + 1023) / 1024);
+    }
+    hipLaunchKernelGGL(convert_x_kernel, dim3(cblocks), dim3(256), 0, stream, cb);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    // Tile space: problems in order of decreasing K (the longest tiles start
+    // first), each problem's tiles back to back, N tiles of one M tile
+    // adjacent.  The kernel looks a tile's problem up by tile_begin, so the
+    // launch gets its own copy of the batch in that order.
+    Batch sb;
+    sb.count = b.count;
+    sb.M = b.M;
+    GemmArgs ga;
+    int order[kMaxBatch];
+    for (int i = 0; i < b.count; ++i) order[i] = i;
+    for (int i = 1; i < b.count; ++i)  // stable insertion sort by K, descending
+        for (int j = i; j > 0 && b.p[order[j]].K > b.p[order[j - 1]].K; --j) {
+            const int o = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = o;
+        }
     int tiles = 0;
+    long long work = 0;  // in 256-deep k blocks
     const int m_tiles = (b.M + kBM - 1) / kBM;
     for (int i = 0; i < b.count; ++i) {
-        b.p[i].tile_begin = tiles;
-        b.p[i].tiles = ((b.p[i].N + kBN - 1) / kBN) * m_tiles;
-        tiles += b.p[i].tiles;
+        sb.p[i] = b.p[order[i]];
+        ga.xh[i] = xh_base + offs[which[order[i]]];
+        sb.p[i].tile_begin = tiles;
+        sb.p[i].tiles = ((sb.p[i].N + kBN - 1) / kBN) * m_tiles;
+        tiles += sb.p[i].tiles;
+        work += static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights);
     }
-    hipLaunchKernelGGL(prefill_kernel, dim3(tiles), dim3(kThreads), 0, stream, b);
+    // Cut the tile space into eight ranges of about equal work.
+    ga.xcd_first[0] = 0;
+    {
+        int i = 0;
+        long long done = 0;  // work of tiles before sb.p[i].tile_begin
+        for (int c = 1; c < kXcds; ++c) {
+            const long long goal = (work * c + kXcds / 2) / kXcds;
+            while (i < sb.count && done + static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights) <= goal) {
+                done += static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights);
+                ++i;
+            }
+            int cut = tiles;
+            if (i < sb.count) {
+                const long long per = sb.p[i].K / kBlockWeights;
+                cut = sb.p[i].tile_begin + static_cast<int>((goal - done + per / 2) / per);
+            }
+            ga.xcd_first[c] = max(cut, ga.xcd_first[c - 1]);
+        }
+        ga.xcd_first[kXcds] = tiles;
+    }
+    int longest = 0;
+    for (int c = 0; c < kXcds; ++c) longest = max(longest, ga.xcd_first[c + 1] - ga.xcd_first[c]);
+    const int grid = longest * kXcds;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kThreads), kLdsBytes, stream, sb, ga);
     return hipGetLastError();
 }
 
