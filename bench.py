@@ -5,13 +5,16 @@ decode pass (16 layers of q, k, v, o, gate, up, down plus the 128256 x 2048
 lm_head, all Q4_K, 695.1 MB of packed weights).  One step is one full pass:
 16 batched launches (one per layer, its seven projections) and one lm_head
 launch, on one stream, with every layer's weights in its own HBM buffers
-(the pass is far larger than the 256 MB last-level cache).  Inputs are seeded
-synthetic data generated on the host and uploaded before timing.
+(the pass is far larger than the 256 MB last-level cache).  The pass is
+captured once in a HIP graph and replayed, so the host's per-call Python work
+does not pace the GPU; every replay runs all 17 launches in full.  Inputs are
+seeded synthetic data generated on the host and uploaded before timing.
 
 Also reported in the same line:
   * ``roofline``: the dominant kernel (the per-layer batched decode launch):
     algorithmic bytes per launch / its average duration, timed with HIP events
-    around every such launch on the launch stream, against 8 TB/s;
+    around every such launch (eager, prepared calls) on the launch stream,
+    against 8 TB/s;
   * ``prefill_m1024``: prefill TFLOP/s on the Qwen3-8B-shaped M = 1024 pass
     (36 layers, one batched launch per layer) against the 2.5 PFLOP/s dense
     binary16 matrix-core peak;
@@ -90,36 +93,59 @@ class Pass:
             seen[X_ROLE[name]] = K
         return list(seen.values())
 
-    def run(self, q4k, layer_events=None):
-        for li, probs in enumerate(self.layers):
-            if layer_events is not None:
-                layer_events[li][0].record()
-            q4k.matmul_batched(probs)
-            if layer_events is not None:
-                layer_events[li][1].record()
+    def prepare(self, q4k):
+        self.calls = [q4k.prepare_batched(probs) for probs in self.layers]
         if self.head is not None:
-            q4k.matmul(*self.head)
+            self.calls.append(q4k.prepare_batched([self.head]))
+
+    def run(self, stream=None, layer_events=None):
+        """One pass: every layer's batched launch, then the lm_head."""
+        for li, call in enumerate(self.calls):
+            if layer_events is not None and li < len(self.layers):
+                layer_events[li][0].record()
+            call(stream)
+            if layer_events is not None and li < len(self.layers):
+                layer_events[li][1].record()
 
 
-def time_pass(ps, q4k, steps, warmup):
+def time_pass(ps, q4k, steps, warmup, graph=True):
     """(ms per step, mean ms of one per-layer batched launch)."""
     import torch
+    ps.prepare(q4k)
     for _ in range(warmup):
-        ps.run(q4k)
+        ps.run()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        ps.run(q4k)
-    t1.record()
+    if graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            ps.run(gs)  # the library's per-stream state exists before capture
+            gs.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                ps.run(gs)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+    else:
+        t0.record()
+        for _ in range(steps):
+            ps.run()
+        t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    # Second timed region: HIP events around every per-layer launch.
+    # Second timed region: HIP events around every per-layer launch (eager).
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
             for _ in ps.layers] for _ in range(steps)]
     for s in range(steps):
-        ps.run(q4k, evs[s])
+        ps.run(layer_events=evs[s])
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for step in evs for a, b in step]
     return ms_step, float(np.mean(per))
@@ -144,31 +170,35 @@ def check_pass(ps, q4k, ncols=64):
     return worst
 
 
-def cpu_baseline(ps, budget_s=12.0):
-    """Oracle (as written, OpenMP over output rows) on a bounded sample of the pass."""
+def cpu_baseline(ps, budget_s=10.0):
+    """Oracle (as written, OpenMP over output columns) on a bounded sample: the
+    pass's projections in order, repeated, until about budget_s of CPU time."""
     import oracle
     import q4k_inputs as qi
     from q4k_inputs.workloads import PROJ_ID, X_ROLE
     threads = len(os.sched_getaffinity(0))
     used = oracle.threads_used(threads)
-    done_bytes, t_total, items = 0, 0.0, []
-    for li, (name, N, K) in [(0, p) for p in ps.wl.layer] + \
-            ([(-1, ps.wl.lm_head)] if ps.wl.lm_head else []) + \
-            [(l, p) for l in range(1, ps.wl.layers) for p in ps.wl.layer]:
-        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, ps.wl.ident, li, PROJ_ID[name]))
-        x = ps.x[X_ROLE[name]].cpu().numpy()
-        t = time.perf_counter()
-        oracle.matmul(w, x, N, K, threads=used)
-        t_total += time.perf_counter() - t
-        done_bytes += w.nbytes
-        items.append(f"{'lm_head' if li < 0 else f'L{li}.{name}'}")
-        if t_total >= budget_s:
-            break
+    done_bytes, t_total, calls, passes = 0, 0.0, 0, 0
+    order = [(0, p) for p in ps.wl.layer] + ([(-1, ps.wl.lm_head)] if ps.wl.lm_head else []) + \
+        [(l, p) for l in range(1, ps.wl.layers) for p in ps.wl.layer]
+    x_host = {r: v.cpu().numpy() for r, v in ps.x.items()}
+    while t_total < budget_s:
+        for li, (name, N, K) in order:
+            w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, ps.wl.ident, li, PROJ_ID[name]))
+            t = time.perf_counter()
+            oracle.matmul(w, x_host[X_ROLE[name]], N, K, threads=used)
+            t_total += time.perf_counter() - t
+            done_bytes += w.nbytes
+            calls += 1
+            if t_total >= budget_s:
+                break
+        else:
+            passes += 1
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used,
             "kind": "oracle",
-            "sample": f"{len(items)} of {len(ps.wl.projections())} projections of the same pass "
-                      f"({done_bytes / 1e6:.1f} MB packed weights, M={ps.M}) in {t_total:.1f} s: "
-                      f"{items[0]}..{items[-1]}"}
+            "sample": f"{calls} projection calls of the same pass ({passes} full passes of "
+                      f"{len(order)}), {done_bytes / 1e6:.1f} MB packed weights at M={ps.M}, "
+                      f"{t_total:.1f} s of oracle time"}
 
 
 def main():
@@ -179,6 +209,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy three times (a known-size "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -194,6 +227,14 @@ def main():
         sys.exit(1)
     q4k.library()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {src.numel() * 4} bytes")
+        del src, dst
 
     wl = WORKLOADS["llama3.2-1b_decode_m1"]
     t = time.time()
@@ -212,7 +253,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "M": 1, "layers": wl.layers,
-                   "launches": "one batched call per layer (q,k,v,o,gate,up,down) + lm_head",
+                   "launches": "one batched call per layer (q,k,v,o,gate,up,down) + lm_head, "
+                               "replayed as one HIP graph per step",
                    "weight_bytes": ps.weight_bytes, "parity_max_err_over_S": parity},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -231,7 +273,7 @@ def main():
         pp = Pass(wl3, 1024, dev)
         torch.cuda.synchronize()
         log(f"prefill inputs ready ({pp.weight_bytes / 1e6:.1f} MB) in {time.time() - t:.1f} s")
-        ms_p, ms_pl = time_pass(pp, q4k, args.prefill_steps, 1)
+        ms_p, ms_pl = time_pass(pp, q4k, args.prefill_steps, 1, graph=False)
         parity_p = check_pass(pp, q4k, ncols=16)
         tflops = pp.flops / (ms_p * 1e-3) / 1e12
         ach = pp.layer_flops / (ms_pl * 1e-3) / 1e12

@@ -8,6 +8,8 @@ CPU fallback.
     y = matmul(w_packed, x)           # w_packed: uint8 [N, K/256*144] on cuda
                                       # x: float32 [M, K] on cuda -> y [M, N]
     matmul_batched([(w, x, y), ...])  # one launch per kernel family
+    call = prepare_batched([(w, x, y), ...])  # validate once ...
+    call()                                    # ... launch many times (same buffers)
 
 Names and semantics mirror include/q4k.h.
 """
@@ -160,6 +162,39 @@ def matmul_batched(problems: Sequence[Tuple], path: int = PATH_AUTO, stream=None
     if rc != OK:
         raise Q4KError(rc, "q4k_matmul_batched")
     return [p[2] for p in problems]
+
+
+class PreparedBatch:
+    """A validated batched call on fixed buffers: the argument array is built
+    once and every call goes straight to ``q4k_matmul_batched_path``.  The
+    tensors must stay alive (and in place) while the object is used."""
+
+    def __init__(self, problems: Sequence[Tuple], path: int = PATH_AUTO):
+        problems = list(problems)
+        if not problems:
+            raise Q4KError(ERR_BAD_DIM, "empty batch")
+        self._keep = problems
+        self._arr = (_Problem * len(problems))()
+        M = None
+        for i, (w, x, y) in enumerate(problems):
+            m, n, k = _check_operands(w, x, y)
+            if M is None:
+                M = m
+            elif m != M:
+                raise ValueError("all problems of a batch share M")
+            self._arr[i] = _Problem(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
+        self.M, self.count, self.path = M, len(problems), int(path)
+        self._fn = library().q4k_matmul_batched_path
+
+    def __call__(self, stream=None) -> None:
+        rc = self._fn(self._arr, self.count, self.M, self.path, _stream_handle(stream))
+        if rc != OK:
+            raise Q4KError(rc, "q4k_matmul_batched")
+
+
+def prepare_batched(problems: Sequence[Tuple], path: int = PATH_AUTO) -> PreparedBatch:
+    """Validate a batch of (w, x, y) once; the returned object launches it."""
+    return PreparedBatch(problems, path)
 
 
 def raw_matmul(w_ptr: int, x_ptr: int, y_ptr: int, M: int, N: int, K: int,

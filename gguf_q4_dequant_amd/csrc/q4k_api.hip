@@ -147,7 +147,7 @@ int run(const q4k_problem *problems, int count, int M, int path, hipStream_t str
     const int dev_rc = check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
     if (path == Q4K_PATH_AUTO) path = pick_path(M);
-    const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode(b, stream) : launch_prefill(b, stream);
+    const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode_mma(b, stream) : launch_prefill(b, stream);
     if (err == hipErrorOutOfMemory || err == hipErrorMemoryAllocation) return Q4K_ERR_ALLOC;
     return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
 }

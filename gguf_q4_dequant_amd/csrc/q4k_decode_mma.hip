@@ -1,0 +1,546 @@
+// Small-M Q4_K product on the matrix cores: y[M,N] = x[M,K] . W[N,K]^T for
+// M <= 16, W in packed Q4_K super-blocks.
+//
+// What is computed (block layout: GGUF K-quant description, Q4_K super-block
+// of 256 weights, 144 bytes):
+//   w = d * sc_j * q - dmin * m_j, so for one row n and one super-block
+//   y_t += d * sum_j sc_j * (sum_{k in sub-block j} x_tk q_k) - dmin * sum_j m_j X_tj
+// with X_tj the plain sum of x_t over sub-block j.
+//
+// How, on gfx950:
+//   * The quant nibbles become the B operand of v_mfma_f32_32x32x16_f16 with
+//     one AND per two weights: a nibble in the low bits of a binary16 is the
+//     subnormal q * 2^-24 (the high nibble, in bits 4..7, is 16q * 2^-24),
+//     exact, and the matrix cores keep subnormal inputs.  Bytes (0,2) and
+//     (1,3) of a dword give the two halves of a register, so the k order
+//     inside an MFMA slice is 0,2,1,3,4,6,5,7; activations are staged in that
+//     order.  The 32 columns of the MFMA are 32 rows n of W.
+//   * Activations are split into two binary16 rows, x' = hi + lo with
+//     hi = rn(x'), lo = rn(x' - hi) (about 22 significant bits), after scaling
+//     each super-block of each token by a power of two 2^e that puts its
+//     largest magnitude in [2^14, 2^15).  Token t uses A rows 2t (hi) and
+//     2t+1 (lo); the other rows of the 32 are don't-care.
+//   * Two MFMAs give one sub-block's sum_k x'_tk q_k * 2^-24 for 32 rows; the
+//     per-row scale d*sc_j (d*sc_j/16 for high nibbles) is applied to that
+//     fp32 result, the factor 2^(24-e) once per super-block, and the min term
+//     is added with fp32 FMAs.
+//   * Weights are read as contiguous 16-byte pieces (32 rows x 144 bytes per
+//     super-block) and parked in LDS with a 144-byte row stride, from where
+//     each lane picks up its own row's bytes (the fragment reads touch 64
+//     distinct banks): reading fragments straight from HBM touches twice as
+//     many cache lines per load and is much slower.
+//   * Two kernels: for M = 1 sixteen waves per workgroup, each owning about
+//     two super-blocks of one 32-row tile and staging its own activations;
+//     for 2 <= M <= 16 four waves per 32-row tile, staging the activations of
+//     all tokens in passes over K.  In both, the waves of a tile add their
+//     partial sums through LDS (no second kernel).
+#include "q4k_internal.h"
+
+namespace q4k {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 32;                           // rows n per workgroup
+constexpr int kMaxTokens = 16;                      // tokens per launch (two A rows each)
+constexpr int kStage = kCols * kBlockBytes;         // one super-block of 32 rows
+constexpr int kStageChunks = kStage / 16;           // 288 sixteen-byte pieces
+
+// Super-blocks of activations staged per pass (8, or fewer for short rows:
+// every wave then takes an even number of super-blocks per pass).
+__host__ __device__ inline int chunk_blocks(int KB) { return KB < 8 ? (KB + 7) & ~7 : 8; }
+__host__ __device__ inline int lds_bytes(int M, int CB) {
+    // weight slots | staged x (M * CB * 1024 B) | X sums and factors (M * CB * 64 B)
+    return kWaves * kStage + M * CB * 1024 + M * CB * 64;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Decoded per-row scales of one super-block: dsc[j] = d * sc_j (times 1/16
+// for odd j, whose quants enter the products as 16q), dm[j] = dmin * m_j.
+__device__ __forceinline__ void block_scales(const uint4 hd, float dsc[8], float dm[8]) {
+    const float d = half_bits_to_float(hd.x & 0xFFFFu);
+    const float d16 = d * 0.0625f;
+    const float dmin = half_bits_to_float(hd.x >> 16);
+    const uint32_t scA = hd.y & 0x3F3F3F3Fu, mnA = hd.z & 0x3F3F3F3Fu;
+    const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dsc[j] = ((j & 1) ? d16 : d) * static_cast<float>((scA >> (8 * j)) & 0xFFu);
+        dsc[4 + j] = ((j & 1) ? d16 : d) * static_cast<float>((scB >> (8 * j)) & 0xFFu);
+        dm[j] = dmin * static_cast<float>((mnA >> (8 * j)) & 0xFFu);
+        dm[4 + j] = dmin * static_cast<float>((mnB >> (8 * j)) & 0xFFu);
+    }
+}
+
+// One parked super-block of 32 rows times the staged activations.  rb points
+// at this lane's row (col) in the staging slot; xs/xsum are the staged
+// activations with jj0 the block's first sub-block, mul_t[i][jj0/8] the factor
+// that undoes token tok[i]'s scaling of this block; token tok[i]'s result for
+// row col is added to acc[i] (i < NP; see the C-register layout below).
+template <int NP>
+__device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, int R2, int arow, int half,
+                                          int jj0, const float *const mul_t[NP], const float *const sum_t[NP],
+                                          float acc[NP]) {
+    float dsc[8], dm[8];
+    block_scales(*reinterpret_cast<const uint4 *>(rb), dsc, dm);
+    float blk[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) blk[i] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(rb + 16 + 32 * g + 16 * half);
+        const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
+        const uint32_t s0 = q.x >> 8, s1 = q.y >> 8, s2 = q.z >> 8, s3 = q.w >> 8;
+        const uint4 blo0 = {q.x & LM, s0 & LM, q.y & LM, s1 & LM};
+        const uint4 blo1 = {q.z & LM, s2 & LM, q.w & LM, s3 & LM};
+        const uint4 bhi0 = {q.x & HM, s0 & HM, q.y & HM, s1 & HM};
+        const uint4 bhi1 = {q.z & HM, s2 & HM, q.w & HM, s3 & HM};
+        const int jl = jj0 + 2 * g, jh = jl + 1;  // sub-blocks 2g, 2g+1 of this block
+        const uint4 alo0 = xs[((jl * 2 + 0) * R2 + arow) * 2 + half];
+        const uint4 alo1 = xs[((jl * 2 + 1) * R2 + arow) * 2 + half];
+        const uint4 ahi0 = xs[((jh * 2 + 0) * R2 + arow) * 2 + half];
+        const uint4 ahi1 = xs[((jh * 2 + 1) * R2 + arow) * 2 + half];
+        float16v zero;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zero[i] = 0.f;
+        float16v clo = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8, alo0), __builtin_bit_cast(half8, blo0), zero, 0, 0, 0);
+        clo = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8, alo1), __builtin_bit_cast(half8, blo1), clo, 0, 0, 0);
+        float16v chi = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8, ahi0), __builtin_bit_cast(half8, bhi0), zero, 0, 0, 0);
+        chi = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8, ahi1), __builtin_bit_cast(half8, bhi1), chi, 0, 0, 0);
+        // C layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+        // column l%32; registers 2i, 2i+1 are the hi and lo rows of token
+        // 4*(i/2) + 2*(l/32) + i%2.
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            blk[i] = __builtin_fmaf(dsc[2 * g], clo[2 * i] + clo[2 * i + 1], blk[i]);
+            blk[i] = __builtin_fmaf(dsc[2 * g + 1], chi[2 * i] + chi[2 * i + 1], blk[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        float mterm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mterm = __builtin_fmaf(dm[j], sum_t[i][jj0 + j], mterm);
+        acc[i] = __builtin_fmaf(mul_t[i][jj0 >> 3], blk[i], acc[i]) - mterm;
+    }
+}
+
+// Stages eight activations x[0..7] of token tt, values 8v..8v+7 of staged
+// sub-block jj, as scaled hi/lo binary16 rows 2tt, 2tt+1 in the MFMA k order.
+// The 32 lanes of one super-block (32 adjacent lanes, from jj%8 == 0, v == 0)
+// call it together: the scale 2^e puts the super-block's largest magnitude in
+// [2^14, 2^15).  The first lane of each sub-block writes its plain sum, the
+// first lane of the super-block the factor 2^(24-e) that undoes the scaling.
+__device__ __forceinline__ void stage_group(const float4 a, const float4 b, int jj, int v, int tt, int R2,
+                                            uint4 *xs, float *sum_t, float *mul_t) {
+    float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float mx = 0.f, sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mx = fmaxf(mx, fabsf(xv[i]));
+        sm += xv[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    sm += __shfl_xor(sm, 1);
+    sm += __shfl_xor(sm, 2);
+    // scale 2^e with e = 14 - floor(log2 mx), limited so 2^e and 2^(24-e) are normal
+    const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
+    int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
+    e = max(-103, min(127, e));
+    const float up = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    const float back = __uint_as_float(static_cast<uint32_t>(24 - e + 127) << 23);
+    half8 hv, lv;
+    constexpr int perm[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float xv2 = xv[perm[i]] * up;
+        const _Float16 h = static_cast<_Float16>(xv2);
+        hv[i] = h;
+        lv[i] = static_cast<_Float16>(xv2 - static_cast<float>(h));
+    }
+    const int s = v & 1, hh = v >> 1;
+    xs[((jj * 2 + s) * R2 + 2 * tt) * 2 + hh] = __builtin_bit_cast(uint4, hv);
+    xs[((jj * 2 + s) * R2 + 2 * tt + 1) * 2 + hh] = __builtin_bit_cast(uint4, lv);
+    if (v == 0) sum_t[jj] = sm;
+    if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
+}
+
+// NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8, 8 for M <= 16).
+template <int NP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NP == 2 ? 2 : 1)))
+void decode_mma_kernel(Batch bt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tile = static_cast<int>(blockIdx.x);
+    int p = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (tile >= bt.p[i].tile_begin) p = i;
+    const DevProblem &P = bt.p[p];
+    const int N = P.N, K = P.K, M = bt.M;
+    const int KB = K >> 8;
+    const int n0 = (tile - P.tile_begin) * kCols;
+    const int CB = chunk_blocks(KB);
+    const int R2 = 2 * M;  // A rows in use
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int col = lane & 31, half = lane >> 5;
+
+    constexpr int kWLds = kWaves * kStage;
+    uint8_t *wst = lds + wave * kStage;  // this wave's weight slot
+    uint4 *xs = reinterpret_cast<uint4 *>(lds + kWLds);
+    float *xsum = reinterpret_cast<float *>(lds + kWLds + M * CB * 1024);
+    float *xmul = xsum + M * CB * 8;
+
+    // Offsets of this lane's five pieces of a super-block from the tile's
+    // first row (32-bit: a tile spans 32 rows).
+    const uint8_t *W = P.w + static_cast<size_t>(n0) * KB * kBlockBytes;
+    const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
+    uint32_t goff[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int f = min(lane + 64 * j, kStageChunks - 1);
+        goff[j] = static_cast<uint32_t>(min(f / 9, N - 1 - n0)) * row_bytes + 16u * (f % 9);
+    }
+    const bool has5 = lane + 256 < kStageChunks;  // fifth piece: lanes 0..31
+    // Piece j of super-block kb of the wave's rows: piece f = lane + 64 j
+    // (f < 288) is bytes 16*(f%9).. of row f/9 (lanes >= 32 re-read a valid
+    // piece for j = 4 and do not park it).
+    auto ld = [&](int kb, int j) -> u32x4 {
+        return *reinterpret_cast<const u32x4 *>(W + (static_cast<uint32_t>(kb) * kBlockBytes + goff[j]));
+    };
+    auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, u32x4 v4) {
+        u32x4 *d = reinterpret_cast<u32x4 *>(wst);
+        d[lane] = v0;
+        d[lane + 64] = v1;
+        d[lane + 128] = v2;
+        d[lane + 192] = v3;
+        if (has5) d[lane + 256] = v4;
+    };
+
+    float acc[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) acc[i] = 0.f;
+    int tok[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) tok[i] = min(4 * (i >> 1) + 2 * half + (i & 1), M - 1);
+    const int arow = min(col, R2 - 1);
+
+    const float *mul_t[NP], *sum_t[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        mul_t[i] = xmul + tok[i] * CB * 8;
+        sum_t[i] = xsum + tok[i] * CB * 8;
+    }
+    // One super-block from the staging area; bo = its index within the pass.
+    auto consume = [&](int bo) {
+        mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
+    };
+
+    // Stage pass c of the activations: super-blocks [c*CB, c*CB + CB) of every
+    // token.  Group gq (8 values) of the pass is token gq/(CB*32), sub-block
+    // (gq%(CB*32))/4, values 8*(gq%4)..; x0/x1 hold this thread's first group
+    // of pass 0, read before the weights are requested.
+    const int groups = M * CB * 32;
+    auto group_src = [&](int c, int gq, int &tt, int &jj, int &v) -> const float4 * {
+        tt = gq / (CB * 32);
+        const int gl = gq - tt * CB * 32;
+        jj = gl >> 2;
+        v = gl & 3;
+        const int kb = c * CB + (jj >> 3);
+        if (kb >= KB) return nullptr;  // the whole super-block (32 lanes) skips together
+        return reinterpret_cast<const float4 *>(P.x + static_cast<size_t>(tt) * K + static_cast<size_t>(kb) * 256 +
+                                                (jj & 7) * 32 + 8 * v);
+    };
+    float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    {
+        int tt, jj, v;
+        const float4 *src = t < groups ? group_src(0, t, tt, jj, v) : nullptr;
+        if (src) {
+            x0 = src[0];
+            x1 = src[1];
+        }
+    }
+    auto stage = [&](int c) {
+        for (int gq = t; gq < groups; gq += kThreads) {
+            int tt, jj, v;
+            const float4 *src = group_src(c, gq, tt, jj, v);
+            if (!src) continue;
+            const bool pre = c == 0 && gq == t;
+            stage_group(pre ? x0 : src[0], pre ? x1 : src[1], jj, v, tt, R2, xs, xsum + tt * CB * 8,
+                        xmul + tt * CB * 8);
+        }
+    };
+
+    // This wave's super-blocks: kb = wave + 4 i.
+    const int nb = KB > wave ? (KB - wave + kWaves - 1) / kWaves : 0;
+    const int per_pass = CB / kWaves;  // even
+    const int passes = (KB + CB - 1) / CB;
+    // Two super-blocks in registers (named: arrays of loaded values end up in
+    // scratch).
+    u32x4 a0, a1, a2, a3, a4, b0, b1, b2, b3, b4;
+    if (nb > 0) {
+        const int kb = wave;
+        a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
+    }
+    if (nb > 1) {
+        const int kb = wave + kWaves;
+        b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
+    }
+    for (int c = 0; c < passes; ++c) {
+        if (c > 0) __syncthreads();  // everyone is done with the previous pass
+        stage(c);
+        __syncthreads();
+        const int i_end = min(nb, (c + 1) * per_pass);
+        for (int i = c * per_pass; i < i_end; i += 2) {
+            const bool two = i + 1 < i_end;
+            const int bo = (wave + kWaves * i) - c * CB;
+            park(a0, a1, a2, a3, a4);
+            if (i + 2 < nb) {
+                const int kb = wave + kWaves * (i + 2);
+                a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
+            }
+            consume(bo);
+            if (two) {
+                park(b0, b1, b2, b3, b4);  // after consume(bo) in program order
+                if (i + 3 < nb) {
+                    const int kb = wave + kWaves * (i + 3);
+                    b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
+                }
+                consume(bo + kWaves);
+            }
+        }
+    }
+
+    // Sum the four waves' partial results.
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) red[(wave * NP + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+        const int n = n0 + col;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const float v = red[(0 * NP + i) * 64 + lane] + red[(1 * NP + i) * 64 + lane] +
+                            red[(2 * NP + i) * 64 + lane] + red[(3 * NP + i) * 64 + lane];
+            const int tt = 4 * (i >> 1) + 2 * half + (i & 1);
+            if (tt < M && n < N) P.y[static_cast<size_t>(tt) * N + n] = v;
+        }
+    }
+}
+
+// ---- M = 1: sixteen waves per workgroup ----------------------------------
+// The waves of a workgroup split the super-blocks of one tile (or, for short
+// rows, several tiles of the same product) so that every wave owns about two
+// super-blocks; partial sums meet in LDS at the end.  Each wave stages the
+// activations of its own super-blocks (one group of 8 per lane for a pair),
+// so no wave waits for another before the final sum.
+constexpr int kWideWaves = 16;
+constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kWideMaxGroups = 512;  // about two rounds of one workgroup per CU
+
+// Waves per tile: the power of two (at most 16) that leaves each wave two
+// super-blocks or fewer where possible.
+__host__ __device__ inline int wide_wpt(int KB) {
+    int w = 1;
+    while (w < kWideWaves && 2 * w < KB) w *= 2;
+    return w;
+}
+
+__global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
+    // Per wave: a weight slot, and the staged activations of a pair of
+    // super-blocks with their sub-block sums and scale factors.
+    __shared__ __attribute__((aligned(16))) uint8_t wslots[kWideWaves * kStage];
+    __shared__ __attribute__((aligned(16))) uint4 xsw[kWideWaves][2 * 64];
+    __shared__ float xsumw[kWideWaves][2 * 8];
+    __shared__ float xmulw[kWideWaves][2];
+    const int g = static_cast<int>(blockIdx.x);
+    int p = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (g >= bt.p[i].tile_begin) p = i;
+    const DevProblem &P = bt.p[p];
+    const int N = P.N, K = P.K;
+    const int KB = K >> 8;
+    const int wpt = wide_wpt(KB);
+    const int T = kWideWaves / wpt;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int tl = wave / wpt, kw = wave - tl * wpt;  // tile within the group, K lane
+    const int n0 = ((g - P.tile_begin) * T + tl) * kCols;
+    const bool active = n0 < N;  // the last group of a product may be short
+
+    uint8_t *wst = wslots + wave * kStage;
+    uint4 *xs = xsw[wave];
+    float *xsum = xsumw[wave];
+    float *xmul = xmulw[wave];
+
+    const int nr = active ? N - 1 - n0 : 0;  // last row of the tile, relative
+    const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * KB * kBlockBytes;
+    const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
+    uint32_t goff[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int f = min(lane + 64 * j, kStageChunks - 1);
+        goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
+    }
+    const bool has5 = lane + 256 < kStageChunks;
+    auto ld = [&](int kb, int j) -> u32x4 {
+        return *reinterpret_cast<const u32x4 *>(W + (static_cast<uint32_t>(kb) * kBlockBytes + goff[j]));
+    };
+    auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, u32x4 v4) {
+        u32x4 *d = reinterpret_cast<u32x4 *>(wst);
+        d[lane] = v0;
+        d[lane + 64] = v1;
+        d[lane + 128] = v2;
+        d[lane + 192] = v3;
+        if (has5) d[lane + 256] = v4;
+    };
+
+    float acc[1] = {0.f};
+    const float *mul_t[1] = {xmul}, *sum_t[1] = {xsum};
+    const int arow = min(col, 1);
+    const uint8_t *rb = wst + col * kBlockBytes;
+
+    // This wave's super-blocks kb = kw + wpt * i, in pairs (i0, i0 + 1).  For
+    // each pair everything is requested at once: the activations (lanes
+    // 0..31 for the first block, 32..63 for the second), the second block by
+    // LDS DMA straight into the slot, the first into registers.
+    const int nb = active && KB > kw ? (KB - kw + wpt - 1) / wpt : 0;
+    for (int i0 = 0; i0 < nb; i0 += 2) {
+        const int bi = min(i0 + half, nb - 1);  // a lone last block is staged twice
+        const float4 *src =
+            reinterpret_cast<const float4 *>(P.x + static_cast<size_t>(kw + wpt * bi) * 256 + 8 * col);
+        const float4 xa = src[0], xb = src[1];
+        const int kb0 = kw + wpt * i0, kb1 = kw + wpt * min(i0 + 1, nb - 1);
+        const u32x4 a0 = ld(kb0, 0), a1 = ld(kb0, 1), a2 = ld(kb0, 2), a3 = ld(kb0, 3), a4 = ld(kb0, 4);
+        const u32x4 b0 = ld(kb1, 0), b1 = ld(kb1, 1), b2 = ld(kb1, 2), b3 = ld(kb1, 3), b4 = ld(kb1, 4);
+        // Loads complete in order: the activations, then the first block, are
+        // used while the second block is still arriving.
+        stage_group(xa, xb, half * 8 + (col >> 2), col & 3, 0, 2, xs, xsum, xmul);
+        park(a0, a1, a2, a3, a4);
+        mma_block<1>(rb, xs, 2, arow, half, 0, mul_t, sum_t, acc);
+        if (i0 + 1 < nb) {
+            park(b0, b1, b2, b3, b4);  // after the reads above, in program order
+            mma_block<1>(rb, xs, 2, arow, half, 8, mul_t, sum_t, acc);
+        }
+    }
+
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(wslots);
+    red[wave * 64 + lane] = acc[0];
+    __syncthreads();
+    if (active && kw == 0 && half == 0) {
+        float v = 0.f;
+        for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
+        const int n = n0 + col;
+        if (n < N) P.y[n] = v;
+    }
+}
+
+template <int NP>
+hipError_t launch_np(const Batch &b, int lds, int grid, hipStream_t stream) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(decode_mma_kernel<NP>, dim3(grid), dim3(kThreads), lds, stream, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
+    Batch sb;
+    sb.count = b.count;
+    sb.M = 1;
+    int groups = 0;
+    for (int i = 0; i < b.count; ++i) {
+        sb.p[i] = b.p[order[i]];
+        const int KB = sb.p[i].K / kBlockWeights;
+        const int T = kWideWaves / wide_wpt(KB);
+        const int tiles = (sb.p[i].N + kCols - 1) / kCols;
+        sb.p[i].tile_begin = groups;
+        sb.p[i].tiles = (tiles + T - 1) / T;
+        sb.p[i].splits = 1;
+        groups += sb.p[i].tiles;
+    }
+    if (groups == 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_wide_kernel, dim3(groups), dim3(kWideThreads), 0, stream, sb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
+    // Workgroups in order of decreasing K, so the longest ones start first.
+    int order[kMaxBatch];
+    for (int i = 0; i < b.count; ++i) order[i] = i;
+    for (int i = 1; i < b.count; ++i)
+        for (int j = i; j > 0 && b.p[order[j]].K > b.p[order[j - 1]].K; --j) {
+            const int o = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = o;
+        }
+    if (b.M == 1) {
+        // One workgroup of sixteen waves per CU: best when the launch fits in
+        // about two rounds; larger launches go to the fp32 GEMV family, whose
+        // small workgroups keep every CU busy across rounds.
+        int groups = 0;
+        for (int i = 0; i < b.count; ++i) {
+            const int T = kWideWaves / wide_wpt(b.p[i].K / kBlockWeights);
+            groups += ((b.p[i].N + kCols - 1) / kCols + T - 1) / T;
+        }
+        if (groups > kWideMaxGroups) return launch_decode(b, stream);
+        return launch_wide(b, order, stream);
+    }
+    // At most 16 tokens per launch (32 A rows); more tokens (only when the
+    // caller forces this path) are done 16 at a time.
+    for (int m0 = 0; m0 < b.M; m0 += kMaxTokens) {
+        Batch sb;
+        sb.count = b.count;
+        sb.M = min(kMaxTokens, b.M - m0);
+        int tiles = 0, lds = 0;
+        for (int i = 0; i < b.count; ++i) {
+            sb.p[i] = b.p[order[i]];
+            sb.p[i].x += static_cast<size_t>(m0) * sb.p[i].K;
+            sb.p[i].y += static_cast<size_t>(m0) * sb.p[i].N;
+            sb.p[i].tile_begin = tiles;
+            sb.p[i].tiles = (sb.p[i].N + kCols - 1) / kCols;
+            sb.p[i].splits = 1;
+            tiles += sb.p[i].tiles;
+            const int KB = sb.p[i].K / kBlockWeights;
+            lds = max(lds, lds_bytes(sb.M, chunk_blocks(KB)));
+        }
+        if (tiles == 0) return hipSuccess;
+        const int M = sb.M;
+        int ident[kMaxBatch];
+        for (int i = 0; i < b.count; ++i) ident[i] = i;
+        const hipError_t e = M <= 1   ? launch_wide(sb, ident, stream)
+                             : M <= 4 ? launch_np<2>(sb, lds, tiles, stream)
+                             : M <= 8 ? launch_np<4>(sb, lds, tiles, stream)
+                                      : launch_np<8>(sb, lds, tiles, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace q4k

@@ -42,6 +42,7 @@ struct Batch {
 // Return hipSuccess or the launch error.
 hipError_t launch_decode(Batch &b, hipStream_t stream);
 hipError_t launch_prefill(Batch &b, hipStream_t stream);
+hipError_t launch_decode_mma(Batch &b, hipStream_t stream);
 
 // Library-owned device scratch, per (device, stream), grown on demand
 // (growing synchronizes the stream first).  Two separate buffers:

@@ -1,0 +1,60 @@
+"""Library calls captured in a HIP graph give the eager results on every replay.
+
+The bench replays its decode pass as a graph; this checks that the captured
+launches (both M = 1 kernel families and the prefill family) reproduce the
+eager outputs bit for bit, replay after replay, with eager work and
+synchronizations in between.
+"""
+import numpy as np
+import pytest
+
+import q4k_inputs as qi
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _dev_inputs(M, N, K, tag):
+    w = torch.from_numpy(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 77, tag, 0))).cuda()
+    x = torch.from_numpy(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 77, tag, 1))).cuda()
+    return w, x
+
+
+def test_graph_replays_match_eager():
+    import gguf_q4_dequant_amd as q4k
+    q4k.library()
+    # M = 1 layer-sized batch (sixteen-wave family), a tall M = 1 product (more
+    # than two rounds of workgroups: fp32 GEMV family) and an M = 64 prefill.
+    layer = []
+    for i, (N, K) in enumerate([(2048, 2048), (512, 2048), (8192, 2048), (2048, 8192)]):
+        w, x = _dev_inputs(1, N, K, i)
+        layer.append((w, x, torch.empty(1, N, device="cuda")))
+    wt, xt = _dev_inputs(1, 70000, 2048, 10)
+    tall = [(wt, xt, torch.empty(1, 70000, device="cuda"))]
+    wp, xp = _dev_inputs(64, 1024, 3072, 11)
+    pre = [(wp, xp, torch.empty(64, 1024, device="cuda"))]
+    calls = [q4k.prepare_batched(b) for b in (layer, tall, pre)]
+    outs = [y for b in (layer, tall, pre) for (_, _, y) in b]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:  # eager, on the capture stream (per-stream state exists before capture)
+            c(side)
+        side.synchronize()
+        eager = [y.clone() for y in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in outs:
+            y.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda") * 3.0  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(outs, eager):
+            assert torch.equal(y, e), f"replay {rep} differs from the eager result"
+        del junk

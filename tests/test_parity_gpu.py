@@ -102,8 +102,10 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
 
 
 @pytest.mark.parametrize("path,M,cuts,bitwise", [
-    (DEC, 4, (2, 3), True),       # every chunk runs the same K split: identical bits
-    (DEC, 9, (5, 6), True),
+    (DEC, 4, (2,), True),         # chunks of 2..16 tokens run one kernel and K split: identical bits
+    (DEC, 9, (5, 7), True),
+    (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
+    (DEC, 9, (5, 6), False),
     (PRE, 9, (5, 6), True),
     (PRE, 200, (130, 131), True),
 ])
