@@ -13,8 +13,9 @@ seeded synthetic data generated on the host and uploaded before timing.
 Also reported in the same line:
   * ``roofline``: the dominant kernel (the per-layer batched decode launch):
     algorithmic bytes per launch / its average duration, timed with HIP events
-    around every such launch (eager, prepared calls) on the launch stream,
-    against 8 TB/s;
+    around graph replays of the 16 layer launches alone, on the replay stream,
+    against 8 TB/s; ``traffic`` is the HBM bytes per launch recorded from
+    FETCH_SIZE / WRITE_SIZE counters in profiles/ (null if the kernel changed);
   * ``prefill_m1024``: prefill TFLOP/s on the Qwen3-8B-shaped M = 1024 pass
     (36 layers, one batched launch per layer) against the 2.5 PFLOP/s dense
     binary16 matrix-core peak;
@@ -108,40 +109,63 @@ class Pass:
                 layer_events[li][1].record()
 
 
+def _capture(fn):
+    """A HIP graph of fn(stream) captured on a side stream (run once eagerly
+    there first, so the library's per-stream state exists before capture)."""
+    import torch
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        fn(gs)
+        gs.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            fn(gs)
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_replays(g, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def time_pass(ps, q4k, steps, warmup, graph=True):
-    """(ms per step, mean ms of one per-layer batched launch)."""
+    """(ms per step, mean ms of one per-layer batched launch).
+
+    graph=True: both figures come from HIP-graph replays bracketed by HIP
+    events on the replay stream: the whole pass, and the per-layer launches
+    alone (their time divided by the number of launches).  graph=False:
+    eager prepared calls, events around the pass and around every layer."""
     import torch
     ps.prepare(q4k)
     for _ in range(warmup):
         ps.run()
     torch.cuda.synchronize()
+    if graph:
+        ms_step = _time_replays(_capture(lambda st: ps.run(st)), steps, warmup)
+        nl = len(ps.layers)
+        layers_only = _capture(lambda st: [c(st) for c in ps.calls[:nl]])
+        ms_layer = _time_replays(layers_only, steps, warmup) / nl
+        return ms_step, ms_layer
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    if graph:
-        gs = torch.cuda.Stream()
-        gs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(gs):
-            ps.run(gs)  # the library's per-stream state exists before capture
-            gs.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=gs):
-                ps.run(gs)
-        torch.cuda.synchronize()
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(steps):
-            g.replay()
-        t1.record()
-    else:
-        t0.record()
-        for _ in range(steps):
-            ps.run()
-        t1.record()
+    t0.record()
+    for _ in range(steps):
+        ps.run()
+    t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    # Second timed region: HIP events around every per-layer launch (eager).
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
             for _ in ps.layers] for _ in range(steps)]
     for s in range(steps):
@@ -149,6 +173,29 @@ def time_pass(ps, q4k, steps, warmup, graph=True):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for step in evs for a, b in step]
     return ms_step, float(np.mean(per))
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch of a kernel from a committed counter summary
+    (profiles/<name>.txt: FETCH_SIZE and WRITE_SIZE scaled by a plain copy of
+    known size), or None when the kernel's sources have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", " ", "|")):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in rec.get("sources", "").split():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if not rec.get("sources") or h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def check_pass(ps, q4k, ncols=64):
@@ -257,8 +304,9 @@ def main():
                                "replayed as one HIP graph per step",
                    "weight_bytes": ps.weight_bytes, "parity_max_err_over_S": parity},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode per-layer batched launch",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("decode_wide_llama1b_layer_m1"),
+                     "kernel": "decode_wide_kernel (per-layer batched launch)",
                      "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)},
     }
     if not args.no_cpu:
@@ -282,8 +330,9 @@ def main():
             "ms_per_step": round(ms_p, 4), "steps": args.prefill_steps, "dtype": "f16 operands, f32 accumulate",
             "parity_max_err_over_S": parity_p,
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "prefill per-layer batched launch",
+                         "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill_qwen3_8b_layer_m1024"),
+                         "kernel": "prefill per-layer batched launch (x conversion + prefill_kernel)",
                          "avg_launch_us": round(ms_pl * 1e3, 2)}}
         log(f"prefill: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
             f"-> {ach:.1f} TFLOP/s; parity {parity_p:.2e}")
