@@ -180,6 +180,92 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
 }
 
 // NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8, 8 for M <= 16).
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// M = 1 variant of mma_block on v_mfma_f32_16x16x32_f16: K = 32 is one
+// sub-block, so no MFMA waits on another.  A holds x' hi in every even row and
+// lo in every odd row (lane l: row l%16, k-quarter l/16); B holds the quants
+// of rows n0 + l%16 (first MFMA) and n0 + 16 + l%16 (second).  Lane l < 16
+// reads its row's result in C rows 0, 1 of the first MFMA, lane 16..31 in C
+// rows 4, 5 of the second, so lane l (< 32) owns row l of the tile and decodes
+// only that row's scales.  xs holds, per staged sub-block jj, the hi then lo
+// row as four 16-byte k-quarters: xs[(jj*2 + hl)*4 + quarter].
+__device__ __forceinline__ void mma_block16(const uint8_t *slot, const uint4 *xs, int lane, int jj0,
+                                            float mul, const float *sum_t, float &acc) {
+    const int c16 = lane & 15, quarter = lane >> 4, hl = lane & 1;
+    const bool second = (lane & 16) != 0;
+    float dsc[8], dm[8];
+    block_scales(*reinterpret_cast<const uint4 *>(slot + (lane & 31) * kBlockBytes), dsc, dm);
+    const uint8_t *ra = slot + c16 * kBlockBytes + 16 + 8 * quarter;
+    const uint8_t *rc = ra + 16 * kBlockBytes;
+    float blk = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint2 qa = *reinterpret_cast<const uint2 *>(ra + 32 * g);
+        const uint2 qc = *reinterpret_cast<const uint2 *>(rc + 32 * g);
+        const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
+        const uint32_t sa0 = qa.x >> 8, sa1 = qa.y >> 8, sc0 = qc.x >> 8, sc1 = qc.y >> 8;
+        const uint4 bla = {qa.x & LM, sa0 & LM, qa.y & LM, sa1 & LM};
+        const uint4 bha = {qa.x & HM, sa0 & HM, qa.y & HM, sa1 & HM};
+        const uint4 blc = {qc.x & LM, sc0 & LM, qc.y & LM, sc1 & LM};
+        const uint4 bhc = {qc.x & HM, sc0 & HM, qc.y & HM, sc1 & HM};
+        const int jl = jj0 + 2 * g, jh = jl + 1;
+        const half8 al = __builtin_bit_cast(half8, xs[(jl * 2 + hl) * 4 + quarter]);
+        const half8 ah = __builtin_bit_cast(half8, xs[(jh * 2 + hl) * 4 + quarter]);
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        const float4v cla = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(half8, bla), z, 0, 0, 0);
+        const float4v clc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(half8, blc), z, 0, 0, 0);
+        const float4v cha = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8, bha), z, 0, 0, 0);
+        const float4v chc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8, bhc), z, 0, 0, 0);
+        // C layout of a 16x16 MFMA: lane l, register r -> row 4*(l/16) + r, column l%16.
+        const float lo = second ? clc[0] + clc[1] : cla[0] + cla[1];
+        const float hi = second ? chc[0] + chc[1] : cha[0] + cha[1];
+        blk = __builtin_fmaf(dsc[2 * g], lo, blk);
+        blk = __builtin_fmaf(dsc[2 * g + 1], hi, blk);
+    }
+    float mterm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mterm = __builtin_fmaf(dm[j], sum_t[jj0 + j], mterm);
+    acc = __builtin_fmaf(mul, blk, acc) - mterm;
+}
+
+// Staging for mma_block16: eight activations (values 8v..8v+7 of staged
+// sub-block jj, v = k-quarter) as scaled hi/lo binary16 in the k order
+// 0,2,1,3,4,6,5,7.  The 32 lanes of one super-block call it together (32
+// adjacent lanes); scale, sums and factor as in stage_group.
+__device__ __forceinline__ void stage_group16(const float4 a, const float4 b, int jj, int v, uint4 *xs,
+                                              float *sum_t, float *mul_t) {
+    float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float mx = 0.f, sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mx = fmaxf(mx, fabsf(xv[i]));
+        sm += xv[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    sm += __shfl_xor(sm, 1);
+    sm += __shfl_xor(sm, 2);
+    const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
+    int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
+    e = max(-103, min(127, e));
+    const float up = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    const float back = __uint_as_float(static_cast<uint32_t>(24 - e + 127) << 23);
+    half8 hv, lv;
+    constexpr int perm[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float xv2 = xv[perm[i]] * up;
+        const _Float16 h = static_cast<_Float16>(xv2);
+        hv[i] = h;
+        lv[i] = static_cast<_Float16>(xv2 - static_cast<float>(h));
+    }
+    xs[(jj * 2 + 0) * 4 + v] = __builtin_bit_cast(uint4, hv);
+    xs[(jj * 2 + 1) * 4 + v] = __builtin_bit_cast(uint4, lv);
+    if (v == 0) sum_t[jj] = sm;
+    if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
+}
+
 template <int NP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NP == 2 ? 2 : 1)))
 void decode_mma_kernel(Batch bt) {
@@ -415,9 +501,6 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
     };
 
     float acc[1] = {0.f};
-    const float *mul_t[1] = {xmul}, *sum_t[1] = {xsum};
-    const int arow = min(col, 1);
-    const uint8_t *rb = wst + col * kBlockBytes;
 
     // This wave's super-blocks kb = kw + wpt * i, in pairs (i0, i0 + 1).  For
     // each pair everything is requested at once: the activations (lanes
@@ -434,12 +517,12 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
         const u32x4 b0 = ld(kb1, 0), b1 = ld(kb1, 1), b2 = ld(kb1, 2), b3 = ld(kb1, 3), b4 = ld(kb1, 4);
         // Loads complete in order: the activations, then the first block, are
         // used while the second block is still arriving.
-        stage_group(xa, xb, half * 8 + (col >> 2), col & 3, 0, 2, xs, xsum, xmul);
+        stage_group16(xa, xb, half * 8 + (col >> 2), col & 3, xs, xsum, xmul);
         park(a0, a1, a2, a3, a4);
-        mma_block<1>(rb, xs, 2, arow, half, 0, mul_t, sum_t, acc);
+        mma_block16(wst, xs, lane, 0, xmul[0], xsum, acc[0]);
         if (i0 + 1 < nb) {
             park(b0, b1, b2, b3, b4);  // after the reads above, in program order
-            mma_block<1>(rb, xs, 2, arow, half, 8, mul_t, sum_t, acc);
+            mma_block16(wst, xs, lane, 8, xmul[1], xsum, acc[0]);
         }
     }
 
@@ -447,7 +530,7 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
     float *red = reinterpret_cast<float *>(wslots);
     red[wave * 64 + lane] = acc[0];
     __syncthreads();
-    if (active && kw == 0 && half == 0) {
+    if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
         float v = 0.f;
         for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
         const int n = n0 + col;
