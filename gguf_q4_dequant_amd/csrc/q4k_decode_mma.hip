@@ -437,24 +437,26 @@ void decode_mma_kernel(Batch bt) {
 // activations of its own super-blocks (one group of 8 per lane for a pair),
 // so no wave waits for another before the final sum.
 constexpr int kWideWaves = 16;
-constexpr int kWideThreads = 64 * kWideWaves;
 constexpr int kWideMaxGroups = 512;  // about two rounds of one workgroup per CU
 
-// Waves per tile: the power of two (at most 16) that leaves each wave two
-// super-blocks or fewer where possible.
-__host__ __device__ inline int wide_wpt(int KB) {
+// Waves per tile: the power of two (at most the workgroup's WAVES) that
+// leaves each wave two super-blocks or fewer where possible.
+__host__ __device__ inline int wide_wpt(int KB, int waves) {
     int w = 1;
-    while (w < kWideWaves && 2 * w < KB) w *= 2;
+    while (w < waves && 2 * w < KB) w *= 2;
     return w;
 }
 
-__global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
+// WAVES = 16 (one workgroup per CU: launches of about two rounds at most) or
+// 4 (several workgroups per CU: long launches of short rows).
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     // Per wave: a weight slot, and the staged activations of a pair of
     // super-blocks with their sub-block sums and scale factors.
-    __shared__ __attribute__((aligned(16))) uint8_t wslots[kWideWaves * kStage];
-    __shared__ __attribute__((aligned(16))) uint4 xsw[kWideWaves][2 * 64];
-    __shared__ float xsumw[kWideWaves][2 * 8];
-    __shared__ float xmulw[kWideWaves][2];
+    __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kStage];
+    __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][2 * 64];
+    __shared__ float xsumw[WAVES][2 * 8];
+    __shared__ float xmulw[WAVES][2];
     const int g = static_cast<int>(blockIdx.x);
     int p = 0;
     for (int i = 1; i < bt.count; ++i)
@@ -462,8 +464,8 @@ __global__ __launch_bounds__(kWideThreads) void decode_wide_kernel(Batch bt) {
     const DevProblem &P = bt.p[p];
     const int N = P.N, K = P.K;
     const int KB = K >> 8;
-    const int wpt = wide_wpt(KB);
-    const int T = kWideWaves / wpt;
+    const int wpt = wide_wpt(KB, WAVES);
+    const int T = WAVES / wpt;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -551,6 +553,17 @@ hipError_t launch_np(const Batch &b, int lds, int grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Workgroups of a sixteen- or four-wave launch over the batch.
+int wide_groups(const Batch &b, int waves) {
+    int groups = 0;
+    for (int i = 0; i < b.count; ++i) {
+        const int T = waves / wide_wpt(b.p[i].K / kBlockWeights, waves);
+        groups += ((b.p[i].N + kCols - 1) / kCols + T - 1) / T;
+    }
+    return groups;
+}
+
+template <int WAVES>
 hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
     Batch sb;
     sb.count = b.count;
@@ -559,7 +572,7 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
     for (int i = 0; i < b.count; ++i) {
         sb.p[i] = b.p[order[i]];
         const int KB = sb.p[i].K / kBlockWeights;
-        const int T = kWideWaves / wide_wpt(KB);
+        const int T = WAVES / wide_wpt(KB, WAVES);
         const int tiles = (sb.p[i].N + kCols - 1) / kCols;
         sb.p[i].tile_begin = groups;
         sb.p[i].tiles = (tiles + T - 1) / T;
@@ -567,7 +580,7 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
         groups += sb.p[i].tiles;
     }
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_wide_kernel, dim3(groups), dim3(kWideThreads), 0, stream, sb);
+    hipLaunchKernelGGL(decode_wide_kernel<WAVES>, dim3(groups), dim3(64 * WAVES), 0, stream, sb);
     return hipGetLastError();
 }
 
@@ -584,16 +597,15 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             order[j - 1] = o;
         }
     if (b.M == 1) {
-        // One workgroup of sixteen waves per CU: best when the launch fits in
-        // about two rounds; larger launches go to the fp32 GEMV family, whose
-        // small workgroups keep every CU busy across rounds.
-        int groups = 0;
-        for (int i = 0; i < b.count; ++i) {
-            const int T = kWideWaves / wide_wpt(b.p[i].K / kBlockWeights);
-            groups += ((b.p[i].N + kCols - 1) / kCols + T - 1) / T;
-        }
-        if (groups > kWideMaxGroups) return launch_decode(b, stream);
-        return launch_wide(b, order, stream);
+        // Sixteen waves per workgroup (one per CU) when the launch fits in
+        // about two rounds; otherwise four-wave workgroups (several per CU keep
+        // every CU busy across rounds) if no wave gets more than two
+        // super-blocks, else the fp32 GEMV family.
+        if (wide_groups(b, kWideWaves) <= kWideMaxGroups) return launch_wide<kWideWaves>(b, order, stream);
+        int maxkb = 0;
+        for (int i = 0; i < b.count; ++i) maxkb = max(maxkb, b.p[i].K / kBlockWeights);
+        if (maxkb <= 8) return launch_wide<4>(b, order, stream);
+        return launch_decode(b, stream);
     }
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
     // caller forces this path) are done 16 at a time.
@@ -617,7 +629,7 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         const int M = sb.M;
         int ident[kMaxBatch];
         for (int i = 0; i < b.count; ++i) ident[i] = i;
-        const hipError_t e = M <= 1   ? launch_wide(sb, ident, stream)
+        const hipError_t e = M <= 1   ? launch_wide<kWideWaves>(sb, ident, stream)
                              : M <= 4 ? launch_np<2>(sb, lds, tiles, stream)
                              : M <= 8 ? launch_np<4>(sb, lds, tiles, stream)
                                       : launch_np<8>(sb, lds, tiles, stream);
