@@ -55,15 +55,11 @@ struct Buffer {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-struct Scratch {
-    Buffer counters;  // zero outside kernels
-    Buffer partials;
-};
 std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, Scratch> g_ws;
+std::map<std::pair<int, uintptr_t>, Buffer> g_ws;
 
-// Grow `b` to at least `bytes`; a new buffer is zero-filled when `zero` is set.
-hipError_t grow(Buffer &b, size_t bytes, bool zero, hipStream_t stream) {
+// Grow `b` to at least `bytes`.
+hipError_t grow(Buffer &b, size_t bytes, hipStream_t stream) {
     if (b.bytes >= bytes) return hipSuccess;
     hipError_t err;
     if (b.ptr) {
@@ -80,35 +76,23 @@ hipError_t grow(Buffer &b, size_t bytes, bool zero, hipStream_t stream) {
         b.ptr = nullptr;
         return err;
     }
-    if (zero) {
-        err = hipMemsetAsync(b.ptr, 0, want, stream);
-        if (err != hipSuccess) return err;
-    }
     b.bytes = want;
     return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t workspace(hipStream_t stream, size_t counter_bytes, size_t partial_bytes,
-                     unsigned **counters, float **partials) {
-    *counters = nullptr;
-    *partials = nullptr;
+hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch) {
+    *scratch = nullptr;
+    if (bytes == 0) return hipSuccess;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Scratch &s = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
-    if (counter_bytes) {
-        err = grow(s.counters, counter_bytes, true, stream);
-        if (err != hipSuccess) return err;
-        *counters = static_cast<unsigned *>(s.counters.ptr);
-    }
-    if (partial_bytes) {
-        err = grow(s.partials, partial_bytes, false, stream);
-        if (err != hipSuccess) return err;
-        *partials = static_cast<float *>(s.partials.ptr);
-    }
+    Buffer &b = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    err = grow(b, bytes, stream);
+    if (err != hipSuccess) return err;
+    *scratch = static_cast<float *>(b.ptr);
     return hipSuccess;
 }
 
@@ -137,11 +121,9 @@ int run(const q4k_problem *problems, int count, int M, int path, hipStream_t str
         d.N = q.N;
         d.K = q.K;
         d.part = nullptr;
-        d.cnt = nullptr;
         d.tile_begin = 0;
         d.tiles = 0;
         d.splits = 1;
-        d.pad_ = 0;
     }
     if (b.count == 0) return Q4K_OK;
     const int dev_rc = check_device();

@@ -267,9 +267,8 @@ hipError_t launch_mt(Batch &b, hipStream_t stream) {
         if (d.splits > 1) n_part += static_cast<size_t>(d.splits) * b.M * d.N;
     }
     if (n_part) {
-        unsigned *unused = nullptr;
         float *part = nullptr;
-        hipError_t err = workspace(stream, 0, n_part * sizeof(float), &unused, &part);
+        hipError_t err = workspace(stream, n_part * sizeof(float), &part);
         if (err != hipSuccess) return err;
         for (int i = 0; i < b.count; ++i) {
             DevProblem &d = b.p[i];

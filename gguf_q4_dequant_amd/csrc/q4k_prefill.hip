@@ -3,17 +3,21 @@
 //
 //   1. x (fp32) is rounded once to binary16 (nearest even) into the library
 //      workspace by a small pre-pass (each distinct x of a batch once).
-//   2. The GEMM streams 256x64 tiles of x (binary16) and of W into
-//      double-buffered LDS.  W tiles are dequantized on the way in: every
-//      weight is w = d*sc_j*q - dmin*m_j evaluated in fp32 (exact products, one
-//      rounding) and then rounded once to binary16 (nearest even).
-//   3. v_mfma_f32_32x32x16_f16 multiplies them with fp32 accumulation: eight
-//      waves (two per SIMD, so that one wave's matrix-core work hides the
-//      other's loads and dequantization), each owning a 128x64 block of the
-//      256x256 output tile in the accumulation registers.
-// While the matrix cores work on k-step s, the waves already load k-step s+1
-// into registers; after the MFMAs they store it (x as is, W dequantized) into
-// the other LDS buffer.
+//   2. W is dequantized to binary16 on the way to the matrix cores: every
+//      weight w = d*sc_j*q - dmin*m_j is rounded once (nearest even) from its
+//      exact value by the mixed-precision FMA.
+//   3. v_mfma_f32_32x32x16_f16 multiplies them with fp32 accumulation.
+//
+// Two tile shapes, both through double-buffered LDS:
+//   * M > 64: 256x256 tiles, eight waves (two per SIMD, so that one wave's
+//     matrix-core work hides the other's loads and dequantization), each
+//     owning a 128x64 block of the output tile.  While the matrix cores work
+//     on k-step s the waves load k-step s+1 into registers; after the MFMAs
+//     they store it into the other LDS buffer.
+//   * M <= 64: 32x128 tiles, four waves of 32x32, a register ring eight
+//     k-steps deep, and K cut into chunks of at most eight blocks (one
+//     workgroup each, partial tiles summed in chunk order by a second kernel),
+//     so that short and long K even out and each CU holds several workgroups.
 //
 // Tile order: workgroup i runs on XCD i % 8, so consecutive tiles are dealt
 // out XCD by XCD: each XCD receives a contiguous run of tiles in which the
@@ -23,11 +27,40 @@
 namespace q4k {
 namespace {
 
-constexpr int kBM = 256;  // rows of x per tile
-constexpr int kBN = 256;  // rows of W per tile
 constexpr int kBK = 64;   // k per step: one 32-byte quant group = two sub-blocks
-constexpr int kThreads = 512;
 constexpr int kXcds = 8;
+
+// Tile shape: BM rows of x by BN rows of W per workgroup, 2*BN threads (two
+// per W row for dequantization), waves in a WM x WN grid each owning a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
+template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_>
+struct Shape {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
+    // Split K: a problem's K is cut into ceil(K/256 / CHUNK) near-equal
+    // chunks, one workgroup each (0: never split).  The cut depends on the
+    // problem alone, so its result does not depend on the batch around it.
+    static constexpr int kChunkBlocks = CHUNK_;
+    static constexpr int kThreads = 2 * BN;
+    static constexpr int kWaves = kThreads / 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int TA = TM / 32, TB = TN / 32;  // MFMA tiles per wave
+    static constexpr int XC = BM * 8 / kThreads;       // 16-byte x chunks per thread per step
+    static constexpr int XROWS = kThreads / 8;         // x rows per chunk index
+    static constexpr size_t kLds = 2 * static_cast<size_t>(BM + BN) * 8 * 16;  // two buffers
+    static_assert(WM * WN == kWaves && TA >= 1 && TB >= 1, "wave grid");
+    static_assert(XC >= 1 && (BM * 8) % kThreads == 0, "x loader");
+    static_assert(R == 1 || R % 4 == 0, "ring: one step, or whole 256-deep blocks");
+    static_assert(R == 1 || (TA == 1 && TB == 1), "ring pipeline: one MFMA block per wave");
+};
+// Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
+using BigTile = Shape<256, 256, 2, 4, 1, 0>;
+// Few tokens (the W stream dominates and the output tiles alone would leave
+// about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
+// steps (two blocks) ahead, K cut into chunks of at most 8 blocks, so that
+// long and short K even out and CUs hold several workgroups.
+using SmallTile = Shape<32, 128, 1, 4, 8, 8>;
+constexpr int kSmallTileMaxM = 64;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -93,29 +126,59 @@ __device__ __forceinline__ void decode_header(const uint4 &hd, RowScales &r) {
     r.mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
 }
 
-__device__ __forceinline__ float byte_f(uint32_t v, int e) { return static_cast<float>((v >> (8 * e)) & 0xFFu); }
-
-// f32 weight -> binary16 with two separate roundings (f32, then nearest-even
-// binary16).  The empty asm keeps the compiler from fusing the FMA and the
-// conversion into one mixed-precision FMA, which would round only once.
-__device__ __forceinline__ float opaque(float v) {
-    asm("" : "+v"(v));
-    return v;
+// Binary16 weights, each w = a*q - c rounded once (nearest even) from its
+// exact value: the mixed-precision FMA reads a binary16 source exactly,
+// fuses, and rounds the result once to binary16.  q enters as a binary16
+// subnormal: a nibble masked into the low bits of a half is q*2^-24 exactly
+// (q*2^-20 for a high nibble left in place), and `a` carries the matching
+// 2^24 (2^20), so the product is d*sc*q exactly.
+//   e holds (q0, q2) and o holds (q1, q3) in their two halves; the result is
+// the packed pair (w0, w1) for half 0 and (w2, w3) for half 1.
+__device__ __forceinline__ uint32_t mix_pair_lo(float a, uint32_t e, uint32_t o, float c) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%4 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, %3, -%4 op_sel_hi:[0,1,0]"
+        : "=&v"(r)
+        : "v"(a), "v"(e), "v"(o), "v"(c));
+    return r;
+}
+__device__ __forceinline__ uint32_t mix_pair_hi(float a, uint32_t e, uint32_t o, float c) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%4 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, %3, -%4 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+        : "=&v"(r)
+        : "v"(a), "v"(e), "v"(o), "v"(c));
+    return r;
 }
 
-// LDS tiles hold 256 rows of 64 halves (128 bytes = 8 chunks of 16 bytes) with
-// no padding; chunk c of row r sits in slot c ^ ((r >> 1) & 7).  Sixteen
+// Sixteen weights from the four quant bytes in `w` (k = 4 consecutive bytes):
+// low nibbles (scale a_lo, offset c_lo) into lo[0..3]/lo[4..7] halves and high
+// nibbles (a_hi, c_hi) likewise, natural k order.  a_lo = d*sc*2^24 and
+// a_hi = d*sc*2^20.
+struct WordWeights {
+    uint32_t lo01, lo23, hi01, hi23;
+};
+__device__ __forceinline__ WordWeights dequant_word(uint32_t w, float a_lo, float c_lo, float a_hi, float c_hi) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t e = w & 0x000F000Fu, o = w8 & 0x000F000Fu;     // bytes 0,2 / 1,3, low nibbles
+    const uint32_t eh = w & 0x00F000F0u, oh = w8 & 0x00F000F0u;   // high nibbles, left in place
+    return {mix_pair_lo(a_lo, e, o, c_lo), mix_pair_hi(a_lo, e, o, c_lo), mix_pair_lo(a_hi, eh, oh, c_hi),
+            mix_pair_hi(a_hi, eh, oh, c_hi)};
+}
+
+// LDS tiles hold rows of 64 halves (128 bytes = 8 chunks of 16 bytes) with no
+// padding; chunk c of row r sits in slot c ^ ((r >> 1) & 7).  Sixteen
 // lanes reading chunk c of 16 consecutive rows then touch 16 distinct
 // (row parity, slot) pairs, i.e. all 64 banks once.
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(Batch bt, GemmArgs ga) {
+template <class S, int MINB>
+__global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, GemmArgs ga) {
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];  // 16-byte slots
-    constexpr int kTileSlots = 256 * 8;  // one 256x64 binary16 tile
-    // buffer b: x tile at lds4 + 2*b*kTileSlots, W tile right after it
-    auto As = [&](int b) { return lds4 + 2 * b * kTileSlots; };
-    auto Bs = [&](int b) { return lds4 + (2 * b + 1) * kTileSlots; };
+    // buffer b: the x tile (BM x 64 halves) then the W tile (BN x 64 halves)
+    auto As = [&](int b) { return lds4 + b * (S::BM + S::BN) * 8; };
+    auto Bs = [&](int b) { return lds4 + b * (S::BM + S::BN) * 8 + S::BM * 8; };
 
     // Workgroup i is dispatched to XCD i % 8; each XCD walks its own range of
     // tiles (the host balances the ranges by work), so that tiles sharing an
@@ -134,151 +197,356 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(Batch bt, GemmArgs
     const int K = P.K;
     const int M = bt.M;
     const int KB = K >> 8;
-    const int local = tile - P.tile_begin;
-    // N tiles of one M tile are adjacent: an XCD keeps its x tile in L2 while
-    // it walks along W.
-    const int n_tiles = (N + kBN - 1) / kBN;
-    const int tm0 = (local / n_tiles) * kBM;
-    const int tn0 = (local % n_tiles) * kBN;
+    // The K chunks of one output tile are adjacent, and N tiles of one M tile
+    // are adjacent: an XCD keeps its x tile in L2 while it walks along W.
+    const int splits = P.splits;
+    const int local = (tile - P.tile_begin) / splits;
+    const int sidx = tile - P.tile_begin - local * splits;
+    const int kb0 = sidx * KB / splits;
+    const int kbn = (sidx + 1) * KB / splits - kb0;  // >= 1
+    const int n_tiles = (N + S::BN - 1) / S::BN;
+    const int tm0 = (local / n_tiles) * S::BM;
+    const int tn0 = (local % n_tiles) * S::BN;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+    const int wm = wave / S::WN, wn = wave % S::WN;
 
-    // Loader: thread t moves 16-byte chunks f = t + 512*j (j < 4) of the
-    // 256x64 binary16 x tile (row f/8, chunk f%8; rows past M re-read row M-1,
+    // Loader: thread t moves 16-byte chunks f = t + threads*j (j < XC) of the
+    // BMx64 binary16 x tile (row f/8, chunk f%8; rows past M re-read row M-1,
     // whose results are never stored), and dequantizes quant chunk t%2 of row
     // t/2 of the W tile (16 quant bytes: 16 weights of each of the two
     // sub-blocks of this k-step).
-    const _Float16 *xcol = XH + 8 * (t & 7);
+    const _Float16 *xcol = XH + static_cast<size_t>(kb0) * kBlockWeights + 8 * (t & 7);
     const int xr0 = tm0 + (t >> 3);
     auto x_chunk = [&](int j, int s) {
-        const size_t row = static_cast<size_t>(min(xr0 + 64 * j, M - 1));
+        const size_t row = static_cast<size_t>(min(xr0 + S::XROWS * j, M - 1));
         return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
     };
     const int wr = t >> 1, wh = t & 1;
-    const uint8_t *wrow = W + static_cast<size_t>(min(tn0 + wr, N - 1)) * KB * kBlockBytes;
+    const uint8_t *wrow = W + (static_cast<size_t>(min(tn0 + wr, N - 1)) * KB + kb0) * kBlockBytes;
 
-    const int steps = KB * 4;
-    uint32_t lo_mask, hi_mask;
-    asm("s_mov_b32 %0, 0x0f0f0f0f" : "=s"(lo_mask));
-    asm("s_mov_b32 %0, 0xf0f0f0f0" : "=s"(hi_mask));
+    const int steps = kbn * 4;
     // Raw data of the next step, loaded while the current one runs on the
     // matrix cores (named registers: arrays of these end up in scratch).
-    uint4 x0, x1, x2, x3, wq, whd;
+    // Register ring of R slots: slot r holds the raw data of a k-step s with
+    // s % R == r.  Slot indices are compile-time (the step loop is unrolled
+    // by R), and with R a multiple of 4 so is the quant group s % 4 of a slot.
+    // Requests past the last step re-read the last step (clamped address,
+    // never used): the loads stay unconditional, so the waits before a slot
+    // is used count only the newer requests.
+    constexpr int R = S::R;
+    uint4 xr[R][S::XC], wq[R], whd[R];
     RowScales rs;
-    auto load_stage = [&](int s) {
-        x0 = x_chunk(0, s);
-        x1 = x_chunk(1, s);
-        x2 = x_chunk(2, s);
-        x3 = x_chunk(3, s);
-        const int kb = s >> 2, g = s & 3;
+    auto load_stage = [&](int r, int s_req) {
+        const int s = min(s_req, steps - 1);
+#pragma unroll
+        for (int j = 0; j < S::XC; ++j) xr[r][j] = x_chunk(j, s);
+        const int kb = s >> 2;
         const uint8_t *blk = wrow + static_cast<size_t>(kb) * kBlockBytes;
-        whd = *reinterpret_cast<const uint4 *>(blk);  // used when g == 0
-        wq = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * g + 16 * wh);
+        if (R == 1 || r % 4 == 0) whd[r] = *reinterpret_cast<const uint4 *>(blk);  // used when g == 0
+        wq[r] = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * (s & 3) + 16 * wh);
     };
-    auto store_stage = [&](int s, uint4 *A, uint4 *B) {
-        A[swz((t >> 3) + 0, t & 7)] = x0;
-        A[swz((t >> 3) + 64, t & 7)] = x1;
-        A[swz((t >> 3) + 128, t & 7)] = x2;
-        A[swz((t >> 3) + 192, t & 7)] = x3;
-        const int g = s & 3;
-        if (g == 0) decode_header(whd, rs);
+    auto store_stage = [&](int r, int s, uint4 *A, uint4 *B) {
+#pragma unroll
+        for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = xr[r][j];
+        const int g = R == 1 ? (s & 3) : (r & 3);
+        if (g == 0) decode_header(whd[r], rs);
         // sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles, k 32..63);
         // quant byte l of the group -> k = l and k = 32 + l
         const uint32_t scw = g < 2 ? rs.scA : rs.scB;
         const uint32_t mnw = g < 2 ? rs.mnA : rs.mnB;
         const int sh = (g & 1) * 16;
-        const float a_lo = rs.d * static_cast<float>((scw >> sh) & 0xFFu);
-        const float a_hi = rs.d * 0.0625f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
+        const float a_lo = rs.d * 16777216.0f * static_cast<float>((scw >> sh) & 0xFFu);
+        const float a_hi = rs.d * 1048576.0f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
         const float c_lo = rs.dmin * static_cast<float>((mnw >> sh) & 0xFFu);
         const float c_hi = rs.dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
         auto two_chunks = [&](uint32_t w0, uint32_t w1, int v) {
-            half8 lo, hi;
-            const uint32_t l0 = w0 & lo_mask, h0 = w0 & hi_mask, l1 = w1 & lo_mask, h1 = w1 & hi_mask;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lo[e] = (_Float16)opaque(__builtin_fmaf(a_lo, byte_f(l0, e), -c_lo));
-                hi[e] = (_Float16)opaque(__builtin_fmaf(a_hi, byte_f(h0, e), -c_hi));
-                lo[4 + e] = (_Float16)opaque(__builtin_fmaf(a_lo, byte_f(l1, e), -c_lo));
-                hi[4 + e] = (_Float16)opaque(__builtin_fmaf(a_hi, byte_f(h1, e), -c_hi));
-            }
-            B[swz(wr, v)] = __builtin_bit_cast(uint4, lo);
-            B[swz(wr, 4 + v)] = __builtin_bit_cast(uint4, hi);
+            const WordWeights p = dequant_word(w0, a_lo, c_lo, a_hi, c_hi);
+            const WordWeights q = dequant_word(w1, a_lo, c_lo, a_hi, c_hi);
+            B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
+            B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
         };
-        two_chunks(wq.x, wq.y, 2 * wh);
-        two_chunks(wq.z, wq.w, 2 * wh + 1);
+        two_chunks(wq[r].x, wq[r].y, 2 * wh);
+        two_chunks(wq[r].z, wq[r].w, 2 * wh + 1);
     };
 
-    float16v acc[4][2];
+    float16v acc[S::TA][S::TB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < S::TA; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < S::TB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     auto mma_step = [&](const uint4 *A, const uint4 *B) {
 #pragma unroll
         for (int kk = 0; kk < kBK / 8; kk += 2) {  // 16 k per MFMA = 2 chunks
-            half8 af[4], bf[2];
+            half8 af[S::TA], bf[S::TB];
             const int c = kk + (lane >> 5);
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                af[a] = __builtin_bit_cast(half8, A[swz(128 * wm + 32 * a + (lane & 31), c)]);
+            for (int a = 0; a < S::TA; ++a)
+                af[a] = __builtin_bit_cast(half8, A[swz(S::TM * wm + 32 * a + (lane & 31), c)]);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                bf[b] = __builtin_bit_cast(half8, B[swz(64 * wn + 32 * b + (lane & 31), c)]);
+            for (int b = 0; b < S::TB; ++b)
+                bf[b] = __builtin_bit_cast(half8, B[swz(S::TN * wn + 32 * b + (lane & 31), c)]);
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < S::TA; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < S::TB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
         }
     };
 
-    // Pipeline: LDS buffer s%2 holds step s; the registers hold step s+1,
-    // loaded while step s runs on the matrix cores.
-    load_stage(0);
-    store_stage(0, As(0), Bs(0));
+    // Pipeline: LDS buffer s%2 holds step s while it runs on the matrix
+    // cores; meanwhile step s+1 moves from its ring slot into the other
+    // buffer and step s+1+R is requested into the slot it left.  Step 0 goes
+    // straight to LDS; steps 1..R start in the ring.
+    load_stage(0, 0);
+    store_stage(0, 0, As(0), Bs(0));
+#pragma unroll
+    for (int r = 1; r <= R; ++r) load_stage(r % R, r);
     __syncthreads();
-    for (int s = 0; s < steps; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < steps) load_stage(s + 1);
-        mma_step(As(cur), Bs(cur));
-        if (s + 1 < steps) store_stage(s + 1, As(cur ^ 1), Bs(cur ^ 1));
-        __syncthreads();
+    // Few-token tiles (one 32x32 block per wave): every fragment of the step
+    // is requested from LDS first, the next step is dequantized while they
+    // arrive, and the MFMAs alternate between two accumulators so that
+    // consecutive ones do not wait on each other.
+    float16v acc2[S::TA][S::TB];
+    if constexpr (S::R > 1) {
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a)
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc2[a][b][r] = 0.f;
     }
-
-    // D layout of a 32x32 MFMA tile: lane l, register r ->
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    auto step = [&](int s, int d) {  // d = s % R, compile-time
+        const uint4 *A = As(d & 1), *B = Bs(d & 1);
+        half8 af[kBK / 16], bf[kBK / 16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+        for (int q = 0; q < kBK / 16; ++q) {
+            const int c = 2 * q + (lane >> 5);
+            af[q] = __builtin_bit_cast(half8, A[swz(S::TM * wm + (lane & 31), c)]);
+            bf[q] = __builtin_bit_cast(half8, B[swz(S::TN * wn + (lane & 31), c)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the three phases in this order
+        store_stage((d + 1) % R, s + 1, As((d + 1) & 1), Bs((d + 1) & 1));  // past the end: unused
+        load_stage((d + 1) % R, s + 1 + R);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = tn0 + 64 * wn + 32 * b + (lane & 31);
+        for (int q = 0; q < kBK / 16; q += 2) {
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q], bf[q], acc[0][0], 0, 0, 0);
+            acc2[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q + 1], bf[q + 1], acc2[0][0], 0, 0, 0);
+        }
+        __syncthreads();
+    };
+    int s0 = 0;
+    if constexpr (R == 1) {
+        for (; s0 < steps; ++s0) {
+            mma_step(As(s0 & 1), Bs(s0 & 1));
+            if (s0 + 1 < steps) {
+                store_stage(0, s0 + 1, As((s0 + 1) & 1), Bs((s0 + 1) & 1));
+                if (s0 + 2 < steps) load_stage(0, s0 + 2);
+            }
+            __syncthreads();
+        }
+    } else {
+        for (; s0 + R <= steps; s0 += R) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = tm0 + 128 * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N) P.y[static_cast<size_t>(m) * N + n] = acc[a][b][r];
+            for (int d = 0; d < R; ++d) step(s0 + d, d);
+        }
+        // Tail: whole blocks of four steps (steps is a multiple of 4).
+#pragma unroll
+        for (int d0 = 0; d0 < R; d0 += 4) {
+            if (s0 + d0 < steps) {
+#pragma unroll
+                for (int d = d0; d < d0 + 4; ++d) step(s0 + d, d);
             }
         }
     }
+
+    if constexpr (S::R > 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc2[0][0][r];
+    }
+    // D layout of a 32x32 MFMA tile: lane l, register r ->
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    auto for_each_out = [&](auto &&f) {
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a) {
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b) {
+                const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, acc[a][b][r]);
+                }
+            }
+        }
+    };
+    if (S::kChunkBlocks == 0 || splits == 1) {
+        for_each_out([&](size_t e, float v) { P.y[e] = v; });
+        return;
+    }
+    // Split K: store this chunk's partial tile ([splits][M][N] in the
+    // workspace); split_sum_kernel adds the chunks in order afterwards.  (A
+    // last-arriving workgroup could add them in place, but the device-scope
+    // release it needs writes back the whole L2 of its XCD each time, which
+    // costs far more than the second launch.)
+    float *part = P.part + static_cast<size_t>(sidx) * M * N;
+    for_each_out([&](size_t e, float v) { part[e] = v; });
 }
 
-constexpr size_t kLdsBytes = 4 * 256 * 8 * 16;  // two buffers of x and W tiles, 32 KiB each
+// y = sum over chunks of the partial sums, in chunk order, for split problems
+// (four outputs per thread).
+__global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
+    int p = 0;
+    for (int i = 1; i < bt.count; ++i)
+        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
+    const DevProblem &P = bt.p[p];
+    const size_t e = (static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x) * 4;
+    const size_t total = static_cast<size_t>(bt.M) * P.N;
+    if (e >= total) return;
+    if (e + 4 <= total && (total & 3) == 0) {
+        float4 v = *reinterpret_cast<const float4 *>(P.part + e);
+        for (int c = 1; c < P.splits; ++c) {
+            const float4 u = *reinterpret_cast<const float4 *>(P.part + static_cast<size_t>(c) * total + e);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        *reinterpret_cast<float4 *>(P.y + e) = v;
+        return;
+    }
+    for (size_t i = e; i < min(e + 4, total); ++i) {
+        float v = P.part[i];
+        for (int c = 1; c < P.splits; ++c) v += P.part[static_cast<size_t>(c) * total + i];
+        P.y[i] = v;
+    }
+}
+
+// Launch plan of one tile shape: problems in order of decreasing K (the
+// longest tiles start first), their K splits, the tile space (each problem's
+// tiles back to back; the K chunks of an output tile adjacent, N tiles of
+// one M tile adjacent) and the XCD ranges.  The kernel looks a tile's problem
+// up by tile_begin, so the launch gets its own copy of the batch in order.
+struct Plan {
+    Batch sb;
+    int order[kMaxBatch];
+    int xcd_first[kXcds + 1];
+    int grid;
+    size_t partial_floats;  // [splits][M][N] per split problem
+};
+
+template <class S>
+void make_plan(const Batch &b, Plan &pl) {
+    Batch &sb = pl.sb;
+    sb.count = b.count;
+    sb.M = b.M;
+    for (int i = 0; i < b.count; ++i) pl.order[i] = i;
+    for (int i = 1; i < b.count; ++i)  // stable insertion sort by K, descending
+        for (int j = i; j > 0 && b.p[pl.order[j]].K > b.p[pl.order[j - 1]].K; --j) {
+            const int o = pl.order[j];
+            pl.order[j] = pl.order[j - 1];
+            pl.order[j - 1] = o;
+        }
+    const int m_tiles = (b.M + S::BM - 1) / S::BM;
+    for (int i = 0; i < b.count; ++i) {
+        sb.p[i] = b.p[pl.order[i]];
+        const int kb = sb.p[i].K / kBlockWeights;
+        constexpr int chunk = S::kChunkBlocks > 0 ? S::kChunkBlocks : 1 << 30;
+        sb.p[i].splits = (kb + chunk - 1) / chunk;
+    }
+    int tiles = 0;
+    long long work = 0;  // in 256-deep blocks, per workgroup the longest chunk of its problem
+    pl.partial_floats = 0;
+    auto unit_work = [&](const DevProblem &d) {
+        const int kb = d.K / kBlockWeights;
+        return static_cast<long long>((kb + d.splits - 1) / d.splits);
+    };
+    for (int i = 0; i < sb.count; ++i) {
+        DevProblem &d = sb.p[i];
+        const int outs = ((d.N + S::BN - 1) / S::BN) * m_tiles;
+        d.tile_begin = tiles;
+        d.tiles = outs * d.splits;
+        d.part = nullptr;
+        if (d.splits > 1) {
+            pl.partial_floats += static_cast<size_t>(d.splits) * b.M * d.N;
+        }
+        tiles += d.tiles;
+        work += d.tiles * unit_work(d);
+    }
+    // Cut the tile space into eight ranges of about equal work.
+    pl.xcd_first[0] = 0;
+    {
+        int i = 0;
+        long long done = 0;  // work of tiles before sb.p[i].tile_begin
+        for (int c = 1; c < kXcds; ++c) {
+            const long long goal = (work * c + kXcds / 2) / kXcds;
+            while (i < sb.count && done + sb.p[i].tiles * unit_work(sb.p[i]) <= goal) {
+                done += sb.p[i].tiles * unit_work(sb.p[i]);
+                ++i;
+            }
+            int cut = tiles;
+            if (i < sb.count) {
+                const long long per = unit_work(sb.p[i]);
+                cut = sb.p[i].tile_begin + static_cast<int>((goal - done + per / 2) / per);
+            }
+            pl.xcd_first[c] = max(cut, pl.xcd_first[c - 1]);
+        }
+        pl.xcd_first[kXcds] = tiles;
+    }
+    int longest = 0;
+    for (int c = 0; c < kXcds; ++c) longest = max(longest, pl.xcd_first[c + 1] - pl.xcd_first[c]);
+    pl.grid = longest * kXcds;
+}
+
+// Launch one tile shape (after the binary16 copies of x are queued).
+template <class S, int MINB>
+hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
+    static bool attr_set = false;  // per process; the attribute is a property of the function
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel<S, MINB>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(S::kLds));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (pl.grid == 0) return hipSuccess;
+    GemmArgs ga;
+    for (int c = 0; c <= kXcds; ++c) ga.xcd_first[c] = pl.xcd_first[c];
+    for (int i = 0; i < pl.sb.count; ++i) {
+        DevProblem &d = pl.sb.p[i];
+        ga.xh[i] = xh[pl.order[i]];
+        if (d.splits > 1) {
+            d.part = part;
+            part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<S, MINB>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, pl.sb, ga);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || pl.partial_floats == 0) return err;
+    Batch red;
+    red.count = 0;
+    red.M = pl.sb.M;
+    int blocks = 0;
+    for (int i = 0; i < pl.sb.count; ++i) {
+        const DevProblem &d = pl.sb.p[i];
+        if (d.splits == 1) continue;
+        DevProblem &r = red.p[red.count++];
+        r = d;
+        r.tile_begin = blocks;
+        blocks += static_cast<int>((static_cast<size_t>(pl.sb.M) * d.N + 1023) / 1024);
+    }
+    hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, red);
+    return hipGetLastError();
+}
 
 }  // namespace
 
 hipError_t launch_prefill(Batch &b, hipStream_t stream) {
-    static bool attr_set = false;  // per process; the attribute is a property of the function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     // Distinct activations, their binary16 copies in the workspace.
     const float *xs[kMaxBatch];
     size_t offs[kMaxBatch];
@@ -296,11 +564,21 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
         }
         which[i] = k;
     }
-    unsigned *unused = nullptr;
+    // Few tokens: the W stream dominates, small tiles (K split as needed)
+    // keep every CU busy.
+    const bool small = b.M <= kSmallTileMaxM;
+    Plan pl;
+    if (small)
+        make_plan<SmallTile>(b, pl);
+    else
+        make_plan<BigTile>(b, pl);
+    // Workspace: the binary16 activations, then the split-K partial sums.
+    const size_t part_off = (halves * sizeof(_Float16) + 255) & ~static_cast<size_t>(255);
     float *wsp = nullptr;
-    hipError_t err = workspace(stream, 0, halves * sizeof(_Float16), &unused, &wsp);
+    hipError_t err = workspace(stream, part_off + pl.partial_floats * sizeof(float), &wsp);
     if (err != hipSuccess) return err;
     _Float16 *xh_base = reinterpret_cast<_Float16 *>(wsp);
+    float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(wsp) + part_off);
 
     CvtBatch cb;
     cb.count = 0;
@@ -319,59 +597,10 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    // Tile space: problems in order of decreasing K (the longest tiles start
-    // first), each problem's tiles back to back, N tiles of one M tile
-    // adjacent.  The kernel looks a tile's problem up by tile_begin, so the
-    // launch gets its own copy of the batch in that order.
-    Batch sb;
-    sb.count = b.count;
-    sb.M = b.M;
-    GemmArgs ga;
-    int order[kMaxBatch];
-    for (int i = 0; i < b.count; ++i) order[i] = i;
-    for (int i = 1; i < b.count; ++i)  // stable insertion sort by K, descending
-        for (int j = i; j > 0 && b.p[order[j]].K > b.p[order[j - 1]].K; --j) {
-            const int o = order[j];
-            order[j] = order[j - 1];
-            order[j - 1] = o;
-        }
-    int tiles = 0;
-    long long work = 0;  // in 256-deep k blocks
-    const int m_tiles = (b.M + kBM - 1) / kBM;
-    for (int i = 0; i < b.count; ++i) {
-        sb.p[i] = b.p[order[i]];
-        ga.xh[i] = xh_base + offs[which[order[i]]];
-        sb.p[i].tile_begin = tiles;
-        sb.p[i].tiles = ((sb.p[i].N + kBN - 1) / kBN) * m_tiles;
-        tiles += sb.p[i].tiles;
-        work += static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights);
-    }
-    // Cut the tile space into eight ranges of about equal work.
-    ga.xcd_first[0] = 0;
-    {
-        int i = 0;
-        long long done = 0;  // work of tiles before sb.p[i].tile_begin
-        for (int c = 1; c < kXcds; ++c) {
-            const long long goal = (work * c + kXcds / 2) / kXcds;
-            while (i < sb.count && done + static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights) <= goal) {
-                done += static_cast<long long>(sb.p[i].tiles) * (sb.p[i].K / kBlockWeights);
-                ++i;
-            }
-            int cut = tiles;
-            if (i < sb.count) {
-                const long long per = sb.p[i].K / kBlockWeights;
-                cut = sb.p[i].tile_begin + static_cast<int>((goal - done + per / 2) / per);
-            }
-            ga.xcd_first[c] = max(cut, ga.xcd_first[c - 1]);
-        }
-        ga.xcd_first[kXcds] = tiles;
-    }
-    int longest = 0;
-    for (int c = 0; c < kXcds; ++c) longest = max(longest, ga.xcd_first[c + 1] - ga.xcd_first[c]);
-    const int grid = longest * kXcds;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(kThreads), kLdsBytes, stream, sb, ga);
-    return hipGetLastError();
+    const _Float16 *xh[kMaxBatch];
+    for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
+    if (small) return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
+    return launch_gemm<BigTile, 2>(pl, xh, part, stream);
 }
 
 }  // namespace q4k

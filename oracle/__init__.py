@@ -63,6 +63,8 @@ def _load():
     lib.q4k_oracle_encode_block.restype = None
     lib.q4k_oracle_dequant.argtypes = [u8p, i64, i64, f32p]
     lib.q4k_oracle_dequant.restype = ctypes.c_int
+    lib.q4k_oracle_dequant_f64.argtypes = [u8p, i64, i64, f64p]
+    lib.q4k_oracle_dequant_f64.restype = ctypes.c_int
     lib.q4k_oracle_threads.argtypes = [ctypes.c_int]
     lib.q4k_oracle_threads.restype = ctypes.c_int
     lib.q4k_oracle_matmul.argtypes = [u8p, f32p, i64, i64, i64, f64p, f64p, ctypes.c_int]
@@ -129,6 +131,17 @@ def dequant(w: np.ndarray, K: int) -> np.ndarray:
     return out
 
 
+def dequant_exact(w: np.ndarray, K: int) -> np.ndarray:
+    """Exact weights [N, K] as doubles (every Q4_K weight is a multiple of 2^-24
+    below 2^27, so a double holds it exactly)."""
+    w2 = _check_w(w, K)
+    out = np.empty((w2.shape[0], K), np.float64)
+    rc = _load().q4k_oracle_dequant_f64(_ptr(w2), w2.shape[0], K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"q4k_oracle_dequant_f64 failed ({rc})")
+    return out
+
+
 def threads_used(threads: int = 0) -> int:
     return _load().q4k_oracle_threads(int(threads))
 
@@ -152,8 +165,9 @@ def matmul_cols(w: np.ndarray, x: np.ndarray, N: int, K: int, cols, threads: int
                 fp16_operands: bool = False):
     """(y, s) restricted to the W rows in ``cols``: arrays of shape [M, len(cols)].
 
-    With ``fp16_operands`` both x and the f32 weights are rounded to binary16
-    (nearest, ties to even) before the exact product."""
+    With ``fp16_operands`` x (from its f32 value) and w (from its exact value)
+    are each rounded once to binary16 (nearest, ties to even) before the exact
+    product."""
     w2 = _check_w(w, K)
     if w2.shape[0] != N:
         raise ValueError("packed weight rows != N")

@@ -149,7 +149,11 @@ void q4k_oracle_encode_block(uint16_t dbits, uint16_t mbits, const uint8_t sc[8]
 }
 
 /* Dequantize one row of K/256 blocks to f32 (one rounding per weight). */
-static void dequant_row(const uint8_t *row, int64_t K, float *out)
+/* Exact weights of one row.  d and dmin are binary16, so both are integer
+ * multiples of 2^-24 below 2^16; with sc, m <= 63 and q <= 15 every weight
+ * d*sc*q - dmin*m is an integer multiple of 2^-24 below 2^27 in magnitude,
+ * which a double holds exactly (51 bits), and so do both products. */
+static void dequant_row_exact(const uint8_t *row, int64_t K, double *out)
 {
     double d, dmin;
     uint8_t sc[8], mn[8], q[256];
@@ -157,14 +161,35 @@ static void dequant_row(const uint8_t *row, int64_t K, float *out)
         q4k_oracle_decode_block(row + b * BLOCK_BYTES, &d, &dmin, sc, mn, q);
         for (int t = 0; t < QK; ++t) {
             int j = t / 32;
-            double exact = d * (double)sc[j] * (double)q[t] - dmin * (double)mn[j];
-            out[b * QK + t] = (float)exact;
+            out[b * QK + t] = d * (double)sc[j] * (double)q[t] - dmin * (double)mn[j];
         }
+    }
+}
+
+/* f32 weights: the exact weight rounded once to binary32. */
+static void dequant_row(const uint8_t *row, int64_t K, float *out)
+{
+    double blk[QK];
+    for (int64_t b = 0; b < K / QK; ++b) {
+        dequant_row_exact(row + b * BLOCK_BYTES, QK, blk);
+        for (int t = 0; t < QK; ++t)
+            out[b * QK + t] = (float)blk[t];
     }
 }
 
 /* Dequantize rows x K to f32, row-major [rows, K].  Returns 0, or -2 if K is
  * not a multiple of 256. */
+/* Exact weights as doubles, [rows, K]. */
+int q4k_oracle_dequant_f64(const uint8_t *w, int64_t rows, int64_t K, double *out)
+{
+    if (K % QK != 0 || rows < 0 || K < 0)
+        return -2;
+    int64_t row_bytes = (K / QK) * BLOCK_BYTES;
+    for (int64_t n = 0; n < rows; ++n)
+        dequant_row_exact(w + n * row_bytes, K, out + n * K);
+    return 0;
+}
+
 int q4k_oracle_dequant(const uint8_t *w, int64_t rows, int64_t K, float *out)
 {
     if (K % QK != 0 || rows < 0 || K < 0)
@@ -194,8 +219,9 @@ int q4k_oracle_threads(int threads) { return set_threads(threads); }
  *   y[m*ncols + c] = sum_k (double)x[m,k] * (double)w[cols[c], k]
  *   s[m*ncols + c] = sum_k |(double)x[m,k] * (double)w[cols[c], k]|
  * k ascends; each W row is dequantized to f32 first.  `fp16_operands`
- * rounds x and w to binary16 (nearest, ties to even) before the product,
- * which is the operand precision of a half-precision matrix-core path. */
+ * instead rounds x (from its f32 value) and w (from its exact value) once to
+ * binary16 (nearest, ties to even) before the product: the operands of a
+ * half-precision matrix-core path. */
 static int matmul_cols(const uint8_t *w, const float *x, int64_t M, int64_t N, int64_t K,
                        const int64_t *cols, int64_t ncols, double *y, double *s,
                        int threads, int fp16_operands)
@@ -220,18 +246,23 @@ static int matmul_cols(const uint8_t *w, const float *x, int64_t M, int64_t N, i
     {
         float *wrow = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
         double *wd = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
-        if (!wrow || !wd) {
+        double *wx = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        if (!wrow || !wd || !wx) {
 #pragma omp atomic write
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 4)
             for (int64_t c = 0; c < ncols; ++c) {
                 int64_t n = cols[c];
-                dequant_row(w + n * row_bytes, K, wrow);
-                for (int64_t k = 0; k < K; ++k)
-                    wd[k] = fp16_operands
-                                ? q4k_oracle_half_to_double(q4k_oracle_double_to_half_rne((double)wrow[k]))
-                                : (double)wrow[k];
+                if (fp16_operands) {
+                    dequant_row_exact(w + n * row_bytes, K, wx);
+                    for (int64_t k = 0; k < K; ++k)
+                        wd[k] = q4k_oracle_half_to_double(q4k_oracle_double_to_half_rne(wx[k]));
+                } else {
+                    dequant_row(w + n * row_bytes, K, wrow);
+                    for (int64_t k = 0; k < K; ++k)
+                        wd[k] = (double)wrow[k];
+                }
                 for (int64_t m = 0; m < M; ++m) {
                     double acc = 0.0, mag = 0.0;
                     for (int64_t k = 0; k < K; ++k) {
@@ -248,6 +279,7 @@ static int matmul_cols(const uint8_t *w, const float *x, int64_t M, int64_t N, i
         }
         free(wrow);
         free(wd);
+        free(wx);
     }
     free(xr);
     return failed ? -3 : 0;
@@ -276,8 +308,9 @@ int q4k_oracle_matmul_cols(const uint8_t *w, const float *x, int64_t M, int64_t 
     return matmul_cols(w, x, M, N, K, cols, ncols, y, s, threads, 0);
 }
 
-/* Same product with both operands first rounded to binary16 (ties to even):
- * the exact value a half-precision-operand, wide-accumulator path approaches. */
+/* Same product with both operands first rounded once to binary16 (ties to
+ * even; w from its exact value): the exact value a half-precision-operand,
+ * wide-accumulator path approaches. */
 int q4k_oracle_matmul_cols_f16(const uint8_t *w, const float *x, int64_t M, int64_t N, int64_t K,
                                const int64_t *cols, int64_t ncols, double *y, double *s,
                                int threads)

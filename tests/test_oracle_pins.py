@@ -75,8 +75,10 @@ def test_golden_blocks_dequantize_to_closed_form(golden_blocks):
     for g in golden_blocks:
         w = oracle.dequant(g.raw, 256)[0]
         exact = g.weights_exact()
-        # every golden weight is exactly representable in float32
-        assert all(Fraction(float(np.float32(float(v)))) == v for v in exact), g.name
+        # every golden weight but F's (built to sit between binary32 values) is
+        # exactly representable in float32
+        if g.name != "F":
+            assert all(Fraction(float(np.float32(float(v)))) == v for v in exact), g.name
         assert np.array_equal(w, g.weights_f32()), g.name
 
 
@@ -90,6 +92,32 @@ def test_closed_forms_written_in_fixture(golden_blocks):
     np.testing.assert_array_equal(by["D"], (2.0 ** -24 * ((j + 1) * (2 * j + t % 2) - 1023 * 2 * j))
                                   .astype(np.float32))
     np.testing.assert_array_equal(by["E"], (-(t % 16) - 1).astype(np.float32))
+    # F: (1 + 3*2^-11) - 2^-24 rounds to the binary32 tie 1 + 3*2^-11 (even fraction)
+    np.testing.assert_array_equal(by["F"], np.full(256, 1 + 3 * 2.0 ** -11, np.float32))
+
+
+def test_exact_dequant_matches_closed_forms(golden_blocks):
+    """dequant_exact returns the rational closed form exactly; dequant is it rounded once to f32."""
+    for g in golden_blocks:
+        exact = oracle.dequant_exact(g.raw.reshape(1, 144), 256)[0]
+        assert [Fraction(float(v)) for v in exact] == g.weights_exact(), g.name
+    w = qi.random_q4k(19, 1024, seed=31)
+    np.testing.assert_array_equal(oracle.dequant_exact(w, 1024).astype(np.float32), oracle.dequant(w, 1024))
+
+
+def test_binary16_weight_is_rounded_once_from_its_exact_value(golden_blocks):
+    """Block F separates one rounding (exact -> binary16) from two (exact -> f32 -> binary16)."""
+    g = {b.name: b for b in golden_blocks}["F"]
+    exact = Fraction(2051, 2048) - Fraction(1, 2 ** 24)
+    assert all(v == exact for v in g.weights_exact())
+    once = np.array([float(exact)], np.float64).astype(np.float16).view(np.uint16)[0]
+    twice = np.array([float(exact)], np.float32).astype(np.float16).view(np.uint16)[0]
+    assert (once, twice) == (0x3C01, 0x3C02)
+    assert oracle.double_to_half_rne(float(exact)) == 0x3C01
+    x = np.zeros((1, 256), np.float32)
+    x[0, 5] = 1.0
+    y, _ = oracle.matmul_cols(g.raw.reshape(1, 144), x, 1, 256, [0], fp16_operands=True)
+    assert y[0, 0] == float(np.float16(1 + 2 ** -10))
 
 
 def test_all_zero_quants_give_minus_dmin_times_m(golden_blocks):
@@ -213,18 +241,18 @@ def test_bruteforce_exact_rationals(M, N, KB):
 
 
 def test_fp16_operand_product_matches_numpy_rounding(golden_blocks):
-    """matmul_cols_f16 rounds x and the f32 weights to binary16 (ties to even)."""
+    """matmul_cols_f16 rounds x and the exact weights once to binary16 (ties to even)."""
     by = {g.name: g for g in golden_blocks}
-    names = ["B", "D", "A"]
+    names = ["B", "D", "A", "F"]
     w = np.stack([by[n].raw for n in names])
     rng = np.random.default_rng(3)
     x = rng.standard_normal((4, 256)).astype(np.float32)
     x[0, :8] = np.float32(1 + 2 ** -11)       # ties that round down to even
     x[0, 8:16] = np.float32(1 + 3 * 2 ** -11)  # ties that round up to even
-    y, _ = oracle.matmul_cols(w, x, 3, 256, [0, 1, 2], fp16_operands=True)
+    y, _ = oracle.matmul_cols(w, x, 4, 256, [0, 1, 2, 3], fp16_operands=True)
     x16 = x.astype(np.float16).astype(np.float64)
     for c, n in enumerate(names):
-        w16 = by[n].weights_f32().astype(np.float16).astype(np.float64)
+        w16 = np.array([float(v) for v in by[n].weights_exact()]).astype(np.float16).astype(np.float64)
         for m in range(4):
             ex = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x16[m], w16))
             assert abs(Fraction(y[m, c]) - ex) <= Fraction(256, 2 ** 52) * sum(

@@ -80,10 +80,9 @@ def test_one_hot_returns_weights(path):
     ks = [0, 1, 31, 32, 33, 63, 64, 100, 255, 256, 511, 700, 1023]
     x = qi.one_hot_x(len(ks), K, ks)
     y = _run(w, x, N, path)
-    wf = oracle.dequant(w, K)
-    want = wf[:, ks].T
-    if path == PRE:
-        want = want.astype(np.float16).astype(np.float32)  # binary16 operands, nearest-even
+    want = oracle.dequant(w, K)[:, ks].T
+    if path == PRE:  # binary16 operands: the exact weight rounded once, nearest-even
+        want = oracle.dequant_exact(w, K)[:, ks].T.astype(np.float16).astype(np.float32)
     assert np.array_equal(y, want)
 
 
@@ -96,8 +95,8 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     y = _run(rows, x, len(golden_blocks), path)
     for n, g in enumerate(golden_blocks):
         want = g.weights_f32()[ks]
-        if path == PRE:
-            want = want.astype(np.float16).astype(np.float32)
+        if path == PRE:  # the exact weight rounded once to binary16
+            want = np.array([float(v) for v in g.weights_exact()])[ks].astype(np.float16).astype(np.float32)
         assert np.array_equal(y[:, n], want), g.name
 
 
@@ -106,12 +105,13 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     (DEC, 9, (5, 7), True),
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
     (DEC, 9, (5, 6), False),
-    (PRE, 9, (5, 6), True),
-    (PRE, 200, (130, 131), True),
+    (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
+    (PRE, 200, (66, 133), True),  # chunks above 64 tokens: 256x256 tiles
+    (PRE, 200, (130, 131), False),  # mixes both tile shapes (different k order): same values to rounding
 ])
 def test_row_split_invariance(path, M, cuts, bitwise):
     """An M-row call equals calls on row chunks (the nx runner's mixed-chunk gates)."""
-    N, K = 140, 1536
+    N, K = (140, 1536) if path == DEC else (140, 2304)  # prefill: small tiles cut K in two
     w, x = _inputs(M, N, K, 4)
     y = _run(w, x, N, path)
     bounds = (0,) + cuts + (M,)
@@ -119,9 +119,10 @@ def test_row_split_invariance(path, M, cuts, bitwise):
     if bitwise:
         assert np.array_equal(parts, y)
     else:
+        tol = DECODE_TOL if path == DEC else PREFILL_TOL
         y_ref, s = oracle.matmul(w, x, N, K)
-        check_close(parts, y_ref, s, DECODE_TOL, "row chunks")
-        check_close(y, y_ref, s, DECODE_TOL, "all rows")
+        check_close(parts, y_ref, s, tol, "row chunks")
+        check_close(y, y_ref, s, tol, "all rows")
 
 
 @pytest.mark.parametrize("path", [DEC, PRE])
@@ -162,14 +163,15 @@ def test_batched_equals_single_calls(M):
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
 
 
-def test_split_k_workspace_reuse_across_layouts():
-    """Consecutive calls whose K-splits lay out the library workspace differently.
-
-    Regression: counters of one call must never start on bytes another call used
-    for partial sums."""
+@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40))])
+def test_split_k_workspace_reuse_across_layouts(path, Ms):
+    """Consecutive calls whose K splits lay out the library workspace differently
+    (partial sums of one call land where another call kept its own, and the
+    prefill family also keeps its binary16 activations there)."""
     import torch
     seq = [[(300, 8192)], [(700, 5120)] * 5 + [(64, 17408)], [(129, 3072), (64, 1280)], [(300, 8192)]]
-    for M in (1, 3):
+    tol = DECODE_TOL if path == DEC else PREFILL_TOL
+    for M in Ms:
         for si, shapes in enumerate(seq):
             hosts, probs = [], []
             for i, (N, K) in enumerate(shapes):
@@ -177,12 +179,12 @@ def test_split_k_workspace_reuse_across_layouts():
                 x = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 801, M, si, i))
                 hosts.append((w, x, N, K))
                 probs.append((to_dev(w), to_dev(x), torch.empty((M, N), dtype=torch.float32, device=device())))
-            q4k.matmul_batched(probs, path=DEC)
+            q4k.matmul_batched(probs, path=path)
             torch.cuda.synchronize()
             for (w, x, N, K), (_, _, y) in zip(hosts, probs):
                 cols = np.arange(0, N, 7)
                 y_ref, s = oracle.matmul_cols(w, x, N, K, cols)
-                check_close(y.cpu().numpy()[:, cols], y_ref, s, DECODE_TOL, f"seq {si} M={M} N={N} K={K}")
+                check_close(y.cpu().numpy()[:, cols], y_ref, s, tol, f"seq {si} M={M} N={N} K={K}")
 
 
 def test_empty_shapes_and_misaligned_pointers_leave_y_untouched():
