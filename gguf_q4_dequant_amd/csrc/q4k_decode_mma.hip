@@ -29,10 +29,15 @@
 //     each lane picks up its own row's bytes (the fragment reads touch 64
 //     distinct banks): reading fragments straight from HBM touches twice as
 //     many cache lines per load and is much slower.
-//   * Two kernels: for M = 1 sixteen waves per workgroup, each owning about
-//     two super-blocks of one 32-row tile and staging its own activations;
-//     for 2 <= M <= 16 four waves per 32-row tile, staging the activations of
-//     all tokens in passes over K.  In both, the waves of a tile add their
+//   * For M = 1 the single token fills only two A rows, so the wide kernel
+//     uses v_mfma_f32_16x16x32_f16 instead: one MFMA covers a whole 32-weight
+//     sub-block for 16 rows of W, with hi in the even and lo in the odd rows
+//     of A (see mma_block16).
+//   * Kernels: for M = 1, workgroups of sixteen waves (four for launches of
+//     more than two rounds of short rows), each wave owning about two
+//     super-blocks of one 32-row tile and staging its own activations; for
+//     2 <= M <= 16 four waves per 32-row tile, staging the activations of all
+//     tokens in passes over K.  In both, the waves of a tile add their
 //     partial sums through LDS (no second kernel).
 #include "q4k_internal.h"
 
