@@ -511,8 +511,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
 
     // This wave's super-blocks kb = kw + wpt * i, in pairs (i0, i0 + 1).  For
     // each pair everything is requested at once: the activations (lanes
-    // 0..31 for the first block, 32..63 for the second), the second block by
-    // LDS DMA straight into the slot, the first into registers.
+    // 0..31 for the first block, 32..63 for the second) and both blocks, into
+    // registers.  (Requesting the second block only after the first arrived,
+    // to overlap its transfer with the first block's arithmetic, was slower.)
     const int nb = active && KB > kw ? (KB - kw + wpt - 1) / wpt : 0;
     for (int i0 = 0; i0 < nb; i0 += 2) {
         const int bi = min(i0 + half, nb - 1);  // a lone last block is staged twice

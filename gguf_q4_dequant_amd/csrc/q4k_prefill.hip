@@ -9,11 +9,12 @@
 //   3. v_mfma_f32_32x32x16_f16 multiplies them with fp32 accumulation.
 //
 // Two tile shapes, both through double-buffered LDS:
-//   * M > 64: 256x256 tiles, eight waves (two per SIMD, so that one wave's
-//     matrix-core work hides the other's loads and dequantization), each
-//     owning a 128x64 block of the output tile.  While the matrix cores work
-//     on k-step s the waves load k-step s+1 into registers; after the MFMAs
-//     they store it into the other LDS buffer.
+//   * M > 64: 256x256 tiles, eight waves (two per SIMD), each owning a
+//     128x64 block of the output tile.  A k-step runs in four phases, one per
+//     16-deep k slice, in which the slice's MFMAs alternate with the next
+//     step's work (x stores, W dequantization and stores, fragment reads), so
+//     that the matrix cores keep working while the rest goes on; each slot's
+//     loads for the step after are issued as soon as the slot is consumed.
 //   * M <= 64: 32x128 tiles, four waves of 32x32, a register ring eight
 //     k-steps deep, and K cut into chunks of at most eight blocks (one
 //     workgroup each, partial tiles summed in chunk order by a second kernel),
@@ -61,6 +62,7 @@ using BigTile = Shape<256, 256, 2, 4, 1, 0>;
 // long and short K even out and CUs hold several workgroups.
 using SmallTile = Shape<32, 128, 1, 4, 8, 8>;
 constexpr int kSmallTileMaxM = 64;
+
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -131,7 +133,10 @@ __device__ __forceinline__ void decode_header(const uint4 &hd, RowScales &r) {
 // fuses, and rounds the result once to binary16.  q enters as a binary16
 // subnormal: a nibble masked into the low bits of a half is q*2^-24 exactly
 // (q*2^-20 for a high nibble left in place), and `a` carries the matching
-// 2^24 (2^20), so the product is d*sc*q exactly.
+// 2^24 (2^20), so the product is d*sc*q exactly.  Written as instructions:
+// from an fma followed by a narrowing the compiler sometimes forms the fused
+// instruction and sometimes an f32 FMA and a separate conversion (a second
+// rounding).
 //   e holds (q0, q2) and o holds (q1, q3) in their two halves; the result is
 // the packed pair (w0, w1) for half 0 and (w2, w3) for half 1.
 __device__ __forceinline__ uint32_t mix_pair_lo(float a, uint32_t e, uint32_t o, float c) {
@@ -239,37 +244,59 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     constexpr int R = S::R;
     uint4 xr[R][S::XC], wq[R], whd[R];
     RowScales rs;
-    auto load_stage = [&](int r, int s_req) {
+    auto load_x = [&](int r, int s_req) {
         const int s = min(s_req, steps - 1);
 #pragma unroll
         for (int j = 0; j < S::XC; ++j) xr[r][j] = x_chunk(j, s);
+    };
+    auto load_w = [&](int r, int s_req) {
+        const int s = min(s_req, steps - 1);
         const int kb = s >> 2;
         const uint8_t *blk = wrow + static_cast<size_t>(kb) * kBlockBytes;
         if (R == 1 || r % 4 == 0) whd[r] = *reinterpret_cast<const uint4 *>(blk);  // used when g == 0
         wq[r] = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * (s & 3) + 16 * wh);
     };
-    auto store_stage = [&](int r, int s, uint4 *A, uint4 *B) {
+    auto load_stage = [&](int r, int s_req) {
+        load_x(r, s_req);
+        load_w(r, s_req);
+    };
+    // g: quant group of the step in slot r.  With a ring (R > 1) it is
+    // compile-time and the header is decoded once per block; with one slot it
+    // is a runtime value and the header (loaded with every step) is decoded
+    // every step, so that the step has no branch.
+    auto store_x = [&](int r, uint4 *A) {
 #pragma unroll
         for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = xr[r][j];
-        const int g = R == 1 ? (s & 3) : (r & 3);
-        if (g == 0) decode_header(whd[r], rs);
-        // sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles, k 32..63);
-        // quant byte l of the group -> k = l and k = 32 + l
+    };
+    // Scales of sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles,
+    // k 32..63) of this thread's W row: quant byte l of the group -> k = l and
+    // k = 32 + l.
+    struct GroupScales {
+        float a_lo, a_hi, c_lo, c_hi;
+    };
+    auto group_scales = [&](int r, int g) {
+        if (R == 1 || g == 0) decode_header(whd[r], rs);
         const uint32_t scw = g < 2 ? rs.scA : rs.scB;
         const uint32_t mnw = g < 2 ? rs.mnA : rs.mnB;
         const int sh = (g & 1) * 16;
-        const float a_lo = rs.d * 16777216.0f * static_cast<float>((scw >> sh) & 0xFFu);
-        const float a_hi = rs.d * 1048576.0f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
-        const float c_lo = rs.dmin * static_cast<float>((mnw >> sh) & 0xFFu);
-        const float c_hi = rs.dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
-        auto two_chunks = [&](uint32_t w0, uint32_t w1, int v) {
-            const WordWeights p = dequant_word(w0, a_lo, c_lo, a_hi, c_hi);
-            const WordWeights q = dequant_word(w1, a_lo, c_lo, a_hi, c_hi);
-            B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
-            B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
-        };
-        two_chunks(wq[r].x, wq[r].y, 2 * wh);
-        two_chunks(wq[r].z, wq[r].w, 2 * wh + 1);
+        return GroupScales{rs.d * 16777216.0f * static_cast<float>((scw >> sh) & 0xFFu),
+                           rs.d * 1048576.0f * static_cast<float>((scw >> (sh + 8)) & 0xFFu),
+                           rs.dmin * static_cast<float>((mnw >> sh) & 0xFFu),
+                           rs.dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu)};
+    };
+    // Half of this thread's 32 weights of the step: quant words w0, w1 ->
+    // 16-byte chunks v (low nibbles) and 4 + v (high nibbles) of its W row.
+    auto two_chunks = [&](const GroupScales &gs, uint32_t w0, uint32_t w1, int v, uint4 *B) {
+        const WordWeights p = dequant_word(w0, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+        const WordWeights q = dequant_word(w1, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+        B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
+        B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
+    };
+    auto store_stage = [&](int r, int g, uint4 *A, uint4 *B) {
+        store_x(r, A);
+        const GroupScales gs = group_scales(r, g);
+        two_chunks(gs, wq[r].x, wq[r].y, 2 * wh, B);
+        two_chunks(gs, wq[r].z, wq[r].w, 2 * wh + 1, B);
     };
 
     float16v acc[S::TA][S::TB];
@@ -280,6 +307,23 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
+    // Fragments of k slice kk (16 k: chunks 2kk, 2kk+1) and its MFMAs.
+    auto read_frags = [&](int kk, const uint4 *A, const uint4 *B, half8 *af, half8 *bf) {
+        const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a)
+            af[a] = __builtin_bit_cast(half8, A[swz(S::TM * wm + 32 * a + (lane & 31), c)]);
+#pragma unroll
+        for (int b = 0; b < S::TB; ++b)
+            bf[b] = __builtin_bit_cast(half8, B[swz(S::TN * wn + 32 * b + (lane & 31), c)]);
+    };
+    auto mfma_slice = [&](const half8 *af, const half8 *bf) {
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a)
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    };
     auto mma_step = [&](const uint4 *A, const uint4 *B) {
 #pragma unroll
         for (int kk = 0; kk < kBK / 8; kk += 2) {  // 16 k per MFMA = 2 chunks
@@ -304,7 +348,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // buffer and step s+1+R is requested into the slot it left.  Step 0 goes
     // straight to LDS; steps 1..R start in the ring.
     load_stage(0, 0);
-    store_stage(0, 0, As(0), Bs(0));
+    store_stage(0, 0, As(0), Bs(0));  // step 0: group 0
 #pragma unroll
     for (int r = 1; r <= R; ++r) load_stage(r % R, r);
     __syncthreads();
@@ -331,7 +375,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
             bf[q] = __builtin_bit_cast(half8, B[swz(S::TN * wn + (lane & 31), c)]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the three phases in this order
-        store_stage((d + 1) % R, s + 1, As((d + 1) & 1), Bs((d + 1) & 1));  // past the end: unused
+        store_stage((d + 1) % R, (d + 1) & 3, As((d + 1) & 1), Bs((d + 1) & 1));  // past the end: unused
         load_stage((d + 1) % R, s + 1 + R);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -343,12 +387,79 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     };
     int s0 = 0;
     if constexpr (R == 1) {
+        // One slot, loads one step ahead.  Each step is straight-line code:
+        // loads past the end re-read the last step and the store after the
+        // last step fills the idle buffer (never read).
+        // Each step runs in four phases, one per 16-deep k slice: the slice's
+        // MFMAs, two at a time, alternate with a quarter of the rest (the x
+        // stores and scales; one word of W dequantization; the next slice's
+        // fragment reads; the next loads), so the matrix cores always have
+        // work queued while the rest goes on.  Sched barriers keep that order.
+        auto mfma2 = [&](const half8 *af, const half8 *bf, int a) {
+            acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[0], acc[a][0], 0, 0, 0);
+            acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[1], acc[a][1], 0, 0, 0);
+        };
+        auto store_w = [&](const WordWeights &p, const WordWeights &q, int v, uint4 *B) {
+            B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
+            B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
+        };
+        static_assert(R > 1 || (S::TA == 4 && S::TB == 2), "phased step: 4 x 2 blocks per wave");
         for (; s0 < steps; ++s0) {
-            mma_step(As(s0 & 1), Bs(s0 & 1));
-            if (s0 + 1 < steps) {
-                store_stage(0, s0 + 1, As((s0 + 1) & 1), Bs((s0 + 1) & 1));
-                if (s0 + 2 < steps) load_stage(0, s0 + 2);
-            }
+            const uint4 *A = As(s0 & 1), *B = Bs(s0 & 1);
+            uint4 *An = As((s0 + 1) & 1), *Bn = Bs((s0 + 1) & 1);
+            half8 af0[S::TA], bf0[S::TB], af1[S::TA], bf1[S::TB];
+            read_frags(0, A, B, af0, bf0);
+            read_frags(1, A, B, af1, bf1);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 0
+            mfma2(af0, bf0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(0, An);
+            load_x(0, s0 + 2);  // the slot's x is in LDS: refill it at once
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af0, bf0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const GroupScales gs = group_scales(0, (s0 + 1) & 3);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af0, bf0, 2);
+            mfma2(af0, bf0, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(2, A, B, af0, bf0);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 1
+            mfma2(af1, bf1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            const WordWeights p0 = dequant_word(wq[0].x, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af1, bf1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const WordWeights q0 = dequant_word(wq[0].y, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+            store_w(p0, q0, 2 * wh, Bn);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af1, bf1, 2);
+            mfma2(af1, bf1, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(3, A, B, af1, bf1);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 2
+            mfma2(af0, bf0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            const WordWeights p1 = dequant_word(wq[0].z, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af0, bf0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const WordWeights q1 = dequant_word(wq[0].w, gs.a_lo, gs.c_lo, gs.a_hi, gs.c_hi);
+            load_w(0, s0 + 2);  // the slot's W words are consumed: refill it
+            store_w(p1, q1, 2 * wh + 1, Bn);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(af0, bf0, 2);
+            mfma2(af0, bf0, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 3
+            mfma2(af1, bf1, 0);
+            mfma2(af1, bf1, 1);
+            mfma2(af1, bf1, 2);
+            mfma2(af1, bf1, 3);
             __syncthreads();
         }
     } else {
