@@ -10,6 +10,7 @@ CPU fallback.
     matmul_batched([(w, x, y), ...])  # one launch per kernel family
     call = prepare_batched([(w, x, y), ...])  # validate once ...
     call()                                    # ... launch many times (same buffers)
+    index, value = matmul_argmax(w, x)  # greedy selection on the device: int32 [M], float32 [M]
 
 Names and semantics mirror include/q4k.h.
 """
@@ -40,7 +41,7 @@ PATH_PREFILL = 2
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
-            "q4k_select_path", "q4k_strerror", "q4k_version")
+            "q4k_matmul_argmax", "q4k_select_path", "q4k_strerror", "q4k_version")
 
 
 class Q4KError(RuntimeError):
@@ -75,6 +76,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_batched.restype = ci
     lib.q4k_matmul_batched_path.argtypes = [ctypes.POINTER(_Problem), ci, ci, ci, vp]
     lib.q4k_matmul_batched_path.restype = ci
+    lib.q4k_matmul_argmax.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp]
+    lib.q4k_matmul_argmax.restype = ci
     lib.q4k_select_path.argtypes = [ci, ci, ci]
     lib.q4k_select_path.restype = ci
     lib.q4k_strerror.argtypes = [ci]
@@ -142,6 +145,44 @@ def matmul(w, x, y=None, path: int = PATH_AUTO, stream=None):
     if rc != OK:
         raise Q4KError(rc, "q4k_matmul")
     return y
+
+
+def matmul_argmax(w, x, N: Optional[int] = None, index=None, value=None, stream=None):
+    """(index int32 [M], value float32 [M]): for each row of x, the lowest n with
+    the largest y[m, n] of y = x . dequant(w)^T, and that value.  The logits stay
+    on the device (library workspace).  N defaults to w's leading dimension."""
+    import torch
+    if N is None:
+        if w.dim() != 2:
+            raise ValueError("pass N, or w shaped [N, K/256*144]")
+        N = w.shape[0]
+    if x.dim() != 2 or x.dtype != torch.float32 or w.dtype != torch.uint8:
+        raise TypeError("expected w uint8 and x float32 [M, K]")
+    if not (w.is_cuda and x.is_cuda and w.is_contiguous() and x.is_contiguous()):
+        raise ValueError("w and x must be contiguous device tensors")
+    M, K = x.shape
+    if K % BLOCK_WEIGHTS != 0:
+        raise Q4KError(ERR_BAD_DIM, f"K={K}")
+    if w.numel() != N * (K // BLOCK_WEIGHTS) * BLOCK_BYTES:
+        raise ValueError(f"w has {w.numel()} bytes, expected N*K/256*144 = "
+                         f"{N * (K // BLOCK_WEIGHTS) * BLOCK_BYTES}")
+    if index is None:
+        index = torch.empty(M, dtype=torch.int32, device=x.device)
+    if value is None:
+        value = torch.empty(M, dtype=torch.float32, device=x.device)
+    if index.dtype != torch.int32 or value.dtype != torch.float32 or index.numel() < M or value.numel() < M:
+        raise ValueError("index must be int32 [M] and value float32 [M]")
+    rc = library().q4k_matmul_argmax(w.data_ptr(), x.data_ptr(), M, N, K, index.data_ptr(),
+                                     value.data_ptr(), _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4k_matmul_argmax")
+    return index, value
+
+
+def raw_matmul_argmax(w_ptr: int, x_ptr: int, M: int, N: int, K: int, index_ptr: int,
+                      value_ptr: Optional[int], stream: Optional[int] = None) -> int:
+    """Direct C-ABI call of q4k_matmul_argmax with raw device addresses; returns the status."""
+    return library().q4k_matmul_argmax(w_ptr, x_ptr, M, N, K, index_ptr, value_ptr, stream)
 
 
 def matmul_batched(problems: Sequence[Tuple], path: int = PATH_AUTO, stream=None):

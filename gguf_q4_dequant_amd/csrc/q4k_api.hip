@@ -56,7 +56,7 @@ struct Buffer {
     size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, Buffer> g_ws;
+std::map<std::pair<std::pair<int, uintptr_t>, int>, Buffer> g_ws;
 
 // Grow `b` to at least `bytes`.
 hipError_t grow(Buffer &b, size_t bytes, hipStream_t stream) {
@@ -82,14 +82,14 @@ hipError_t grow(Buffer &b, size_t bytes, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch) {
+hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot) {
     *scratch = nullptr;
     if (bytes == 0) return hipSuccess;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Buffer &b = g_ws[std::make_pair(dev, reinterpret_cast<uintptr_t>(stream))];
+    Buffer &b = g_ws[std::make_pair(std::make_pair(dev, reinterpret_cast<uintptr_t>(stream)), slot)];
     err = grow(b, bytes, stream);
     if (err != hipSuccess) return err;
     *scratch = static_cast<float *>(b.ptr);
@@ -156,6 +156,29 @@ int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_
 
 int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int path, hipStream_t stream) {
     return q4k::run(problems, count, M, path, stream);
+}
+
+int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K, int *index, float *value,
+                      hipStream_t stream) {
+    if (M < 0 || N < 0 || K < 0) return Q4K_ERR_BAD_DIM;
+    if (M == 0) return Q4K_OK;
+    if (N == 0 || K == 0 || K % q4k::kBlockWeights != 0) return Q4K_ERR_BAD_DIM;
+    if (!w_packed || !x || !index) return Q4K_ERR_NULL;
+    if (!q4k::aligned16(w_packed) || !q4k::aligned16(x) || (reinterpret_cast<uintptr_t>(index) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(value) & 3u) != 0)
+        return Q4K_ERR_ALIGN;
+    const int dev_rc = q4k::check_device();
+    if (dev_rc != Q4K_OK) return dev_rc;
+    // Logits, then the (value, index) partials, in workspace slot 1.
+    const size_t logits = (static_cast<size_t>(M) * N + 3) & ~static_cast<size_t>(3);
+    float *ws = nullptr;
+    hipError_t err = q4k::workspace(stream, (logits + 2 * q4k::argmax_partials(M, N)) * sizeof(float), &ws, 1);
+    if (err != hipSuccess) return Q4K_ERR_ALLOC;
+    const q4k_problem p = {w_packed, x, ws, N, K};
+    const int rc = q4k::run(&p, 1, M, Q4K_PATH_AUTO, stream);
+    if (rc != Q4K_OK) return rc;
+    err = q4k::launch_argmax(ws, M, N, ws + logits, index, value, stream);
+    return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
 }
 
 int q4k_select_path(int M, int N, int K) {

@@ -42,9 +42,18 @@ hipError_t launch_decode(Batch &b, hipStream_t stream);
 hipError_t launch_prefill(Batch &b, hipStream_t stream);
 hipError_t launch_decode_mma(Batch &b, hipStream_t stream);
 
-// Library-owned device scratch, per (device, stream), grown on demand
+// Library-owned device scratch, per (device, stream, slot), grown on demand
 // (growing synchronizes the stream first), with no guaranteed contents.
-// A null pointer is returned for a zero-byte request.
-hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch);
+// Slot 0 belongs to the product kernels; slot 1 holds the logits of an
+// argmax call while the product under it uses slot 0.  A null pointer is
+// returned for a zero-byte request.
+hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot = 0);
+
+// Row-wise argmax of y [M, N] (lowest index among equal maxima; NaN never
+// wins, an all-NaN row gives index 0 and value NaN).  part holds one
+// (value, index) pair per (row, chunk): argmax_partials(M, N) pairs.
+size_t argmax_partials(int M, int N);
+hipError_t launch_argmax(const float *y, int M, int N, float *part, int *index, float *value,
+                         hipStream_t stream);
 
 }  // namespace q4k

@@ -80,6 +80,24 @@ typedef struct q4k_problem {
  * Problems may share x; no y may overlap any x, W or another y. */
 int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_t stream);
 
+/* Greedy selection over the product, with the argmax on the device: for each
+ * row m of x
+ *     index[m] = the lowest n with y[m, n] == max over n of y[m, n],
+ *     value[m] = that maximum,
+ * where y = x . dequant(W)^T is computed exactly as q4k_matmul computes it
+ * but kept in the library workspace and never returned.  This is the lm_head
+ * of greedy decoding (the host-greedy lm_head of the rlx-llama32 crate page,
+ * "Decode") with the selection moved to the device, so that a decode step
+ * reads back one token id instead of N logits.
+ *   w_packed, x: as for q4k_matmul.  index: DEVICE int32 [M].  value: DEVICE
+ *   float32 [M], or NULL.  NaN logits never win; a row of only NaN logits
+ *   gives index 0 and value NaN.
+ *   Errors: as for q4k_matmul, and N == 0 (no maximum) is Q4K_ERR_BAD_DIM,
+ *   index NULL is Q4K_ERR_NULL, index or value not 4-byte aligned is
+ *   Q4K_ERR_ALIGN, M above 65535 is Q4K_ERR_LAUNCH.  M == 0 is a no-op. */
+int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K, int *index,
+                      float *value, hipStream_t stream);
+
 /* Kernel-family selection for tests and benchmarks. */
 enum q4k_path {
     Q4K_PATH_AUTO = 0,    /* the library's per-shape policy */
