@@ -19,6 +19,8 @@ Also reported in the same line:
   * ``prefill_m1024``: prefill TFLOP/s on the Qwen3-8B-shaped M = 1024 pass
     (36 layers, one batched launch per layer) against the 2.5 PFLOP/s dense
     binary16 matrix-core peak;
+  * ``lm_head_argmax``: the lm_head alone and with greedy selection on the
+    device (one token id per step instead of 128256 logits), graph replays;
   * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the decode
     workload on the host's cores.
 
@@ -198,6 +200,25 @@ def recorded_traffic(name):
     return int(rec["hbm_bytes_per_launch"])
 
 
+def time_head_argmax(ps, q4k, steps, warmup):
+    """The lm_head alone (logits to HBM) and with the greedy selection on the
+    device (q4k_matmul_argmax: one token id per row), each as graph replays;
+    the selected index must be the first maximum of the logits."""
+    import torch
+    w, x, y = ps.head
+    idx = torch.empty(ps.M, dtype=torch.int32, device=x.device)
+    val = torch.empty(ps.M, dtype=torch.float32, device=x.device)
+    ms_logits = _time_replays(_capture(lambda st: q4k.matmul(w, x, y, stream=st)), steps, warmup)
+    ms_argmax = _time_replays(_capture(lambda st: q4k.matmul_argmax(w, x, index=idx, value=val, stream=st)),
+                              steps, warmup)
+    yh = y.cpu().numpy()
+    first = np.argmax(yh, axis=1)
+    if not (np.array_equal(idx.cpu().numpy(), first) and np.array_equal(val.cpu().numpy(), yh[np.arange(ps.M), first])):
+        raise AssertionError("lm_head argmax differs from the first maximum of the logits")
+    return {"shape": [ps.M, int(y.shape[1]), int(x.shape[1])], "us_logits": round(ms_logits * 1e3, 2),
+            "us_argmax": round(ms_argmax * 1e3, 2), "index": int(idx[0])}
+
+
 def check_pass(ps, q4k, ncols=64):
     """Sampled parity of the last pass's outputs against the oracle (lm_head and last layer)."""
     import oracle
@@ -309,6 +330,8 @@ def main():
                      "kernel": "decode_wide_kernel (per-layer batched launch)",
                      "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)},
     }
+    out["lm_head_argmax"] = time_head_argmax(ps, q4k, args.steps, args.warmup)
+    log(f"lm_head argmax: {out['lm_head_argmax']}")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(ps)
         log(f"cpu baseline: {out['cpu_baseline']}")
