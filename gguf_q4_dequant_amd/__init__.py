@@ -11,6 +11,7 @@ CPU fallback.
     call = prepare_batched([(w, x, y), ...])  # validate once ...
     call()                                    # ... launch many times (same buffers)
     index, value = matmul_argmax(w, x)  # greedy selection on the device: int32 [M], float32 [M]
+    h = matmul_swiglu(w_gate, w_up, x)  # silu(x.Wg^T) * (x.Wu^T), the down projection's input
 
 Names and semantics mirror include/q4k.h.
 """
@@ -41,7 +42,7 @@ PATH_PREFILL = 2
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
-            "q4k_matmul_argmax", "q4k_select_path", "q4k_strerror", "q4k_version")
+            "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_select_path", "q4k_strerror", "q4k_version")
 
 
 class Q4KError(RuntimeError):
@@ -78,6 +79,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_batched_path.restype = ci
     lib.q4k_matmul_argmax.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp]
     lib.q4k_matmul_argmax.restype = ci
+    lib.q4k_matmul_swiglu.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.q4k_matmul_swiglu.restype = ci
     lib.q4k_select_path.argtypes = [ci, ci, ci]
     lib.q4k_select_path.restype = ci
     lib.q4k_strerror.argtypes = [ci]
@@ -177,6 +180,28 @@ def matmul_argmax(w, x, N: Optional[int] = None, index=None, value=None, stream=
     if rc != OK:
         raise Q4KError(rc, "q4k_matmul_argmax")
     return index, value
+
+
+def matmul_swiglu(w_gate, w_up, x, out=None, stream=None):
+    """out[M, N] = silu(x . dequant(w_gate)^T) * (x . dequant(w_up)^T)."""
+    import torch
+    if out is None:
+        if w_gate.dim() != 2:
+            raise ValueError("pass out, or w_gate shaped [N, K/256*144]")
+        out = torch.empty((x.shape[0], w_gate.shape[0]), dtype=torch.float32, device=x.device)
+    M, N, K = _check_operands(w_gate, x, out)
+    _check_operands(w_up, x, out)
+    rc = library().q4k_matmul_swiglu(w_gate.data_ptr(), w_up.data_ptr(), x.data_ptr(), out.data_ptr(), M, N, K,
+                                     _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4k_matmul_swiglu")
+    return out
+
+
+def raw_matmul_swiglu(wg_ptr: int, wu_ptr: int, x_ptr: int, out_ptr: int, M: int, N: int, K: int,
+                      stream: Optional[int] = None) -> int:
+    """Direct C-ABI call of q4k_matmul_swiglu with raw device addresses; returns the status."""
+    return library().q4k_matmul_swiglu(wg_ptr, wu_ptr, x_ptr, out_ptr, M, N, K, stream)
 
 
 def raw_matmul_argmax(w_ptr: int, x_ptr: int, M: int, N: int, K: int, index_ptr: int,

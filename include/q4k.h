@@ -98,6 +98,20 @@ int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_
 int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K, int *index,
                       float *value, hipStream_t stream);
 
+/* Gate and up projections of a SwiGLU MLP with the epilogue applied:
+ *     out[m, n] = silu(g[m, n]) * u[m, n],   silu(z) = z / (1 + exp(-z)),
+ *     g = x . dequant(W_gate)^T,   u = x . dequant(W_up)^T,
+ * the input of the down projection (the Qwen3 family on the pages uses a
+ * SwiGLU MLP).  g and u are computed as one q4k_matmul_batched launch over
+ * the shared x (same kernels, same results as q4k_matmul) and kept in the
+ * library workspace; exp is the device math library's single precision exp.
+ *   w_gate, w_up: DEVICE packed Q4_K [N, K/256*144] each.  x: DEVICE float32
+ *   [M, K].  out: DEVICE float32 [M, N], overwritten; it must not overlap x or
+ *   either W.  All four 16-byte aligned.
+ *   Errors: as for q4k_matmul.  M == 0 or N == 0 is a no-op. */
+int q4k_matmul_swiglu(const void *w_gate, const void *w_up, const float *x, float *out, int M, int N, int K,
+                      hipStream_t stream);
+
 /* Kernel-family selection for tests and benchmarks. */
 enum q4k_path {
     Q4K_PATH_AUTO = 0,    /* the library's per-shape policy */

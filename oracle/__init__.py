@@ -6,7 +6,8 @@ never imports it, and it imports nothing from the product path.
 
 The arithmetic lives in ``q4k_oracle.c`` (plain C, f32 weights, double
 accumulation); this module only builds that file with gcc and marshals numpy
-arrays into it.  See the header of ``q4k_oracle.c`` for what is computed and
+arrays into it, apart from the SwiGLU epilogue (``swiglu``), which applies
+silu(g) * u in numpy double precision to two of those products.  See the header of ``q4k_oracle.c`` for what is computed and
 which passages it follows.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
@@ -181,3 +182,20 @@ def matmul_cols(w: np.ndarray, x: np.ndarray, N: int, K: int, cols, threads: int
     if rc != 0:
         raise RuntimeError(f"oracle matmul_cols failed ({rc})")
     return y, s
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), in double (the SwiGLU MLP
+    of the Qwen3 model family on the pages)."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu(w_gate: np.ndarray, w_up: np.ndarray, x: np.ndarray, N: int, K: int, threads: int = 0):
+    """(out, g, u, s_g, s_u): out = silu(g) * u with g = x . dequant(w_gate)^T and
+    u = x . dequant(w_up)^T (the oracle's products in double, with their
+    sum |x*w| magnitudes for error bounds)."""
+    g, s_g = matmul(w_gate, x, N, K, threads)
+    u, s_u = matmul(w_up, x, N, K, threads)
+    return silu(g) * u, g, u, s_g, s_u

@@ -302,3 +302,28 @@ def test_empty_shapes_and_bad_k():
     assert y.shape == (0, 2)
     with pytest.raises(ValueError):
         oracle.matmul(np.zeros((1, 144), np.uint8), np.zeros((1, 100), np.float32), 1, 100)
+
+
+def test_silu_identities_and_library_sigmoid():
+    """silu(z) - silu(-z) = z (sigmoid(z) + sigmoid(-z) = 1), silu(0) = 0, the
+    limits, and z * scipy's expit(z)."""
+    from scipy.special import expit
+    z = np.concatenate([np.linspace(-40, 40, 801), [0.0, 1e-9, -1e-9, 88.0, -88.0, 700.0, -700.0]])
+    s = oracle.silu(z)
+    np.testing.assert_allclose(s - oracle.silu(-z), z, rtol=1e-15, atol=1e-13)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(s, z * expit(z), rtol=1e-14, atol=1e-300)
+    assert abs(oracle.silu(np.array([700.0]))[0] - 700.0) < 1e-9 and oracle.silu(np.array([-700.0]))[0] <= 0.0
+
+
+def test_swiglu_is_silu_of_gate_times_up():
+    wg = qi.random_q4k(9, 512, seed=41)
+    wu = qi.random_q4k(9, 512, seed=42)
+    x = qi.random_x(3, 512, seed=43)
+    out, g, u, s_g, s_u = oracle.swiglu(wg, wu, x, 9, 512)
+    g2, _ = oracle.matmul(wg, x, 9, 512)
+    u2, _ = oracle.matmul(wu, x, 9, 512)
+    assert np.array_equal(g, g2) and np.array_equal(u, u2)
+    assert np.array_equal(out, (g2 / (1.0 + np.exp(-g2))) * u2)
+    # swapping the roles changes the result (gate and up are not interchangeable)
+    assert not np.allclose(oracle.swiglu(wu, wg, x, 9, 512)[0], out)
