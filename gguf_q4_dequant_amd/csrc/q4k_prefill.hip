@@ -34,14 +34,16 @@ constexpr int kXcds = 8;
 // Tile shape: BM rows of x by BN rows of W per workgroup, 2*BN threads (two
 // per W row for dequantization), waves in a WM x WN grid each owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_>
+template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_, int SPLIT_ABOVE_>
 struct Shape {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
-    // Split K: a problem's K is cut into ceil(K/256 / CHUNK) near-equal
-    // chunks, one workgroup each (0: never split).  The cut depends on the
-    // problem alone, so its result does not depend on the batch around it.
+    // Split K: a problem whose K/256 exceeds SPLIT_ABOVE is cut into
+    // ceil(K/256 / CHUNK) near-equal chunks, one workgroup each (CHUNK 0:
+    // never split).  The cut depends on the problem's K alone, so its result
+    // does not depend on the batch around it.
     static constexpr int kChunkBlocks = CHUNK_;
+    static constexpr int kSplitAboveBlocks = SPLIT_ABOVE_;
     static constexpr int kThreads = 2 * BN;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -55,12 +57,17 @@ struct Shape {
     static_assert(R == 1 || (TA == 1 && TB == 1), "ring pipeline: one MFMA block per wave");
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
-using BigTile = Shape<256, 256, 2, 4, 1, 0>;
+// Rows longer than 48 blocks (K > 12288) are cut into chunks of at most 32
+// blocks, close to the length of the other projections' tiles, so that a long
+// down projection does not leave a tail of long tiles (Qwen3-14B-shaped layer:
+// 997 -> 802 us).  Shorter rows are not cut: the partial sums and the second
+// launch cost more than they even out (a K = 12288 row cut in two: +10%).
+using BigTile = Shape<256, 256, 2, 4, 1, 32, 48>;
 // Few tokens (the W stream dominates and the output tiles alone would leave
 // about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
 // steps (two blocks) ahead, K cut into chunks of at most 8 blocks, so that
 // long and short K even out and CUs hold several workgroups.
-using SmallTile = Shape<32, 128, 1, 4, 8, 8>;
+using SmallTile = Shape<32, 128, 1, 4, 8, 8, 0>;
 constexpr int kSmallTileMaxM = 64;
 
 
@@ -569,7 +576,7 @@ void make_plan(const Batch &b, Plan &pl) {
         sb.p[i] = b.p[pl.order[i]];
         const int kb = sb.p[i].K / kBlockWeights;
         constexpr int chunk = S::kChunkBlocks > 0 ? S::kChunkBlocks : 1 << 30;
-        sb.p[i].splits = (kb + chunk - 1) / chunk;
+        sb.p[i].splits = kb > S::kSplitAboveBlocks ? (kb + chunk - 1) / chunk : 1;
     }
     int tiles = 0;
     long long work = 0;  // in 256-deep blocks, per workgroup the longest chunk of its problem

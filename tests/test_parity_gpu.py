@@ -50,7 +50,9 @@ def test_decode_family_matches_oracle(M, N, K):
 
 
 PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
-                  (17, 45, 1280), (1, 128, 1024), (256, 129, 3072)]
+                  (17, 45, 1280), (1, 128, 1024), (256, 129, 3072),
+                  # rows longer than 48 blocks: the 256x256 tiles cut K into chunks
+                  (80, 300, 13056), (130, 70, 17408)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
