@@ -23,6 +23,8 @@
 // Tile order: workgroup i runs on XCD i % 8, so consecutive tiles are dealt
 // out XCD by XCD: each XCD receives a contiguous run of tiles in which the
 // N tiles of one M tile (same rows of x) are adjacent and share that XCD's L2.
+#include <type_traits>
+
 #include "q4k_internal.h"
 
 namespace q4k {
@@ -34,8 +36,11 @@ constexpr int kXcds = 8;
 // Tile shape: BM rows of x by BN rows of W per workgroup, 2*BN threads (two
 // per W row for dequantization), waves in a WM x WN grid each owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_, int SPLIT_ABOVE_>
+template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_, int SPLIT_ABOVE_, bool XF32_>
 struct Shape {
+    // x read as float32 and rounded to binary16 by the kernel itself (no
+    // pre-pass): worth it when few x rows are read per W tile.
+    static constexpr bool kXF32 = XF32_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
     // Split K: a problem whose K/256 exceeds SPLIT_ABOVE is cut into
@@ -62,12 +67,12 @@ struct Shape {
 // down projection does not leave a tail of long tiles (Qwen3-14B-shaped layer:
 // 997 -> 802 us).  Shorter rows are not cut: the partial sums and the second
 // launch cost more than they even out (a K = 12288 row cut in two: +10%).
-using BigTile = Shape<256, 256, 2, 4, 1, 32, 48>;
+using BigTile = Shape<256, 256, 2, 4, 1, 32, 48, false>;
 // Few tokens (the W stream dominates and the output tiles alone would leave
 // about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
 // steps (two blocks) ahead, K cut into chunks of at most 8 blocks, so that
 // long and short K even out and CUs hold several workgroups.
-using SmallTile = Shape<32, 128, 1, 4, 8, 8, 0>;
+using SmallTile = Shape<32, 128, 1, 4, 8, 8, 0, true>;
 constexpr int kSmallTileMaxM = 64;
 
 
@@ -231,10 +236,32 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // t/2 of the W tile (16 quant bytes: 16 weights of each of the two
     // sub-blocks of this k-step).
     const _Float16 *xcol = XH + static_cast<size_t>(kb0) * kBlockWeights + 8 * (t & 7);
+    const float *xcolf = P.x + static_cast<size_t>(kb0) * kBlockWeights + 8 * (t & 7);
     const int xr0 = tm0 + (t >> 3);
-    auto x_chunk = [&](int j, int s) {
+    // A raw x chunk: 8 binary16 values, or (kXF32) the 8 float32 values.
+    struct XPair {
+        uint4 a, b;
+    };
+    using XRaw = typename std::conditional<S::kXF32, XPair, uint4>::type;
+    auto x_chunk = [&](int j, int s) -> XRaw {
         const size_t row = static_cast<size_t>(min(xr0 + S::XROWS * j, M - 1));
-        return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
+        if constexpr (S::kXF32) {
+            const float *src = xcolf + row * K + static_cast<size_t>(s) * kBK;
+            return XPair{*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 4)};
+        } else {
+            return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
+        }
+    };
+    // The 16 bytes of binary16 x that a raw chunk becomes (nearest even).
+    auto x_bits = [&](const XRaw &v) -> uint4 {
+        if constexpr (S::kXF32) {
+            const float4 a = __builtin_bit_cast(float4, v.a), b = __builtin_bit_cast(float4, v.b);
+            const half8 h = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                             (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+            return __builtin_bit_cast(uint4, h);
+        } else {
+            return v;
+        }
     };
     const int wr = t >> 1, wh = t & 1;
     const uint8_t *wrow = W + (static_cast<size_t>(min(tn0 + wr, N - 1)) * KB + kb0) * kBlockBytes;
@@ -249,7 +276,8 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // never used): the loads stay unconditional, so the waits before a slot
     // is used count only the newer requests.
     constexpr int R = S::R;
-    uint4 xr[R][S::XC], wq[R], whd[R];
+    XRaw xr[R][S::XC];
+    uint4 wq[R], whd[R];
     RowScales rs;
     auto load_x = [&](int r, int s_req) {
         const int s = min(s_req, steps - 1);
@@ -273,7 +301,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // every step, so that the step has no branch.
     auto store_x = [&](int r, uint4 *A) {
 #pragma unroll
-        for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = xr[r][j];
+        for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = x_bits(xr[r][j]);
     };
     // Scales of sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles,
     // k 32..63) of this thread's W row: quant byte l of the group -> k = l and
@@ -690,7 +718,9 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
         make_plan<SmallTile>(b, pl);
     else
         make_plan<BigTile>(b, pl);
-    // Workspace: the binary16 activations, then the split-K partial sums.
+    // Workspace: the binary16 activations (unless the tile reads float32 x
+    // itself), then the split-K partial sums.
+    if (small && SmallTile::kXF32) halves = 0;
     const size_t part_off = (halves * sizeof(_Float16) + 255) & ~static_cast<size_t>(255);
     float *wsp = nullptr;
     hipError_t err = workspace(stream, part_off + pl.partial_floats * sizeof(float), &wsp);
@@ -698,6 +728,11 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     _Float16 *xh_base = reinterpret_cast<_Float16 *>(wsp);
     float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(wsp) + part_off);
 
+    const _Float16 *xh[kMaxBatch];
+    if (small && SmallTile::kXF32) {
+        for (int i = 0; i < b.count; ++i) xh[i] = nullptr;
+        return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
+    }
     CvtBatch cb;
     cb.count = 0;
     int cblocks = 0;
@@ -715,7 +750,6 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    const _Float16 *xh[kMaxBatch];
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
     if (small) return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);
