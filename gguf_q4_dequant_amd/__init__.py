@@ -12,6 +12,7 @@ CPU fallback.
     call()                                    # ... launch many times (same buffers)
     index, value = matmul_argmax(w, x)  # greedy selection on the device: int32 [M], float32 [M]
     h = matmul_swiglu(w_gate, w_up, x)  # silu(x.Wg^T) * (x.Wu^T), the down projection's input
+    ws = load_q4k("model.gguf")         # Q4_K tensors of a GGUF file, bytes unchanged, on the device
 
 Names and semantics mirror include/q4k.h.
 """
@@ -35,6 +36,9 @@ ERR_LAUNCH = -3
 ERR_ALIGN = -4
 ERR_DEVICE = -5
 ERR_ALLOC = -6
+ERR_FORMAT = -7
+ERR_IO = -8
+GGUF_TYPE_Q4_K = 12
 
 PATH_AUTO = 0
 PATH_DECODE = 1
@@ -42,7 +46,8 @@ PATH_PREFILL = 2
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
-            "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_select_path", "q4k_strerror", "q4k_version")
+            "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_gguf_list", "q4k_select_path", "q4k_strerror",
+            "q4k_version")
 
 
 class Q4KError(RuntimeError):
@@ -54,6 +59,11 @@ class Q4KError(RuntimeError):
 class _Problem(ctypes.Structure):
     _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+class GgufTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 128), ("type", ctypes.c_uint32), ("n_dims", ctypes.c_uint32),
+                ("dims", ctypes.c_uint64 * 4), ("offset", ctypes.c_uint64), ("nbytes", ctypes.c_uint64)]
 
 
 _lib = None
@@ -81,6 +91,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_argmax.restype = ci
     lib.q4k_matmul_swiglu.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
     lib.q4k_matmul_swiglu.restype = ci
+    lib.q4k_gguf_list.argtypes = [ctypes.c_char_p, ctypes.POINTER(GgufTensor), ci, ctypes.POINTER(ci)]
+    lib.q4k_gguf_list.restype = ci
     lib.q4k_select_path.argtypes = [ci, ci, ci]
     lib.q4k_select_path.restype = ci
     lib.q4k_strerror.argtypes = [ci]
@@ -277,3 +289,48 @@ def raw_matmul_batched(items: Iterable[Tuple[int, int, int, int, int]], M: int,
     for i, (w, x, y, n, k) in enumerate(items):
         arr[i] = _Problem(w, x, y, n, k)
     return library().q4k_matmul_batched_path(arr, len(items), M, path, stream)
+
+
+def gguf_tensors(path) -> list:
+    """Tensor directory of a GGUF file (q4k_gguf_list): a list of dicts with
+    name, type, dims (innermost first), offset (absolute) and nbytes."""
+    lib = library()
+    n = ctypes.c_int(0)
+    p = os.fsencode(path)
+    rc = lib.q4k_gguf_list(p, None, 0, ctypes.byref(n))
+    if rc != OK:
+        raise Q4KError(rc, f"q4k_gguf_list({path!r})")
+    arr = (GgufTensor * max(n.value, 1))()
+    rc = lib.q4k_gguf_list(p, arr, n.value, ctypes.byref(n))
+    if rc != OK:
+        raise Q4KError(rc, f"q4k_gguf_list({path!r})")
+    return [{"name": e.name.decode(), "type": int(e.type), "dims": tuple(int(d) for d in e.dims[:e.n_dims]),
+             "offset": int(e.offset), "nbytes": int(e.nbytes)} for e in arr[:n.value]]
+
+
+def load_q4k(path, names=None, device=None) -> dict:
+    """The Q4_K tensors of a GGUF file (all, or those in ``names``) uploaded with
+    their bytes unchanged into one device buffer: name -> uint8 view shaped
+    [N, K/256*144] (N = product of dims[1:], K = dims[0]), ready for matmul."""
+    import numpy as np
+    import torch
+    entries = [e for e in gguf_tensors(path) if e["type"] == GGUF_TYPE_Q4_K]
+    if names is not None:
+        want = set(names)
+        missing = want - {e["name"] for e in entries}
+        if missing:
+            raise KeyError(f"no Q4_K tensor named {sorted(missing)} in {path}")
+        entries = [e for e in entries if e["name"] in want]
+    offs, total = [], 0
+    for e in entries:
+        offs.append(total)
+        total += (e["nbytes"] + 255) // 256 * 256
+    arena = torch.empty(max(total, 1), dtype=torch.uint8, device=device or "cuda")
+    out = {}
+    for e, o in zip(entries, offs):
+        data = np.fromfile(path, dtype=np.uint8, count=e["nbytes"], offset=e["offset"])
+        view = arena[o:o + e["nbytes"]]
+        view.copy_(torch.from_numpy(data))
+        rows = e["nbytes"] // (e["dims"][0] // BLOCK_WEIGHTS * BLOCK_BYTES)
+        out[e["name"]] = view.view(rows, e["dims"][0] // BLOCK_WEIGHTS * BLOCK_BYTES)
+    return out

@@ -195,6 +195,8 @@ const char *q4k_strerror(int status) {
     case Q4K_ERR_ALIGN: return "pointer not 16-byte aligned";
     case Q4K_ERR_DEVICE: return "no usable gfx950 device";
     case Q4K_ERR_ALLOC: return "device workspace allocation failed";
+    case Q4K_ERR_FORMAT: return "not a GGUF file (version 2 or 3), or a malformed one";
+    case Q4K_ERR_IO: return "file could not be opened or read";
     default: return "unknown status";
     }
 }

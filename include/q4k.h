@@ -57,7 +57,9 @@ enum q4k_status {
     Q4K_ERR_LAUNCH = -3,  /* the HIP runtime rejected a kernel launch */
     Q4K_ERR_ALIGN = -4,   /* w_packed, x or y not 16-byte aligned */
     Q4K_ERR_DEVICE = -5,  /* no usable HIP device, or not a gfx950 device */
-    Q4K_ERR_ALLOC = -6    /* the library could not allocate its device workspace */
+    Q4K_ERR_ALLOC = -6,   /* the library could not allocate its device workspace */
+    Q4K_ERR_FORMAT = -7,  /* not a GGUF file of version 2 or 3, or a malformed / truncated one */
+    Q4K_ERR_IO = -8       /* the file could not be opened or read */
 };
 
 /* y = x . dequant(W)^T for one packed weight matrix.
@@ -111,6 +113,34 @@ int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K,
  *   Errors: as for q4k_matmul.  M == 0 or N == 0 is a no-op. */
 int q4k_matmul_swiglu(const void *w_gate, const void *w_up, const float *x, float *out, int M, int N, int K,
                       hipStream_t stream);
+
+/* GGUF tensor directory.  The pages load GGUF checkpoints and keep their
+ * K-quant tensors packed in device memory (rlx-qwen3 crate page, "Quick
+ * start"); this lists where each tensor's bytes sit in such a file so that the
+ * Q4_K ones can be uploaded unchanged and passed to q4k_matmul as w_packed.
+ * The container layout is not on the pages; the reader follows the published
+ * GGUF description, versions 2 and 3 (metadata of every value type is
+ * skipped; general.alignment, default 32, is honoured). */
+#define Q4K_GGUF_TYPE_Q4_K 12
+typedef struct q4k_gguf_tensor {
+    char name[128];   /* NUL-terminated tensor name (longer names: Q4K_ERR_FORMAT) */
+    uint32_t type;    /* tensor type id of the file; Q4K_GGUF_TYPE_Q4_K for Q4_K */
+    uint32_t n_dims;  /* 1..4 */
+    uint64_t dims[4]; /* dims[0] innermost (K of a weight matrix, N = dims[1]); unused dims are 1 */
+    uint64_t offset;  /* absolute byte offset of the tensor's data in the file */
+    uint64_t nbytes;  /* data size for Q4_K, F32 and F16 tensors; 0 for other types */
+} q4k_gguf_tensor;
+
+/* Reads the header, metadata and tensor infos of the GGUF file at `path` (a
+ * host path; host code only, no device is touched).  Writes the first
+ * min(capacity, total) entries, in file order, to `tensors` (a HOST array)
+ * and the total number of tensors to *count (call with capacity 0 to size the
+ * array).  Errors: path or count NULL, or tensors NULL with capacity > 0:
+ * Q4K_ERR_NULL; capacity < 0: Q4K_ERR_BAD_DIM; cannot open: Q4K_ERR_IO;
+ * bad magic, version other than 2 or 3, malformed fields, a Q4_K tensor whose
+ * dims[0] is not a multiple of 256, or data running past the end of the
+ * file: Q4K_ERR_FORMAT. */
+int q4k_gguf_list(const char *path, q4k_gguf_tensor *tensors, int capacity, int *count);
 
 /* Kernel-family selection for tests and benchmarks. */
 enum q4k_path {
