@@ -43,6 +43,7 @@ GGUF_TYPE_Q4_K = 12
 PATH_AUTO = 0
 PATH_DECODE = 1
 PATH_PREFILL = 2
+PATH_GEMV = 3
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",

@@ -103,7 +103,8 @@ int pick_path(int M) { return M <= kDecodeMaxM ? Q4K_PATH_DECODE : Q4K_PATH_PREF
 int run(const q4k_problem *problems, int count, int M, int path, hipStream_t stream) {
     if (count < 1 || count > kMaxBatch) return Q4K_ERR_BAD_DIM;
     if (!problems) return Q4K_ERR_NULL;
-    if (path != Q4K_PATH_AUTO && path != Q4K_PATH_DECODE && path != Q4K_PATH_PREFILL)
+    if (path != Q4K_PATH_AUTO && path != Q4K_PATH_DECODE && path != Q4K_PATH_PREFILL &&
+        path != Q4K_PATH_GEMV)
         return Q4K_ERR_BAD_DIM;
     if (M < 0) return Q4K_ERR_BAD_DIM;
     Batch b;
@@ -129,7 +130,9 @@ int run(const q4k_problem *problems, int count, int M, int path, hipStream_t str
     const int dev_rc = check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
     if (path == Q4K_PATH_AUTO) path = pick_path(M);
-    const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode_mma(b, stream) : launch_prefill(b, stream);
+    const hipError_t err = path == Q4K_PATH_DECODE ? launch_decode_mma(b, stream)
+                           : path == Q4K_PATH_GEMV ? launch_decode(b, stream)
+                                                   : launch_prefill(b, stream);
     if (err == hipErrorOutOfMemory || err == hipErrorMemoryAllocation) return Q4K_ERR_ALLOC;
     return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
 }

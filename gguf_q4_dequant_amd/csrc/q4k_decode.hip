@@ -1,5 +1,6 @@
-// Decode family: GEMV-style Q4_K dequant-matmul for few tokens, fp32
-// arithmetic throughout (the path the benchmark's M = 1 decode pass takes).
+// GEMV family: Q4_K dequant-matmul for few tokens with fp32 arithmetic on the
+// vector units throughout (chosen explicitly; the automatic policy sends small
+// M to the matrix-core decode kernels).
 //
 // Work item ("tile").  A workgroup of four 64-lane waves owns 32 consecutive
 // rows of W and a chunk of at most 8*BPL consecutive super-blocks of those

@@ -34,7 +34,7 @@
 //     sub-block for 16 rows of W, with hi in the even and lo in the odd rows
 //     of A (see mma_block16).
 //   * Kernels: for M = 1, workgroups of sixteen waves (four for launches of
-//     more than two rounds of short rows), each wave owning about two
+//     more than about two rounds), each wave owning about two
 //     super-blocks of one 32-row tile and staging its own activations; for
 //     2 <= M <= 16 four waves per 32-row tile, staging the activations of all
 //     tokens in passes over K.  In both, the waves of a tile add their
@@ -453,7 +453,7 @@ __host__ __device__ inline int wide_wpt(int KB, int waves) {
 }
 
 // WAVES = 16 (one workgroup per CU: launches of about two rounds at most) or
-// 4 (several workgroups per CU: long launches of short rows).
+// 4 (several workgroups per CU: longer launches).
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     // Per wave: a weight slot, and the staged activations of a pair of
@@ -604,14 +604,10 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         }
     if (b.M == 1) {
         // Sixteen waves per workgroup (one per CU) when the launch fits in
-        // about two rounds; otherwise four-wave workgroups (several per CU keep
-        // every CU busy across rounds) if no wave gets more than two
-        // super-blocks, else the fp32 GEMV family.
+        // about two rounds; otherwise four-wave workgroups, several per CU,
+        // which keep every CU busy across rounds whatever the row length.
         if (wide_groups(b, kWideWaves) <= kWideMaxGroups) return launch_wide<kWideWaves>(b, order, stream);
-        int maxkb = 0;
-        for (int i = 0; i < b.count; ++i) maxkb = max(maxkb, b.p[i].K / kBlockWeights);
-        if (maxkb <= 8) return launch_wide<4>(b, order, stream);
-        return launch_decode(b, stream);
+        return launch_wide<4>(b, order, stream);
     }
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
     // caller forces this path) are done 16 at a time.

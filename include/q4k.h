@@ -145,12 +145,18 @@ int q4k_gguf_list(const char *path, q4k_gguf_tensor *tensors, int capacity, int 
 /* Kernel-family selection for tests and benchmarks. */
 enum q4k_path {
     Q4K_PATH_AUTO = 0,    /* the library's per-shape policy */
-    Q4K_PATH_DECODE = 1,  /* GEMV family: fp32 arithmetic, meant for M <= 16 */
-    Q4K_PATH_PREFILL = 2  /* matrix-core family: binary16 operands, fp32 accumulation */
+    Q4K_PATH_DECODE = 1,  /* small-M family: matrix-core products of the quants with
+                             activations split into two binary16 parts (about 22
+                             significant bits), fp32 scales and accumulation;
+                             meant for M <= 16 */
+    Q4K_PATH_PREFILL = 2, /* matrix-core family: binary16 operands, fp32 accumulation */
+    Q4K_PATH_GEMV = 3     /* plain GEMV family: fp32 arithmetic on the vector units
+                             throughout; a one-hot x returns the f32 weight exactly */
 };
 
 /* As q4k_matmul / q4k_matmul_batched with an explicit kernel family.  The
- * decode family accepts any M; its cost grows with M. */
+ * decode and GEMV families accept any M; their cost grows with M.  An unknown
+ * path gives Q4K_ERR_BAD_DIM. */
 int q4k_matmul_path(const void *w_packed, const float *x, float *y, int M, int N, int K,
                     int path, hipStream_t stream);
 int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int path,

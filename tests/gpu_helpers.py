@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 
 # Tolerances, relative to S[m,n] = sum_k |x[m,k] * w[n,k]|:
-DECODE_TOL = 1e-5   # fp32 GEMV family
+DECODE_TOL = 1e-5   # small-M families (matrix-core decode, fp32 GEMV)
 PREFILL_TOL = 2e-3  # binary16-operand matrix-core family (x and w each carry <= 2^-11 relative rounding)
 # Against the oracle's binary16-operand product (same operand roundings), only the
 # order of the fp32 accumulation differs.

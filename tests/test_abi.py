@@ -72,6 +72,8 @@ def test_argument_errors_before_any_device_call(lib):
     assert q4k.raw_matmul(A, A + 8, A, 1, 4, 256) == q4k.ERR_ALIGN
     assert q4k.raw_matmul(A, A, A + 4, 1, 4, 256) == q4k.ERR_ALIGN
     assert q4k.raw_matmul(A, A, A, 1, 4, 256, path=7) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(A, A, A, 1, 4, 256, path=4) == q4k.ERR_BAD_DIM
+    assert q4k.raw_matmul(A, A, A, 1, 4, 256, path=-1) == q4k.ERR_BAD_DIM
     # empty products are successful no-ops, even with NULL pointers
     assert q4k.raw_matmul(0, 0, 0, 0, 4, 256) == q4k.OK
     assert q4k.raw_matmul(0, 0, 0, 3, 0, 256) == q4k.OK

@@ -23,8 +23,9 @@ def _dev_inputs(M, N, K, tag):
 def test_graph_replays_match_eager():
     import gguf_q4_dequant_amd as q4k
     q4k.library()
-    # M = 1 layer-sized batch (sixteen-wave family), a tall M = 1 product (more
-    # than two rounds of workgroups: fp32 GEMV family) and an M = 64 prefill.
+    # M = 1 layer-sized batch (sixteen-wave kernel), a tall M = 1 product (more
+    # than two rounds of workgroups: four-wave kernel), an M = 64 prefill and
+    # long rows through the fp32 GEMV family (split-K partials in the workspace).
     layer = []
     for i, (N, K) in enumerate([(2048, 2048), (512, 2048), (8192, 2048), (2048, 8192)]):
         w, x = _dev_inputs(1, N, K, i)
@@ -33,8 +34,11 @@ def test_graph_replays_match_eager():
     tall = [(wt, xt, torch.empty(1, 70000, device="cuda"))]
     wp, xp = _dev_inputs(64, 1024, 3072, 11)
     pre = [(wp, xp, torch.empty(64, 1024, device="cuda"))]
+    wg, xg = _dev_inputs(1, 300, 8192, 12)
+    gemv = [(wg, xg, torch.empty(1, 300, device="cuda"))]
     calls = [q4k.prepare_batched(b) for b in (layer, tall, pre)]
-    outs = [y for b in (layer, tall, pre) for (_, _, y) in b]
+    calls.append(q4k.prepare_batched(gemv, path=q4k.PATH_GEMV))
+    outs = [y for b in (layer, tall, pre, gemv) for (_, _, y) in b]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

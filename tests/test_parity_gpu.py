@@ -1,11 +1,13 @@
 """GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
 
-Same seeded inputs on both sides.  The fp32 GEMV family must meet
-|y - y_ref| <= 1e-5 * sum|x*w|, the binary16 matrix-core family 2e-3 * sum|x*w|
+Same seeded inputs on both sides.  The small-M families (matrix-core decode
+with split binary16 activations, and the fp32 GEMV) must meet
+|y - y_ref| <= 1e-5 * sum|x*w|, the binary16 prefill family 2e-3 * sum|x*w|
 (and 2e-5 against the oracle's binary16-operand product).  In the exact regime
-(q4k_inputs.exact_q4k / exact_x) every summation order is exact, so both
-families must equal the oracle bit for bit; one-hot activations must return
-the f32 weight (GEMV) or its binary16 rounding (matrix cores) bit for bit.
+(q4k_inputs.exact_q4k / exact_x) every summation order is exact, so every
+family must equal the oracle bit for bit; one-hot activations must return
+the f32 weight (small-M families) or its binary16 rounding (prefill) bit for
+bit.
 """
 import numpy as np
 import pytest
@@ -18,7 +20,7 @@ from tests.gpu_helpers import (DECODE_TOL, PREFILL_F16_TOL, PREFILL_TOL, check_c
 
 pytestmark = pytest.mark.gpu
 
-DEC, PRE = q4k.PATH_DECODE, q4k.PATH_PREFILL
+DEC, PRE, GEMV = q4k.PATH_DECODE, q4k.PATH_PREFILL, q4k.PATH_GEMV
 
 
 def _run(w, x, N, path):
@@ -41,12 +43,13 @@ DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 
                  (9, 70, 512), (16, 100, 5120), (16, 33, 8192), (1, 40, 17408)]
 
 
+@pytest.mark.parametrize("path", [DEC, GEMV])
 @pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
-def test_decode_family_matches_oracle(M, N, K):
+def test_decode_family_matches_oracle(path, M, N, K):
     w, x = _inputs(M, N, K, 1)
-    y = _run(w, x, N, DEC)
+    y = _run(w, x, N, path)
     y_ref, s = oracle.matmul(w, x, N, K)
-    check_close(y, y_ref, s, DECODE_TOL, f"decode M={M} N={N} K={K}")
+    check_close(y, y_ref, s, DECODE_TOL, f"path {path} M={M} N={N} K={K}")
 
 
 PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
@@ -65,7 +68,7 @@ def test_prefill_family_matches_oracle(M, N, K):
     check_close(y, y16, s16, PREFILL_F16_TOL, f"prefill vs f16-operand oracle M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GEMV])
 @pytest.mark.parametrize("M,N,K", [(1, 77, 2048), (5, 64, 1024), (40, 150, 768)])
 def test_exact_regime_is_bitwise(path, M, N, K):
     w = qi.exact_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 600, M, N, K))
@@ -75,7 +78,7 @@ def test_exact_regime_is_bitwise(path, M, N, K):
     assert np.array_equal(y.astype(np.float64), y_ref)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GEMV])
 def test_one_hot_returns_weights(path):
     N, K = 70, 1024
     w, _ = _inputs(1, N, K, 3)
@@ -88,7 +91,7 @@ def test_one_hot_returns_weights(path):
     assert np.array_equal(y, want)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GEMV])
 def test_golden_blocks_through_gpu(golden_blocks, path):
     """Closed-form weights of the hand-built blocks come back through the kernels."""
     rows = np.stack([g.raw for g in golden_blocks])  # N = 5 rows, K = 256
@@ -110,10 +113,12 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
     (PRE, 200, (66, 133), True),  # chunks above 64 tokens: 256x256 tiles
     (PRE, 200, (130, 131), False),  # mixes both tile shapes (different k order): same values to rounding
+    (GEMV, 9, (5, 6), True),      # one K split for every token count: identical bits
+    (GEMV, 4, (1, 3), True),
 ])
 def test_row_split_invariance(path, M, cuts, bitwise):
     """An M-row call equals calls on row chunks (the nx runner's mixed-chunk gates)."""
-    N, K = (140, 1536) if path == DEC else (140, 2304)  # prefill: small tiles cut K in two
+    N, K = (140, 2304) if path == PRE else (140, 1536)  # prefill: small tiles cut K in two
     w, x = _inputs(M, N, K, 4)
     y = _run(w, x, N, path)
     bounds = (0,) + cuts + (M,)
@@ -121,16 +126,16 @@ def test_row_split_invariance(path, M, cuts, bitwise):
     if bitwise:
         assert np.array_equal(parts, y)
     else:
-        tol = DECODE_TOL if path == DEC else PREFILL_TOL
+        tol = PREFILL_TOL if path == PRE else DECODE_TOL
         y_ref, s = oracle.matmul(w, x, N, K)
         check_close(parts, y_ref, s, tol, "row chunks")
         check_close(y, y_ref, s, tol, "all rows")
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GEMV])
 def test_linearity_determinism_and_weights_untouched(path):
     import torch
-    M, N, K = 6 if path == DEC else 48, 190, 2048
+    M, N, K = 48 if path == PRE else 6, 190, 2048
     w, x = _inputs(M, N, K, 5)
     wd, xd = to_dev(w), to_dev(x)
     y1 = q4k.matmul(wd, xd, path=path)
@@ -165,14 +170,14 @@ def test_batched_equals_single_calls(M):
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
 
 
-@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40))])
+@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40)), (GEMV, (1, 3))])
 def test_split_k_workspace_reuse_across_layouts(path, Ms):
     """Consecutive calls whose K splits lay out the library workspace differently
     (partial sums of one call land where another call kept its own, and the
     prefill family also keeps its binary16 activations there)."""
     import torch
     seq = [[(300, 8192)], [(700, 5120)] * 5 + [(64, 17408)], [(129, 3072), (64, 1280)], [(300, 8192)]]
-    tol = DECODE_TOL if path == DEC else PREFILL_TOL
+    tol = PREFILL_TOL if path == PRE else DECODE_TOL
     for M in Ms:
         for si, shapes in enumerate(seq):
             hosts, probs = [], []
