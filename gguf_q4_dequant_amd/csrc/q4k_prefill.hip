@@ -19,6 +19,8 @@
 //     k-steps deep, and K cut into chunks of at most eight blocks (one
 //     workgroup each, partial tiles summed in chunk order by a second kernel),
 //     so that short and long K even out and each CU holds several workgroups.
+//   * Long rows are cut into K chunks on the 256x256 tiles too: beyond 16
+//     blocks up to 512 tokens, beyond 48 blocks above that.
 //
 // Tile order: workgroup i runs on XCD i % 8, so consecutive tiles are dealt
 // out XCD by XCD: each XCD receives a contiguous run of tiles in which the
@@ -36,19 +38,13 @@ constexpr int kXcds = 8;
 // Tile shape: BM rows of x by BN rows of W per workgroup, 2*BN threads (two
 // per W row for dequantization), waves in a WM x WN grid each owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-template <int BM_, int BN_, int WM_, int WN_, int R_, int CHUNK_, int SPLIT_ABOVE_, bool XF32_>
+template <int BM_, int BN_, int WM_, int WN_, int R_, bool XF32_>
 struct Shape {
     // x read as float32 and rounded to binary16 by the kernel itself (no
     // pre-pass): worth it when few x rows are read per W tile.
     static constexpr bool kXF32 = XF32_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
-    // Split K: a problem whose K/256 exceeds SPLIT_ABOVE is cut into
-    // ceil(K/256 / CHUNK) near-equal chunks, one workgroup each (CHUNK 0:
-    // never split).  The cut depends on the problem's K alone, so its result
-    // does not depend on the batch around it.
-    static constexpr int kChunkBlocks = CHUNK_;
-    static constexpr int kSplitAboveBlocks = SPLIT_ABOVE_;
     static constexpr int kThreads = 2 * BN;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -62,18 +58,37 @@ struct Shape {
     static_assert(R == 1 || (TA == 1 && TB == 1), "ring pipeline: one MFMA block per wave");
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
-// Rows longer than 48 blocks (K > 12288) are cut into chunks of at most 32
-// blocks, close to the length of the other projections' tiles, so that a long
-// down projection does not leave a tail of long tiles (Qwen3-14B-shaped layer:
-// 997 -> 802 us).  Shorter rows are not cut: the partial sums and the second
-// launch cost more than they even out (a K = 12288 row cut in two: +10%).
-using BigTile = Shape<256, 256, 2, 4, 1, 32, 48, false>;
+using BigTile = Shape<256, 256, 2, 4, 1, false>;
 // Few tokens (the W stream dominates and the output tiles alone would leave
 // about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
-// steps (two blocks) ahead, K cut into chunks of at most 8 blocks, so that
-// long and short K even out and CUs hold several workgroups.
-using SmallTile = Shape<32, 128, 1, 4, 8, 8, 0, true>;
+// steps (two blocks) ahead.
+using SmallTile = Shape<32, 128, 1, 4, 8, true>;
 constexpr int kSmallTileMaxM = 64;
+
+// Split K: a problem whose K/256 exceeds `above` is cut into
+// ceil(K/256 / chunk) near-equal chunks, one workgroup each; a second kernel
+// adds the partial tiles in chunk order.  The rule depends on M and the
+// problem's K only, so a problem's result does not depend on the batch
+// around it.
+struct SplitRule {
+    int chunk, above;
+};
+// Small tiles: chunks of at most 8 blocks, so that long and short K even out
+// and CUs hold several workgroups.
+constexpr SplitRule kSmallSplit = {8, 0};
+// 256x256 tiles, up to 512 tokens (at most two tile rows, so fewer output
+// tiles than twice the CUs): rows longer than 16 blocks are cut into chunks of
+// at most 16, so that no tile is much longer than a K = 4096 one (Qwen3-8B
+// layer: the 16 tiles of the K = 12288 down projection otherwise set the
+// critical path, 300 -> 145 us at M = 128, 347 -> 285 us at M = 512).
+constexpr int kMidMaxM = 512;
+constexpr SplitRule kMidSplit = {16, 16};
+// More tokens: only rows longer than 48 blocks (K > 12288) are cut, into
+// chunks of at most 32 blocks (Qwen3-14B-shaped layer at M = 1024:
+// 997 -> 802 us).  Shorter rows are not cut: with enough output tiles the
+// partial sums and the second launch cost more than they even out (a
+// K = 12288 row cut in two: +10% at M = 1024).
+constexpr SplitRule kBigSplit = {32, 48};
 
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -532,7 +547,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
             }
         }
     };
-    if (S::kChunkBlocks == 0 || splits == 1) {
+    if (splits == 1) {
         for_each_out([&](size_t e, float v) { P.y[e] = v; });
         return;
     }
@@ -588,7 +603,7 @@ struct Plan {
 };
 
 template <class S>
-void make_plan(const Batch &b, Plan &pl) {
+void make_plan(const Batch &b, SplitRule rule, Plan &pl) {
     Batch &sb = pl.sb;
     sb.count = b.count;
     sb.M = b.M;
@@ -603,8 +618,7 @@ void make_plan(const Batch &b, Plan &pl) {
     for (int i = 0; i < b.count; ++i) {
         sb.p[i] = b.p[pl.order[i]];
         const int kb = sb.p[i].K / kBlockWeights;
-        constexpr int chunk = S::kChunkBlocks > 0 ? S::kChunkBlocks : 1 << 30;
-        sb.p[i].splits = kb > S::kSplitAboveBlocks ? (kb + chunk - 1) / chunk : 1;
+        sb.p[i].splits = kb > rule.above ? (kb + rule.chunk - 1) / rule.chunk : 1;
     }
     int tiles = 0;
     long long work = 0;  // in 256-deep blocks, per workgroup the longest chunk of its problem
@@ -715,9 +729,9 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     const bool small = b.M <= kSmallTileMaxM;
     Plan pl;
     if (small)
-        make_plan<SmallTile>(b, pl);
+        make_plan<SmallTile>(b, kSmallSplit, pl);
     else
-        make_plan<BigTile>(b, pl);
+        make_plan<BigTile>(b, b.M <= kMidMaxM ? kMidSplit : kBigSplit, pl);
     // Workspace: the binary16 activations (unless the tile reads float32 x
     // itself), then the split-K partial sums.
     if (small && SmallTile::kXF32) halves = 0;

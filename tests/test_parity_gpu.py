@@ -54,8 +54,10 @@ def test_decode_family_matches_oracle(path, M, N, K):
 
 PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
                   (17, 45, 1280), (1, 128, 1024), (256, 129, 3072),
-                  # rows longer than 48 blocks: the 256x256 tiles cut K into chunks
-                  (80, 300, 13056), (130, 70, 17408)]
+                  # 256x256 tiles up to 512 tokens cut rows longer than 16 blocks
+                  (80, 300, 13056), (130, 70, 17408), (100, 300, 4352), (512, 64, 5120),
+                  # more tokens: only rows longer than 48 blocks are cut
+                  (513, 40, 4352), (600, 33, 12544)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
@@ -111,7 +113,7 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
     (DEC, 9, (5, 6), False),
     (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
-    (PRE, 200, (66, 133), True),  # chunks above 64 tokens: 256x256 tiles
+    (PRE, 200, (66, 133), True),  # chunks of 65..512 tokens: 256x256 tiles, same K chunks
     (PRE, 200, (130, 131), False),  # mixes both tile shapes (different k order): same values to rounding
     (GEMV, 9, (5, 6), True),      # one K split for every token count: identical bits
     (GEMV, 4, (1, 3), True),
@@ -170,7 +172,7 @@ def test_batched_equals_single_calls(M):
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
 
 
-@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40)), (GEMV, (1, 3))])
+@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40, 100)), (GEMV, (1, 3))])
 def test_split_k_workspace_reuse_across_layouts(path, Ms):
     """Consecutive calls whose K splits lay out the library workspace differently
     (partial sums of one call land where another call kept its own, and the
