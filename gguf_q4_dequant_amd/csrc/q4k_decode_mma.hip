@@ -184,6 +184,52 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
 
+// Bytes of one pass's staged activations (the LDS image: x pairs, then the
+// sub-block sums, then the per-block factors) for M tokens, CB blocks a pass.
+__host__ __device__ inline int stage_bytes(int M, int CB) { return M * CB * 1024 + M * CB * 64; }
+
+// Activations staged once per call: pass c of an x (M tokens, K values) is
+// written as the exact LDS image decode_mma_kernel copies in, so every tile
+// of every product that reads this x starts a pass with a plain copy.
+struct StageSeg {
+    const float *x;
+    uint8_t *img;   // passes * stage_bytes(M, CB) bytes
+    int K;
+    int blk_begin;  // first workgroup of this segment
+};
+struct StageBatch {
+    StageSeg s[kMaxBatch];
+    int count;
+    int M;
+};
+
+// One 64-lane wave per two super-blocks of one token and pass: thread gq of
+// pass c handles values 8*(gq%4).. of sub-block (gq%(CB*32))/4 of token
+// gq/(CB*32), as the tile's own staging did.
+__global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
+    int p = 0;
+    for (int i = 1; i < sb.count; ++i)
+        if (static_cast<int>(blockIdx.x) >= sb.s[i].blk_begin) p = i;
+    const StageSeg &S = sb.s[p];
+    const int M = sb.M, K = S.K, KB = K >> 8;
+    const int CB = chunk_blocks(KB);
+    const int groups = M * CB * 32;  // per pass, a multiple of 256
+    const int g = (static_cast<int>(blockIdx.x) - S.blk_begin) * 256 + static_cast<int>(threadIdx.x);
+    const int c = g / groups, gq = g - c * groups;
+    const int tt = gq / (CB * 32);
+    const int gl = gq - tt * CB * 32;
+    const int jj = gl >> 2, v = gl & 3;
+    const int kb = c * CB + (jj >> 3);
+    if (kb >= KB) return;  // past the last block: the whole super-block (32 lanes) leaves together
+    const float4 *src = reinterpret_cast<const float4 *>(S.x + static_cast<size_t>(tt) * K +
+                                                         static_cast<size_t>(kb) * 256 + (jj & 7) * 32 + 8 * v);
+    uint8_t *img = S.img + static_cast<size_t>(c) * stage_bytes(M, CB);
+    float *xsum = reinterpret_cast<float *>(img + M * CB * 1024);
+    float *xmul = xsum + M * CB * 8;
+    stage_group(src[0], src[1], jj, v, tt, 2 * M, reinterpret_cast<uint4 *>(img), xsum + tt * CB * 8,
+                xmul + tt * CB * 8);
+}
+
 // NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8, 8 for M <= 16).
 typedef float float4v __attribute__((ext_vector_type(4)));
 
@@ -342,39 +388,15 @@ void decode_mma_kernel(Batch bt) {
         mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
     };
 
-    // Stage pass c of the activations: super-blocks [c*CB, c*CB + CB) of every
-    // token.  Group gq (8 values) of the pass is token gq/(CB*32), sub-block
-    // (gq%(CB*32))/4, values 8*(gq%4)..; x0/x1 hold this thread's first group
-    // of pass 0, read before the weights are requested.
-    const int groups = M * CB * 32;
-    auto group_src = [&](int c, int gq, int &tt, int &jj, int &v) -> const float4 * {
-        tt = gq / (CB * 32);
-        const int gl = gq - tt * CB * 32;
-        jj = gl >> 2;
-        v = gl & 3;
-        const int kb = c * CB + (jj >> 3);
-        if (kb >= KB) return nullptr;  // the whole super-block (32 lanes) skips together
-        return reinterpret_cast<const float4 *>(P.x + static_cast<size_t>(tt) * K + static_cast<size_t>(kb) * 256 +
-                                                (jj & 7) * 32 + 8 * v);
-    };
-    float4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-    {
-        int tt, jj, v;
-        const float4 *src = t < groups ? group_src(0, t, tt, jj, v) : nullptr;
-        if (src) {
-            x0 = src[0];
-            x1 = src[1];
-        }
-    }
+    // Pass c of the activations (super-blocks [c*CB, c*CB + CB) of every
+    // token) is staged by a plain copy of its image, written once per call by
+    // prestage_kernel.
+    const int n16 = stage_bytes(M, CB) / 16;
     auto stage = [&](int c) {
-        for (int gq = t; gq < groups; gq += kThreads) {
-            int tt, jj, v;
-            const float4 *src = group_src(c, gq, tt, jj, v);
-            if (!src) continue;
-            const bool pre = c == 0 && gq == t;
-            stage_group(pre ? x0 : src[0], pre ? x1 : src[1], jj, v, tt, R2, xs, xsum + tt * CB * 8,
-                        xmul + tt * CB * 8);
-        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c) * n16;
+        uint4 *dst = reinterpret_cast<uint4 *>(lds + kWLds);
+#pragma unroll 4
+        for (int i = t; i < n16; i += kThreads) dst[i] = src[i];
     };
 
     // This wave's super-blocks: kb = wave + 4 i.
@@ -631,10 +653,52 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         const int M = sb.M;
         int ident[kMaxBatch];
         for (int i = 0; i < b.count; ++i) ident[i] = i;
-        const hipError_t e = M <= 1   ? launch_wide<kWideWaves>(sb, ident, stream)
-                             : M <= 4 ? launch_np<2>(sb, lds, tiles, stream)
-                             : M <= 8 ? launch_np<4>(sb, lds, tiles, stream)
-                                      : launch_np<8>(sb, lds, tiles, stream);
+        if (M <= 1) {
+            const hipError_t e = launch_wide<kWideWaves>(sb, ident, stream);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        // Stage each distinct (x, K) once into the workspace (the chunks of a
+        // forced M > 16 call run one after another on the stream, so each
+        // reuses the same workspace).
+        StageBatch st;
+        st.count = 0;
+        st.M = M;
+        size_t img_bytes = 0;
+        size_t offs[kMaxBatch];
+        int which[kMaxBatch];
+        for (int i = 0; i < sb.count; ++i) {
+            int k = 0;
+            while (k < st.count && !(st.s[k].x == sb.p[i].x && st.s[k].K == sb.p[i].K)) ++k;
+            if (k == st.count) {
+                const int KB = sb.p[i].K / kBlockWeights;
+                const int CB = chunk_blocks(KB);
+                st.s[k].x = sb.p[i].x;
+                st.s[k].K = sb.p[i].K;
+                offs[k] = img_bytes;
+                img_bytes += static_cast<size_t>((KB + CB - 1) / CB) * stage_bytes(M, CB);
+                ++st.count;
+            }
+            which[i] = k;
+        }
+        float *ws = nullptr;
+        hipError_t e = workspace(stream, img_bytes, &ws);
+        if (e != hipSuccess) return e;
+        int blocks = 0;
+        for (int k = 0; k < st.count; ++k) {
+            const int KB = st.s[k].K / kBlockWeights;
+            const int CB = chunk_blocks(KB);
+            st.s[k].img = reinterpret_cast<uint8_t *>(ws) + offs[k];
+            st.s[k].blk_begin = blocks;
+            blocks += (KB + CB - 1) / CB * M * CB * 32 / 256;
+        }
+        for (int i = 0; i < sb.count; ++i) sb.p[i].part = reinterpret_cast<float *>(st.s[which[i]].img);
+        hipLaunchKernelGGL(prestage_kernel, dim3(blocks), dim3(256), 0, stream, st);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = M <= 4 ? launch_np<2>(sb, lds, tiles, stream)
+            : M <= 8 ? launch_np<4>(sb, lds, tiles, stream)
+                     : launch_np<8>(sb, lds, tiles, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -14,9 +14,9 @@ constexpr int kMaxBatch = 32;
 
 // One product of a launch.  tile_begin is the first workgroup index (along
 // grid x) that belongs to this problem; problems are laid out back to back.
-// part points into the library workspace when the problem's K is split
-// across `splits` workgroups (partial sums [splits][M][N]); otherwise it is
-// unused.
+// part points into the library workspace: the partial sums [splits][M][N]
+// when the problem's K is split across `splits` workgroups, or (small-M
+// matrix-core kernel) the staged activations of its x; otherwise unused.
 struct DevProblem {
     const uint8_t *w;
     const float *x;
