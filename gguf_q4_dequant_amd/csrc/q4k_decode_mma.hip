@@ -57,9 +57,13 @@ constexpr int kStageChunks = kStage / 16;           // 288 sixteen-byte pieces
 // Super-blocks of activations staged per pass (8, or fewer for short rows:
 // every wave then takes an even number of super-blocks per pass).
 __host__ __device__ inline int chunk_blocks(int KB) { return KB < 8 ? (KB + 7) & ~7 : 8; }
+// Bytes of one pass's staged activations (the LDS image: x pairs, then the
+// sub-block sums, then the per-block factors) for M tokens, CB blocks a pass,
+// rounded up to whole kilobytes (one 64-lane copy instruction moves 1 KB).
+__host__ __device__ inline int stage_bytes(int M, int CB) { return (M * CB * 1088 + 1023) & ~1023; }
 __host__ __device__ inline int lds_bytes(int M, int CB) {
-    // weight slots | staged x (M * CB * 1024 B) | X sums and factors (M * CB * 64 B)
-    return kWaves * kStage + M * CB * 1024 + M * CB * 64;
+    // weight slots | staged x (M * CB * 1024 B) | X sums and factors (M * CB * 64 B) | padding
+    return kWaves * kStage + stage_bytes(M, CB);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -183,10 +187,6 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
     if (v == 0) sum_t[jj] = sm;
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
-
-// Bytes of one pass's staged activations (the LDS image: x pairs, then the
-// sub-block sums, then the per-block factors) for M tokens, CB blocks a pass.
-__host__ __device__ inline int stage_bytes(int M, int CB) { return M * CB * 1024 + M * CB * 64; }
 
 // Activations staged once per call: pass c of an x (M tokens, K values) is
 // written as the exact LDS image decode_mma_kernel copies in, so every tile
@@ -390,13 +390,16 @@ void decode_mma_kernel(Batch bt) {
 
     // Pass c of the activations (super-blocks [c*CB, c*CB + CB) of every
     // token) is staged by a plain copy of its image, written once per call by
-    // prestage_kernel.
-    const int n16 = stage_bytes(M, CB) / 16;
+    // prestage_kernel: wave w moves kilobytes w, w + 4, ... straight from
+    // memory into LDS (lane l's 16 bytes land 16*l bytes past the wave's
+    // base), all requests in flight at once and no registers held.  The
+    // barrier after the copy waits for them.
+    const int n1k = stage_bytes(M, CB) / 1024;
     auto stage = [&](int c) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c) * n16;
+        const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c) * n1k * 64;
         uint4 *dst = reinterpret_cast<uint4 *>(lds + kWLds);
-#pragma unroll 4
-        for (int i = t; i < n16; i += kThreads) dst[i] = src[i];
+        for (int r = wave; r < n1k; r += kWaves)
+            __builtin_amdgcn_global_load_lds(src + r * 64 + lane, dst + r * 64, 16, 0, 0);
     };
 
     // This wave's super-blocks: kb = wave + 4 i.
