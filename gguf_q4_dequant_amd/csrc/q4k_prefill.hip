@@ -9,8 +9,10 @@
 //   3. v_mfma_f32_32x32x16_f16 multiplies them with fp32 accumulation.
 //
 // Two tile shapes, both through double-buffered LDS:
-//   * M > 64: 256x256 tiles, eight waves (two per SIMD), each owning a
-//     128x64 block of the output tile.  A k-step runs in four phases, one per
+//   * M > 128: 256x256 tiles, eight waves (two per SIMD), each owning a
+//     128x64 block of the output tile (65 <= M <= 128: 128x256 tiles, blocks
+//     of 64x64, the same loop with half the MFMAs and x per step; each output
+//     sums its k in the same order, so the two shapes agree bit for bit).  A k-step runs in four phases, one per
 //     16-deep k slice, in which the slice's MFMAs alternate with the next
 //     step's work (x stores, W dequantization and stores, fragment reads), so
 //     that the matrix cores keep working while the rest goes on; each slot's
@@ -59,6 +61,12 @@ struct Shape {
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
 using BigTile = Shape<256, 256, 2, 4, 1, false>;
+// Up to one 128-row tile of tokens: 128x256 tiles, eight waves of 64x64, the
+// same loop with half the MFMAs and x per step.
+using MidTile = Shape<128, 256, 2, 4, 1, false>;
+// Qwen3-8B-shaped layer: M = 65..128 144 -> 104..107 us; at M = 160..256
+// two tile rows of 128 cost more than one of 256 (147 -> 184 us at M = 160).
+constexpr int kMidTileMaxM = 128;
 // Few tokens (the W stream dominates and the output tiles alone would leave
 // about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
 // steps (two blocks) ahead.
@@ -445,15 +453,18 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
         // stores and scales; one word of W dequantization; the next slice's
         // fragment reads; the next loads), so the matrix cores always have
         // work queued while the rest goes on.  Sched barriers keep that order.
+        // Row block a of the wave (a >= TA: no such block, nothing to do).
         auto mfma2 = [&](const half8 *af, const half8 *bf, int a) {
-            acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[0], acc[a][0], 0, 0, 0);
-            acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[1], acc[a][1], 0, 0, 0);
+            if (a < S::TA) {
+                acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[0], acc[a][0], 0, 0, 0);
+                acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[1], acc[a][1], 0, 0, 0);
+            }
         };
         auto store_w = [&](const WordWeights &p, const WordWeights &q, int v, uint4 *B) {
             B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
             B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
         };
-        static_assert(R > 1 || (S::TA == 4 && S::TB == 2), "phased step: 4 x 2 blocks per wave");
+        static_assert(R > 1 || ((S::TA == 4 || S::TA == 2) && S::TB == 2), "phased step: 4 or 2 x 2 blocks per wave");
         for (; s0 < steps; ++s0) {
             const uint4 *A = As(s0 & 1), *B = Bs(s0 & 1);
             uint4 *An = As((s0 + 1) & 1), *Bn = Bs((s0 + 1) & 1);
@@ -728,8 +739,11 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     // keep every CU busy.
     const bool small = b.M <= kSmallTileMaxM;
     Plan pl;
+    const bool mid = !small && b.M <= kMidTileMaxM;
     if (small)
         make_plan<SmallTile>(b, kSmallSplit, pl);
+    else if (mid)
+        make_plan<MidTile>(b, kMidSplit, pl);
     else
         make_plan<BigTile>(b, b.M <= kMidMaxM ? kMidSplit : kBigSplit, pl);
     // Workspace: the binary16 activations (unless the tile reads float32 x
@@ -766,6 +780,7 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
 
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
     if (small) return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
+    if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);
 }
 

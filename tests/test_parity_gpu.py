@@ -54,8 +54,10 @@ def test_decode_family_matches_oracle(path, M, N, K):
 
 PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
                   (17, 45, 1280), (1, 128, 1024), (256, 129, 3072),
-                  # 256x256 tiles up to 512 tokens cut rows longer than 16 blocks
+                  # 128x256 tiles up to 128 tokens, 256x256 above; up to 512 tokens rows
+                  # longer than 16 blocks are cut
                   (80, 300, 13056), (130, 70, 17408), (100, 300, 4352), (512, 64, 5120),
+                  (65, 40, 768), (128, 257, 2048), (129, 64, 1024),
                   # more tokens: only rows longer than 48 blocks are cut
                   (513, 40, 4352), (600, 33, 12544)]
 
@@ -113,7 +115,7 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
     (DEC, 9, (5, 6), False),
     (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
-    (PRE, 200, (66, 133), True),  # chunks of 65..512 tokens: 256x256 tiles, same K chunks
+    (PRE, 200, (66, 133), True),  # 128- and 256-row tiles: same K chunks, same k order
     (PRE, 200, (130, 131), False),  # mixes both tile shapes (different k order): same values to rounding
     (GEMV, 9, (5, 6), True),      # one K split for every token count: identical bits
     (GEMV, 4, (1, 3), True),
