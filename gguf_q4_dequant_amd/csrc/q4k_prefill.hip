@@ -375,31 +375,6 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
         for (int b = 0; b < S::TB; ++b)
             bf[b] = __builtin_bit_cast(half8, B[swz(S::TN * wn + 32 * b + (lane & 31), c)]);
     };
-    auto mfma_slice = [&](const half8 *af, const half8 *bf) {
-#pragma unroll
-        for (int a = 0; a < S::TA; ++a)
-#pragma unroll
-            for (int b = 0; b < S::TB; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-    };
-    auto mma_step = [&](const uint4 *A, const uint4 *B) {
-#pragma unroll
-        for (int kk = 0; kk < kBK / 8; kk += 2) {  // 16 k per MFMA = 2 chunks
-            half8 af[S::TA], bf[S::TB];
-            const int c = kk + (lane >> 5);
-#pragma unroll
-            for (int a = 0; a < S::TA; ++a)
-                af[a] = __builtin_bit_cast(half8, A[swz(S::TM * wm + 32 * a + (lane & 31), c)]);
-#pragma unroll
-            for (int b = 0; b < S::TB; ++b)
-                bf[b] = __builtin_bit_cast(half8, B[swz(S::TN * wn + 32 * b + (lane & 31), c)]);
-#pragma unroll
-            for (int a = 0; a < S::TA; ++a)
-#pragma unroll
-                for (int b = 0; b < S::TB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-        }
-    };
 
     // Pipeline: LDS buffer s%2 holds step s while it runs on the matrix
     // cores; meanwhile step s+1 moves from its ring slot into the other

@@ -174,7 +174,7 @@ def test_batched_equals_single_calls(M):
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
 
 
-@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3)), (PRE, (32, 40, 100)), (GEMV, (1, 3))])
+@pytest.mark.parametrize("path,Ms", [(DEC, (1, 3, 16)), (PRE, (32, 40, 100)), (GEMV, (1, 3))])
 def test_split_k_workspace_reuse_across_layouts(path, Ms):
     """Consecutive calls whose K splits lay out the library workspace differently
     (partial sums of one call land where another call kept its own, and the
@@ -196,6 +196,17 @@ def test_split_k_workspace_reuse_across_layouts(path, Ms):
                 cols = np.arange(0, N, 7)
                 y_ref, s = oracle.matmul_cols(w, x, N, K, cols)
                 check_close(y.cpu().numpy()[:, cols], y_ref, s, tol, f"seq {si} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [17, 20, 33])
+def test_decode_forced_above_16_tokens(M):
+    """The decode family runs more than 16 tokens 16 at a time (the last chunk of
+    33 is a single token, on the M = 1 kernel); the chunks share the workspace."""
+    N, K = 150, 2560
+    w, x = _inputs(M, N, K, 6)
+    y = _run(w, x, N, DEC)
+    y_ref, s = oracle.matmul(w, x, N, K)
+    check_close(y, y_ref, s, DECODE_TOL, f"forced decode M={M}")
 
 
 def test_empty_shapes_and_misaligned_pointers_leave_y_untouched():
