@@ -30,6 +30,13 @@
  *     nx_f32_llm_run_v3 source page (0 success, -1 null pointer, -2 bad
  *     dimension, -3 failure while running the forward), extended with -4..-6.
  *   - Calls are thread-safe; calls on different streams may run concurrently.
+ *   - Workspace: the library keeps device scratch memory per (device, stream)
+ *     for split-K partial sums, the binary16 copy of x (prefill) and the
+ *     staged activations of 2 <= M <= 16 calls.  It grows on demand with
+ *     hipMalloc, so a call whose shape needs more than any earlier call on
+ *     that stream allocates; calls on one stream reuse it in stream order.
+ *     Code that captures HIP graphs makes one eager call of each shape on the
+ *     capture stream first.
  */
 #ifndef Q4K_H
 #define Q4K_H
