@@ -104,6 +104,9 @@ __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, in
     float blk[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) blk[i] = 0.f;
+    // All sixteen MFMAs of the block first (eight independent accumulators),
+    // then the scaling: no product waits on the previous one's result.
+    float16v clo[4], chi[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const uint4 q = *reinterpret_cast<const uint4 *>(rb + 16 + 32 * g + 16 * half);
@@ -113,7 +116,7 @@ __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, in
         const uint4 blo1 = {q.z & LM, s2 & LM, q.w & LM, s3 & LM};
         const uint4 bhi0 = {q.x & HM, s0 & HM, q.y & HM, s1 & HM};
         const uint4 bhi1 = {q.z & HM, s2 & HM, q.w & HM, s3 & HM};
-        const int jl = jj0 + 2 * g, jh = jl + 1;  // sub-blocks 2g, 2g+1 of this block
+        const int jl = jj0 + 2 * g, jh = jl + 1;
         const uint4 alo0 = xs[((jl * 2 + 0) * R2 + arow) * 2 + half];
         const uint4 alo1 = xs[((jl * 2 + 1) * R2 + arow) * 2 + half];
         const uint4 ahi0 = xs[((jh * 2 + 0) * R2 + arow) * 2 + half];
@@ -121,21 +124,21 @@ __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, in
         float16v zero;
 #pragma unroll
         for (int i = 0; i < 16; ++i) zero[i] = 0.f;
-        float16v clo = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, alo0), __builtin_bit_cast(half8, blo0), zero, 0, 0, 0);
-        clo = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, alo1), __builtin_bit_cast(half8, blo1), clo, 0, 0, 0);
-        float16v chi = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, ahi0), __builtin_bit_cast(half8, bhi0), zero, 0, 0, 0);
-        chi = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, ahi1), __builtin_bit_cast(half8, bhi1), chi, 0, 0, 0);
-        // C layout of a 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-        // column l%32; registers 2i, 2i+1 are the hi and lo rows of token
-        // 4*(i/2) + 2*(l/32) + i%2.
+        clo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, alo0), __builtin_bit_cast(half8, blo0),
+                                                        zero, 0, 0, 0);
+        chi[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, ahi0), __builtin_bit_cast(half8, bhi0),
+                                                        zero, 0, 0, 0);
+        clo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, alo1), __builtin_bit_cast(half8, blo1),
+                                                        clo[g], 0, 0, 0);
+        chi[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, ahi1), __builtin_bit_cast(half8, bhi1),
+                                                        chi[g], 0, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            blk[i] = __builtin_fmaf(dsc[2 * g], clo[2 * i] + clo[2 * i + 1], blk[i]);
-            blk[i] = __builtin_fmaf(dsc[2 * g + 1], chi[2 * i] + chi[2 * i + 1], blk[i]);
+            blk[i] = __builtin_fmaf(dsc[2 * g], clo[g][2 * i] + clo[g][2 * i + 1], blk[i]);
+            blk[i] = __builtin_fmaf(dsc[2 * g + 1], chi[g][2 * i] + chi[g][2 * i + 1], blk[i]);
         }
     }
 #pragma unroll
