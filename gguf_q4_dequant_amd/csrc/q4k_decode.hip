@@ -142,10 +142,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
     __shared__ __attribute__((aligned(16))) float xs[MT * kXsRow];
     __shared__ float xsum[MT * kChunk * 8];
 
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, static_cast<int>(blockIdx.x));
+    const DevProblem P = load_problem(bt, p);
     const uint8_t *__restrict__ W = P.w;
     const float *__restrict__ X = P.x;
     const int N = P.N;
@@ -236,10 +234,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
 // y = sum over chunks of the partial sums, in chunk order, for split problems.
 // One thread per output element; problems laid out back to back in grid x.
 __global__ __launch_bounds__(256) void split_reduce_kernel(Batch bt) {
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, static_cast<int>(blockIdx.x));
+    const DevProblem P = load_problem(bt, p);
     const size_t e = static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x;
     const size_t total = static_cast<size_t>(bt.M) * P.N;
     if (e >= total) return;
@@ -283,10 +279,10 @@ hipError_t launch_mt(Batch &b, hipStream_t stream) {
             red_tiles += r.tiles;
         }
     }
-    hipLaunchKernelGGL((decode_kernel<MT, BPL>), dim3(tiles, m_tiles), dim3(kThreads), 0, stream, b);
+    hipLaunchKernelGGL((decode_kernel<MT, BPL>), dim3(tiles, m_tiles), dim3(kThreads), 0, stream, sealed(b));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || red.count == 0) return err;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3(red_tiles), dim3(256), 0, stream, red);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(red_tiles), dim3(256), 0, stream, sealed(red));
     return hipGetLastError();
 }
 

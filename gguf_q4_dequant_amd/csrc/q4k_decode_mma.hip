@@ -325,10 +325,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NP == 
 void decode_mma_kernel(Batch bt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tile = static_cast<int>(blockIdx.x);
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (tile >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, tile);
+    const DevProblem P = load_problem(bt, p);
     const int N = P.N, K = P.K, M = bt.M;
     const int KB = K >> 8;
     const int n0 = (tile - P.tile_begin) * kCols;
@@ -491,10 +489,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     __shared__ float xsumw[WAVES][2 * 8];
     __shared__ float xmulw[WAVES][2];
     const int g = static_cast<int>(blockIdx.x);
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (g >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, g);
+    const DevProblem P = load_problem(bt, p);
     const int N = P.N, K = P.K;
     const int KB = K >> 8;
     const int wpt = wide_wpt(KB, WAVES);
@@ -583,7 +579,7 @@ hipError_t launch_np(const Batch &b, int lds, int grid, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(decode_mma_kernel<NP>, dim3(grid), dim3(kThreads), lds, stream, b);
+    hipLaunchKernelGGL(decode_mma_kernel<NP>, dim3(grid), dim3(kThreads), lds, stream, sealed(b));
     return hipGetLastError();
 }
 
@@ -614,7 +610,7 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
         groups += sb.p[i].tiles;
     }
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_wide_kernel<WAVES>, dim3(groups), dim3(64 * WAVES), 0, stream, sb);
+    hipLaunchKernelGGL(decode_wide_kernel<WAVES>, dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
     return hipGetLastError();
 }
 

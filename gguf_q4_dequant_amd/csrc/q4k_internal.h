@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace q4k {
 
 constexpr int kBlockWeights = 256;  // weights per Q4_K super-block
@@ -30,11 +32,65 @@ struct DevProblem {
 };
 
 // Passed by value in the kernel-argument segment (well under its 4 KiB limit).
+// tb[i] repeats p[i].tile_begin (INT_MAX past count) as one contiguous table,
+// so that a workgroup finds its problem with a single scalar memory round
+// trip: launches pass sealed(b), which fills it.
 struct Batch {
+    int tb[kMaxBatch];
     DevProblem p[kMaxBatch];
     int count;
     int M;
 };
+
+inline Batch sealed(Batch b) {
+    for (int i = 0; i < kMaxBatch; ++i) b.tb[i] = i < b.count ? b.p[i].tile_begin : INT_MAX;
+    return b;
+}
+
+// Index of the problem that owns workgroup tile g: the last i < count whose
+// tile_begin <= g (problems are laid out back to back, tile_begin ascending;
+// the table is INT_MAX past count; g is uniform).  Every entry is compared,
+// so the whole table is requested at once before the first weight load.
+__device__ __forceinline__ int find_problem(const Batch &bt, int g) {
+    typedef int int16v __attribute__((ext_vector_type(16)));
+    static_assert(kMaxBatch == 32, "table read as two 16-entry vectors");
+    const int16v t0 = *reinterpret_cast<const int16v *>(bt.tb);
+    const int16v t1 = *reinterpret_cast<const int16v *>(bt.tb + 16);
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) p += g >= t0[i] ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p += g >= t1[i] ? 1 : 0;
+    return __builtin_amdgcn_readfirstlane(p);  // uniform: keeps the problem's fields in scalar loads
+}
+
+// The problem's fields, requested together (one round trip) rather than each
+// where it is first used.
+__device__ __forceinline__ DevProblem load_problem(const Batch &bt, int p) {
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    struct Raw {
+        u32x8 a;
+        u32x4 b;
+        u32x2 c;
+    };
+    static_assert(sizeof(DevProblem) == 56 && sizeof(Raw) == 64, "DevProblem read as 8 + 4 + 2 dwords");
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(&bt.p[p]);
+    uint32_t raw[14];
+    const u32x8 a = *reinterpret_cast<const u32x8 *>(src);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
+    const u32x2 c = *reinterpret_cast<const u32x2 *>(src + 12);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[i] = a[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[8 + i] = b[i];
+    raw[12] = c[0];
+    raw[13] = c[1];
+    DevProblem P;
+    __builtin_memcpy(&P, raw, sizeof(P));
+    return P;
+}
 
 // Enqueue the GEMV family / the matrix-core family for every problem of `b`.
 // Return hipSuccess or the launch error.

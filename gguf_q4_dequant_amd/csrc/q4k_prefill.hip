@@ -227,10 +227,8 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     const int tile = ga.xcd_first[xcd] + static_cast<int>(blockIdx.x) / kXcds;
     if (tile >= ga.xcd_first[xcd + 1]) return;
 
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (tile >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, tile);
+    const DevProblem P = load_problem(bt, p);
     const _Float16 *__restrict__ XH = ga.xh[p];
     const uint8_t *__restrict__ W = P.w;
     const int N = P.N;
@@ -549,10 +547,8 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
 // y = sum over chunks of the partial sums, in chunk order, for split problems
 // (four outputs per thread).
 __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
-    int p = 0;
-    for (int i = 1; i < bt.count; ++i)
-        if (static_cast<int>(blockIdx.x) >= bt.p[i].tile_begin) p = i;
-    const DevProblem &P = bt.p[p];
+    const int p = find_problem(bt, static_cast<int>(blockIdx.x));
+    const DevProblem P = load_problem(bt, p);
     const size_t e = (static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x) * 4;
     const size_t total = static_cast<size_t>(bt.M) * P.N;
     if (e >= total) return;
@@ -671,7 +667,7 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
             part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<S, MINB>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, pl.sb, ga);
+    hipLaunchKernelGGL((prefill_kernel<S, MINB>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, sealed(pl.sb), ga);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.partial_floats == 0) return err;
     Batch red;
@@ -686,7 +682,7 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
         r.tile_begin = blocks;
         blocks += static_cast<int>((static_cast<size_t>(pl.sb.M) * d.N + 1023) / 1024);
     }
-    hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, red);
+    hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, sealed(red));
     return hipGetLastError();
 }
 
