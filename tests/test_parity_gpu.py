@@ -174,6 +174,35 @@ def test_batched_equals_single_calls(M):
     check_close(probs[-1][2].cpu().numpy()[:, ::37], y_ref, s, tol, "batched")
 
 
+@pytest.mark.parametrize("M", [1, 5, 40, 130, 300])
+def test_batch_of_32_problems(M):
+    """The largest batch (32 problems, the whole problem table of a launch):
+    every workgroup must find its own problem.  Ragged N (1, 31, 33, ...) and
+    mixed K; each output equals its single call bit for bit, and a few
+    problems are checked against the oracle."""
+    import torch
+    Ks = (256, 512, 1024, 2304)
+    xs = {K: to_dev(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 710, M, K))) for K in Ks}
+    host = []
+    probs = []
+    for i in range(32):
+        N = (1, 31, 33, 64, 97, 130, 257, 40)[i % 8] + 3 * (i // 8)
+        K = Ks[(i * 3) % 4]
+        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 711, M, i))
+        host.append((w, N, K))
+        probs.append((to_dev(w), xs[K], torch.empty((M, N), dtype=torch.float32, device=device())))
+    q4k.matmul_batched(probs)
+    singles = [q4k.matmul(w, x) for w, x, _ in probs]
+    torch.cuda.synchronize()
+    for i, ((_, _, y), ys) in enumerate(zip(probs, singles)):
+        assert torch.equal(y, ys), f"problem {i}"
+    tol = DECODE_TOL if M <= 16 else PREFILL_TOL
+    for i in (0, 13, 31):
+        w, N, K = host[i]
+        y_ref, s = oracle.matmul(w, xs[K].cpu().numpy(), N, K)
+        check_close(probs[i][2].cpu().numpy(), y_ref, s, tol, f"problem {i}")
+
+
 @pytest.mark.parametrize("path,Ms", [(DEC, (1, 3, 16)), (PRE, (32, 40, 100)), (GEMV, (1, 3))])
 def test_split_k_workspace_reuse_across_layouts(path, Ms):
     """Consecutive calls whose K splits lay out the library workspace differently
