@@ -19,6 +19,10 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the small-M decode kernels scale every
+    # result with VALU instructions, and results kept in the accumulation
+    # registers cost one extra read instruction per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

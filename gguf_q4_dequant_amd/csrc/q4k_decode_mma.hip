@@ -60,9 +60,14 @@ __host__ __device__ inline int chunk_blocks(int KB) { return KB < 8 ? (KB + 7) &
 // Bytes of one pass's staged activations (the LDS image: x pairs, then the
 // sub-block sums, then the per-block factors) for M tokens, CB blocks a pass,
 // rounded up to whole kilobytes (one 64-lane copy instruction moves 1 KB).
-__host__ __device__ inline int stage_bytes(int M, int CB) { return (M * CB * 1088 + 1023) & ~1023; }
+// Token rows an image holds: M in the pair-row layout (M <= 8), 16 in the
+// token-row layout (9..16 tokens, fixed stride so that every fragment offset
+// is an immediate).
+__host__ __device__ inline int stage_rows(int M) { return M > 8 ? 16 : M; }
+__host__ __device__ inline int stage_bytes(int M, int CB) { return (stage_rows(M) * CB * 1088 + 1023) & ~1023; }
 __host__ __device__ inline int lds_bytes(int M, int CB) {
-    // weight slots | staged x (M * CB * 1024 B) | X sums and factors (M * CB * 64 B) | padding
+    // weight slots | staged x (R * CB * 1024 B) | X sums and factors (R * CB * 64 B) | padding,
+    // R = stage_rows(M)
     return kWaves * kStage + stage_bytes(M, CB);
 }
 
@@ -150,13 +155,104 @@ __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, in
     }
 }
 
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// One parked super-block of 32 rows times the staged activations of 9..16
+// tokens (the token-row layout), on v_mfma_f32_16x16x32_f16: A is the 16
+// token rows (token min(r, M - 1) in row r) of one 32-weight sub-block, hi or
+// lo; B the quants of 16 rows of W; the hi and the lo product accumulate in
+// the same C, so no per-token hi + lo sum is needed.  Lane l owns tokens
+// 4*(l/16) + r (r < 4) of rows n0 + l%16 (acc[r]) and n0 + 16 + l%16
+// (acc[4 + r]).  xs/xsum/xmul are the staged pass with jj0 the block's first
+// sub-block and CB8 = 8 * (blocks per pass) the per-token stride of the sums
+// and factors.
+__device__ __forceinline__ void mma_block_rows(const uint8_t *slot, const uint4 *xs, const float *xsum,
+                                               const float *xmul, int M, int CB8, int lane, int jj0,
+                                               float acc[8]) {
+    const int c16 = lane & 15, quarter = lane >> 4;
+    float dsc0[8], dm0[8], dsc1[8], dm1[8];
+    block_scales(*reinterpret_cast<const uint4 *>(slot + c16 * kBlockBytes), dsc0, dm0);
+    block_scales(*reinterpret_cast<const uint4 *>(slot + (16 + c16) * kBlockBytes), dsc1, dm1);
+    const uint8_t *ra = slot + c16 * kBlockBytes + 16 + 8 * quarter;
+    const uint8_t *rc = ra + 16 * kBlockBytes;
+    // this lane's A fragment of sub-block jj, part h (0 hi, 1 lo): xa[(jj*2 + h) * 64]
+    const uint4 *xa = xs + (jj0 * 2 * 16 + min(c16, M - 1)) * 4 + quarter;
+    // Group g (sub-blocks jj0 + 2g, jj0 + 2g + 1): eight MFMAs, the hi products
+    // before the lo products so that none waits on the one before.
+    // cc = {rows 0..15 low nibbles, rows 16..31 low, rows 0..15 high, rows 16..31 high}.
+    auto issue = [&](int g, float4v *cc) {
+        const uint2 qa = *reinterpret_cast<const uint2 *>(ra + 32 * g);
+        const uint2 qc = *reinterpret_cast<const uint2 *>(rc + 32 * g);
+        const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
+        const uint32_t sa0 = qa.x >> 8, sa1 = qa.y >> 8, sc0 = qc.x >> 8, sc1 = qc.y >> 8;
+        const half8 bla = __builtin_bit_cast(half8, uint4{qa.x & LM, sa0 & LM, qa.y & LM, sa1 & LM});
+        const half8 bha = __builtin_bit_cast(half8, uint4{qa.x & HM, sa0 & HM, qa.y & HM, sa1 & HM});
+        const half8 blc = __builtin_bit_cast(half8, uint4{qc.x & LM, sc0 & LM, qc.y & LM, sc1 & LM});
+        const half8 bhc = __builtin_bit_cast(half8, uint4{qc.x & HM, sc0 & HM, qc.y & HM, sc1 & HM});
+        const half8 xlh = __builtin_bit_cast(half8, xa[(4 * g + 0) * 64]);
+        const half8 xll = __builtin_bit_cast(half8, xa[(4 * g + 1) * 64]);
+        const half8 xhh = __builtin_bit_cast(half8, xa[(4 * g + 2) * 64]);
+        const half8 xhl = __builtin_bit_cast(half8, xa[(4 * g + 3) * 64]);
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        cc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xlh, bla, z, 0, 0, 0);
+        cc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xlh, blc, z, 0, 0, 0);
+        cc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xhh, bha, z, 0, 0, 0);
+        cc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xhh, bhc, z, 0, 0, 0);
+        cc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xll, bla, cc[0], 0, 0, 0);
+        cc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xll, blc, cc[1], 0, 0, 0);
+        cc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xhl, bha, cc[2], 0, 0, 0);
+        cc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xhl, bhc, cc[3], 0, 0, 0);
+    };
+    // C layout of a 16x16 MFMA: lane l, register r -> row (token) 4*(l/16) + r,
+    // column (row of W) l%16.  Sub-blocks are scaled in ascending order.
+    float blk0[4] = {0.f, 0.f, 0.f, 0.f}, blk1[4] = {0.f, 0.f, 0.f, 0.f};
+    auto scale = [&](int g, const float4v *cc) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            blk0[r] = __builtin_fmaf(dsc0[2 * g], cc[0][r], blk0[r]);
+            blk1[r] = __builtin_fmaf(dsc1[2 * g], cc[1][r], blk1[r]);
+            blk0[r] = __builtin_fmaf(dsc0[2 * g + 1], cc[2][r], blk0[r]);
+            blk1[r] = __builtin_fmaf(dsc1[2 * g + 1], cc[3][r], blk1[r]);
+        }
+    };
+    // Two groups in flight: group g is scaled while group g + 1 is on the
+    // matrix cores.
+    float4v ca[4], cb[4];
+    issue(0, ca);
+    issue(1, cb);
+    scale(0, ca);
+    issue(2, ca);
+    scale(1, cb);
+    issue(3, cb);
+    scale(2, ca);
+    scale(3, cb);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tt = min(4 * quarter + r, M - 1);
+        const float *sm = xsum + tt * CB8 + jj0;
+        float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            m0 = __builtin_fmaf(dm0[j], sm[j], m0);
+            m1 = __builtin_fmaf(dm1[j], sm[j], m1);
+        }
+        const float mul = xmul[tt * CB8 + (jj0 >> 3)];
+        acc[r] = __builtin_fmaf(mul, blk0[r], acc[r]) - m0;
+        acc[4 + r] = __builtin_fmaf(mul, blk1[r], acc[4 + r]) - m1;
+    }
+}
+
 // Stages eight activations x[0..7] of token tt, values 8v..8v+7 of staged
-// sub-block jj, as scaled hi/lo binary16 rows 2tt, 2tt+1 in the MFMA k order.
+// sub-block jj, as scaled hi and lo binary16 values in the MFMA k order: in
+// the pair-row layout (mma_block) as A rows 2tt (hi) and 2tt+1 (lo) of
+// v_mfma_f32_32x32x16_f16, in the token-row layout (mma_block_rows) as row tt
+// of separate hi and lo operands, xs[((jj*2 + 0|1)*16 + tt)*4 + v].
 // The 32 lanes of one super-block (32 adjacent lanes, from jj%8 == 0, v == 0)
 // call it together: the scale 2^e puts the super-block's largest magnitude in
 // [2^14, 2^15).  The first lane of each sub-block writes its plain sum, the
 // first lane of the super-block the factor 2^(24-e) that undoes the scaling.
-__device__ __forceinline__ void stage_group(const float4 a, const float4 b, int jj, int v, int tt, int R2,
+template <bool kTokenRows>
+__device__ __forceinline__ void stage_group(const float4 a, const float4 b, int jj, int v, int tt, int M,
                                             uint4 *xs, float *sum_t, float *mul_t) {
     float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float mx = 0.f, sm = 0.f;
@@ -184,9 +280,14 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
         hv[i] = h;
         lv[i] = static_cast<_Float16>(xv2 - static_cast<float>(h));
     }
-    const int s = v & 1, hh = v >> 1;
-    xs[((jj * 2 + s) * R2 + 2 * tt) * 2 + hh] = __builtin_bit_cast(uint4, hv);
-    xs[((jj * 2 + s) * R2 + 2 * tt + 1) * 2 + hh] = __builtin_bit_cast(uint4, lv);
+    if constexpr (kTokenRows) {
+        xs[((jj * 2 + 0) * 16 + tt) * 4 + v] = __builtin_bit_cast(uint4, hv);
+        xs[((jj * 2 + 1) * 16 + tt) * 4 + v] = __builtin_bit_cast(uint4, lv);
+    } else {
+        const int s = v & 1, hh = v >> 1, R2 = 2 * M;
+        xs[((jj * 2 + s) * R2 + 2 * tt) * 2 + hh] = __builtin_bit_cast(uint4, hv);
+        xs[((jj * 2 + s) * R2 + 2 * tt + 1) * 2 + hh] = __builtin_bit_cast(uint4, lv);
+    }
     if (v == 0) sum_t[jj] = sm;
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
@@ -209,6 +310,7 @@ struct StageBatch {
 // One 64-lane wave per two super-blocks of one token and pass: thread gq of
 // pass c handles values 8*(gq%4).. of sub-block (gq%(CB*32))/4 of token
 // gq/(CB*32), as the tile's own staging did.
+template <bool kTokenRows>
 __global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
     int p = 0;
     for (int i = 1; i < sb.count; ++i)
@@ -227,14 +329,14 @@ __global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
     const float4 *src = reinterpret_cast<const float4 *>(S.x + static_cast<size_t>(tt) * K +
                                                          static_cast<size_t>(kb) * 256 + (jj & 7) * 32 + 8 * v);
     uint8_t *img = S.img + static_cast<size_t>(c) * stage_bytes(M, CB);
-    float *xsum = reinterpret_cast<float *>(img + M * CB * 1024);
-    float *xmul = xsum + M * CB * 8;
-    stage_group(src[0], src[1], jj, v, tt, 2 * M, reinterpret_cast<uint4 *>(img), xsum + tt * CB * 8,
+    float *xsum = reinterpret_cast<float *>(img + stage_rows(M) * CB * 1024);
+    float *xmul = xsum + stage_rows(M) * CB * 8;
+    stage_group<kTokenRows>(src[0], src[1], jj, v, tt, M, reinterpret_cast<uint4 *>(img), xsum + tt * CB * 8,
                 xmul + tt * CB * 8);
 }
 
-// NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8, 8 for M <= 16).
-typedef float float4v __attribute__((ext_vector_type(4)));
+// NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8); 8 (9..16
+// tokens) runs mma_block_rows on the token-row layout instead.
 
 // M = 1 variant of mma_block on v_mfma_f32_16x16x32_f16: K = 32 is one
 // sub-block, so no MFMA waits on another.  A holds x' hi in every even row and
@@ -341,8 +443,8 @@ void decode_mma_kernel(Batch bt) {
     constexpr int kWLds = kWaves * kStage;
     uint8_t *wst = lds + wave * kStage;  // this wave's weight slot
     uint4 *xs = reinterpret_cast<uint4 *>(lds + kWLds);
-    float *xsum = reinterpret_cast<float *>(lds + kWLds + M * CB * 1024);
-    float *xmul = xsum + M * CB * 8;
+    float *xsum = reinterpret_cast<float *>(lds + kWLds + stage_rows(M) * CB * 1024);
+    float *xmul = xsum + stage_rows(M) * CB * 8;
 
     // Offsets of this lane's five pieces of a super-block from the tile's
     // first row (32-bit: a tile spans 32 rows).
@@ -386,7 +488,10 @@ void decode_mma_kernel(Batch bt) {
     }
     // One super-block from the staging area; bo = its index within the pass.
     auto consume = [&](int bo) {
-        mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
+        if constexpr (NP == 8)
+            mma_block_rows(wst, xs, xsum, xmul, M, CB * 8, lane, bo * 8, acc);
+        else
+            mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
     };
 
     // Pass c of the activations (super-blocks [c*CB, c*CB + CB) of every
@@ -455,8 +560,10 @@ void decode_mma_kernel(Batch bt) {
         for (int i = 0; i < NP; ++i) {
             const float v = red[(0 * NP + i) * 64 + lane] + red[(1 * NP + i) * 64 + lane] +
                             red[(2 * NP + i) * 64 + lane] + red[(3 * NP + i) * 64 + lane];
-            const int tt = 4 * (i >> 1) + 2 * half + (i & 1);
-            if (tt < M && n < N) P.y[static_cast<size_t>(tt) * N + n] = v;
+            // token and row of acc[i]: pair rows (32x32 C layout) or token rows (16x16)
+            const int tt = NP == 8 ? 4 * (lane >> 4) + (i & 3) : 4 * (i >> 1) + 2 * half + (i & 1);
+            const int nn = NP == 8 ? n0 + 16 * (i >> 2) + (lane & 15) : n;
+            if (tt < M && nn < N) P.y[static_cast<size_t>(tt) * N + nn] = v;
         }
     }
 }
@@ -695,7 +802,10 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             blocks += (KB + CB - 1) / CB * M * CB * 32 / 256;
         }
         for (int i = 0; i < sb.count; ++i) sb.p[i].part = reinterpret_cast<float *>(st.s[which[i]].img);
-        hipLaunchKernelGGL(prestage_kernel, dim3(blocks), dim3(256), 0, stream, st);
+        if (M > 8)
+            hipLaunchKernelGGL(prestage_kernel<true>, dim3(blocks), dim3(256), 0, stream, st);
+        else
+            hipLaunchKernelGGL(prestage_kernel<false>, dim3(blocks), dim3(256), 0, stream, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = M <= 4 ? launch_np<2>(sb, lds, tiles, stream)

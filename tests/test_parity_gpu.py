@@ -110,8 +110,10 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
 
 
 @pytest.mark.parametrize("path,M,cuts,bitwise", [
-    (DEC, 4, (2,), True),         # chunks of 2..16 tokens run one kernel and K split: identical bits
-    (DEC, 9, (5, 7), True),
+    (DEC, 4, (2,), True),         # chunks of 2..8 tokens run one kernel and K split: identical bits
+    (DEC, 8, (3, 5), True),
+    (DEC, 29, (13,), True),       # chunks of 9..16 tokens (16 at a time above 16): identical bits
+    (DEC, 9, (5, 7), False),      # 9 tokens against chunks of 5 and 2: two layouts, same values to rounding
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
     (DEC, 9, (5, 6), False),
     (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
