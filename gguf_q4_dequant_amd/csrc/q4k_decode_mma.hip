@@ -65,10 +65,10 @@ __host__ __device__ inline int chunk_blocks(int KB) { return KB < 8 ? (KB + 7) &
 // is an immediate).
 __host__ __device__ inline int stage_rows(int M) { return M > 8 ? 16 : M; }
 __host__ __device__ inline int stage_bytes(int M, int CB) { return (stage_rows(M) * CB * 1088 + 1023) & ~1023; }
-__host__ __device__ inline int lds_bytes(int M, int CB) {
+__host__ __device__ inline int lds_bytes(int M, int CB, int waves) {
     // weight slots | staged x (R * CB * 1024 B) | X sums and factors (R * CB * 64 B) | padding,
     // R = stage_rows(M)
-    return kWaves * kStage + stage_bytes(M, CB);
+    return waves * kStage + stage_bytes(M, CB);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -422,25 +422,30 @@ __device__ __forceinline__ void stage_group16(const float4 a, const float4 b, in
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
 
-template <int NP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NP == 2 ? 2 : 1)))
+// T 32-row tiles per workgroup, four waves each (wave w: tile w / 4, K lane
+// w % 4); the tiles share one staged copy of every pass of the activations.
+template <int NP, int T>
+__global__ __launch_bounds__(kThreads * T) __attribute__((amdgpu_waves_per_eu(NP == 8 ? 1 : 2)))
 void decode_mma_kernel(Batch bt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tile = static_cast<int>(blockIdx.x);
-    const int p = find_problem(bt, tile);
+    constexpr int kGroupWaves = kWaves * T;
+    const int g = static_cast<int>(blockIdx.x);
+    const int p = find_problem(bt, g);
     const DevProblem P = load_problem(bt, p);
     const int N = P.N, K = P.K, M = bt.M;
     const int KB = K >> 8;
-    const int n0 = (tile - P.tile_begin) * kCols;
     const int CB = chunk_blocks(KB);
     const int R2 = 2 * M;  // A rows in use
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
+    const int kw = wave % kWaves;  // K lane within the tile
+    const int n0 = ((g - P.tile_begin) * T + wave / kWaves) * kCols;
+    const bool active = n0 < N;  // the last group of a product may be short
     const int col = lane & 31, half = lane >> 5;
 
-    constexpr int kWLds = kWaves * kStage;
+    constexpr int kWLds = kGroupWaves * kStage;
     uint8_t *wst = lds + wave * kStage;  // this wave's weight slot
     uint4 *xs = reinterpret_cast<uint4 *>(lds + kWLds);
     float *xsum = reinterpret_cast<float *>(lds + kWLds + stage_rows(M) * CB * 1024);
@@ -448,13 +453,14 @@ void decode_mma_kernel(Batch bt) {
 
     // Offsets of this lane's five pieces of a super-block from the tile's
     // first row (32-bit: a tile spans 32 rows).
-    const uint8_t *W = P.w + static_cast<size_t>(n0) * KB * kBlockBytes;
+    const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * KB * kBlockBytes;
     const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
+    const int nr = active ? N - 1 - n0 : 0;  // last row of the tile, relative
     uint32_t goff[5];
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
         const int f = min(lane + 64 * j, kStageChunks - 1);
-        goff[j] = static_cast<uint32_t>(min(f / 9, N - 1 - n0)) * row_bytes + 16u * (f % 9);
+        goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
     }
     const bool has5 = lane + 256 < kStageChunks;  // fifth piece: lanes 0..31
     // Piece j of super-block kb of the wave's rows: piece f = lane + 64 j
@@ -504,23 +510,23 @@ void decode_mma_kernel(Batch bt) {
     auto stage = [&](int c) {
         const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c) * n1k * 64;
         uint4 *dst = reinterpret_cast<uint4 *>(lds + kWLds);
-        for (int r = wave; r < n1k; r += kWaves)
+        for (int r = wave; r < n1k; r += kGroupWaves)
             __builtin_amdgcn_global_load_lds(src + r * 64 + lane, dst + r * 64, 16, 0, 0);
     };
 
-    // This wave's super-blocks: kb = wave + 4 i.
-    const int nb = KB > wave ? (KB - wave + kWaves - 1) / kWaves : 0;
+    // This wave's super-blocks: kb = kw + 4 i.
+    const int nb = active && KB > kw ? (KB - kw + kWaves - 1) / kWaves : 0;
     const int per_pass = CB / kWaves;  // even
     const int passes = (KB + CB - 1) / CB;
     // Two super-blocks in registers (named: arrays of loaded values end up in
     // scratch).
     u32x4 a0, a1, a2, a3, a4, b0, b1, b2, b3, b4;
     if (nb > 0) {
-        const int kb = wave;
+        const int kb = kw;
         a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
     }
     if (nb > 1) {
-        const int kb = wave + kWaves;
+        const int kb = kw + kWaves;
         b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
     }
     for (int c = 0; c < passes; ++c) {
@@ -530,17 +536,17 @@ void decode_mma_kernel(Batch bt) {
         const int i_end = min(nb, (c + 1) * per_pass);
         for (int i = c * per_pass; i < i_end; i += 2) {
             const bool two = i + 1 < i_end;
-            const int bo = (wave + kWaves * i) - c * CB;
+            const int bo = (kw + kWaves * i) - c * CB;
             park(a0, a1, a2, a3, a4);
             if (i + 2 < nb) {
-                const int kb = wave + kWaves * (i + 2);
+                const int kb = kw + kWaves * (i + 2);
                 a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
             }
             consume(bo);
             if (two) {
                 park(b0, b1, b2, b3, b4);  // after consume(bo) in program order
                 if (i + 3 < nb) {
-                    const int kb = wave + kWaves * (i + 3);
+                    const int kb = kw + kWaves * (i + 3);
                     b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
                 }
                 consume(bo + kWaves);
@@ -548,18 +554,19 @@ void decode_mma_kernel(Batch bt) {
         }
     }
 
-    // Sum the four waves' partial results.
+    // Sum the partial results of each tile's four waves.
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
     for (int i = 0; i < NP; ++i) red[(wave * NP + i) * 64 + lane] = acc[i];
     __syncthreads();
-    if (wave == 0) {
+    if (active && kw == 0) {
         const int n = n0 + col;
+        const float *rt = red + wave * NP * 64;  // the tile's first wave
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const float v = red[(0 * NP + i) * 64 + lane] + red[(1 * NP + i) * 64 + lane] +
-                            red[(2 * NP + i) * 64 + lane] + red[(3 * NP + i) * 64 + lane];
+            const float v = rt[(0 * NP + i) * 64 + lane] + rt[(1 * NP + i) * 64 + lane] +
+                            rt[(2 * NP + i) * 64 + lane] + rt[(3 * NP + i) * 64 + lane];
             // token and row of acc[i]: pair rows (32x32 C layout) or token rows (16x16)
             const int tt = NP == 8 ? 4 * (lane >> 4) + (i & 3) : 4 * (i >> 1) + 2 * half + (i & 1);
             const int nn = NP == 8 ? n0 + 16 * (i >> 2) + (lane & 15) : n;
@@ -677,16 +684,31 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     }
 }
 
+// Tiles per workgroup: two for up to 8 tokens (eight waves, 2 per SIMD, on one
+// staged copy), one for 9..16 (whose staged passes fill most of the LDS).
 template <int NP>
-hipError_t launch_np(const Batch &b, int lds, int grid, hipStream_t stream) {
+constexpr int mma_tiles() { return NP == 8 ? 1 : 2; }
+
+template <int NP>
+hipError_t launch_np(Batch &b, int M, hipStream_t stream) {
+    constexpr int T = mma_tiles<NP>();
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP, T>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(decode_mma_kernel<NP>, dim3(grid), dim3(kThreads), lds, stream, sealed(b));
+    int groups = 0, lds = 0;
+    for (int i = 0; i < b.count; ++i) {
+        const int tiles = (b.p[i].N + kCols - 1) / kCols;
+        b.p[i].tile_begin = groups;
+        b.p[i].tiles = (tiles + T - 1) / T;
+        groups += b.p[i].tiles;
+        lds = max(lds, lds_bytes(M, chunk_blocks(b.p[i].K / kBlockWeights), kWaves * T));
+    }
+    if (groups == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_mma_kernel<NP, T>), dim3(groups), dim3(kThreads * T), lds, stream, sealed(b));
     return hipGetLastError();
 }
 
@@ -746,7 +768,7 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         Batch sb;
         sb.count = b.count;
         sb.M = min(kMaxTokens, b.M - m0);
-        int tiles = 0, lds = 0;
+        int tiles = 0;
         for (int i = 0; i < b.count; ++i) {
             sb.p[i] = b.p[order[i]];
             sb.p[i].x += static_cast<size_t>(m0) * sb.p[i].K;
@@ -755,8 +777,6 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             sb.p[i].tiles = (sb.p[i].N + kCols - 1) / kCols;
             sb.p[i].splits = 1;
             tiles += sb.p[i].tiles;
-            const int KB = sb.p[i].K / kBlockWeights;
-            lds = max(lds, lds_bytes(sb.M, chunk_blocks(KB)));
         }
         if (tiles == 0) return hipSuccess;
         const int M = sb.M;
@@ -808,9 +828,9 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             hipLaunchKernelGGL(prestage_kernel<false>, dim3(blocks), dim3(256), 0, stream, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = M <= 4 ? launch_np<2>(sb, lds, tiles, stream)
-            : M <= 8 ? launch_np<4>(sb, lds, tiles, stream)
-                     : launch_np<8>(sb, lds, tiles, stream);
+        e = M <= 4 ? launch_np<2>(sb, M, stream)
+            : M <= 8 ? launch_np<4>(sb, M, stream)
+                     : launch_np<8>(sb, M, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
