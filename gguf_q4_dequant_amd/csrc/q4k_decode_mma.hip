@@ -47,16 +47,16 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kCols = 32;                           // rows n per workgroup
 constexpr int kMaxTokens = 16;                      // tokens per launch (two A rows each)
 constexpr int kStage = kCols * kBlockBytes;         // one super-block of 32 rows
 constexpr int kStageChunks = kStage / 16;           // 288 sixteen-byte pieces
 
-// Super-blocks of activations staged per pass (8, or fewer for short rows:
-// every wave then takes an even number of super-blocks per pass).
-__host__ __device__ inline int chunk_blocks(int KB) { return KB < 8 ? (KB + 7) & ~7 : 8; }
+// Super-blocks of activations staged per pass: 8 for up to 8 tokens, 4 for
+// 9..16 (whose 16-row image is twice as large).  Each wave of a tile takes an
+// even number of a pass's blocks (four waves per tile below 9 tokens, two
+// above).
+__host__ __device__ inline int pass_blocks(int M) { return M > 8 ? 4 : 8; }
 // Bytes of one pass's staged activations (the LDS image: x pairs, then the
 // sub-block sums, then the per-block factors) for M tokens, CB blocks a pass,
 // rounded up to whole kilobytes (one 64-lane copy instruction moves 1 KB).
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
         if (static_cast<int>(blockIdx.x) >= sb.s[i].blk_begin) p = i;
     const StageSeg &S = sb.s[p];
     const int M = sb.M, K = S.K, KB = K >> 8;
-    const int CB = chunk_blocks(KB);
+    const int CB = pass_blocks(M);
     const int groups = M * CB * 32;  // per pass, a multiple of 256
     const int g = (static_cast<int>(blockIdx.x) - S.blk_begin) * 256 + static_cast<int>(threadIdx.x);
     const int c = g / groups, gq = g - c * groups;
@@ -422,26 +422,27 @@ __device__ __forceinline__ void stage_group16(const float4 a, const float4 b, in
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
 
-// T 32-row tiles per workgroup, four waves each (wave w: tile w / 4, K lane
-// w % 4); the tiles share one staged copy of every pass of the activations.
-template <int NP, int T>
-__global__ __launch_bounds__(kThreads * T) __attribute__((amdgpu_waves_per_eu(NP == 8 ? 1 : 2)))
+// T 32-row tiles per workgroup, WPT waves each splitting the tile's
+// super-blocks round robin (wave w: tile w / WPT, K lane w % WPT); the tiles
+// share one staged copy of every pass of the activations.
+template <int NP, int T, int WPT>
+__global__ __launch_bounds__(64 * T * WPT) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mma_kernel(Batch bt) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int kGroupWaves = kWaves * T;
+    constexpr int kGroupWaves = T * WPT;
     const int g = static_cast<int>(blockIdx.x);
     const int p = find_problem(bt, g);
     const DevProblem P = load_problem(bt, p);
     const int N = P.N, K = P.K, M = bt.M;
     const int KB = K >> 8;
-    const int CB = chunk_blocks(KB);
+    const int CB = pass_blocks(M);
     const int R2 = 2 * M;  // A rows in use
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int kw = wave % kWaves;  // K lane within the tile
-    const int n0 = ((g - P.tile_begin) * T + wave / kWaves) * kCols;
+    const int kw = wave % WPT;  // K lane within the tile
+    const int n0 = ((g - P.tile_begin) * T + wave / WPT) * kCols;
     const bool active = n0 < N;  // the last group of a product may be short
     const int col = lane & 31, half = lane >> 5;
 
@@ -514,9 +515,9 @@ void decode_mma_kernel(Batch bt) {
             __builtin_amdgcn_global_load_lds(src + r * 64 + lane, dst + r * 64, 16, 0, 0);
     };
 
-    // This wave's super-blocks: kb = kw + 4 i.
-    const int nb = active && KB > kw ? (KB - kw + kWaves - 1) / kWaves : 0;
-    const int per_pass = CB / kWaves;  // even
+    // This wave's super-blocks: kb = kw + WPT i.
+    const int nb = active && KB > kw ? (KB - kw + WPT - 1) / WPT : 0;
+    const int per_pass = CB / WPT;  // even
     const int passes = (KB + CB - 1) / CB;
     // Two super-blocks in registers (named: arrays of loaded values end up in
     // scratch).
@@ -526,7 +527,7 @@ void decode_mma_kernel(Batch bt) {
         a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
     }
     if (nb > 1) {
-        const int kb = kw + kWaves;
+        const int kb = kw + WPT;
         b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
     }
     for (int c = 0; c < passes; ++c) {
@@ -536,25 +537,25 @@ void decode_mma_kernel(Batch bt) {
         const int i_end = min(nb, (c + 1) * per_pass);
         for (int i = c * per_pass; i < i_end; i += 2) {
             const bool two = i + 1 < i_end;
-            const int bo = (kw + kWaves * i) - c * CB;
+            const int bo = (kw + WPT * i) - c * CB;
             park(a0, a1, a2, a3, a4);
             if (i + 2 < nb) {
-                const int kb = kw + kWaves * (i + 2);
+                const int kb = kw + WPT * (i + 2);
                 a0 = ld(kb, 0); a1 = ld(kb, 1); a2 = ld(kb, 2); a3 = ld(kb, 3); a4 = ld(kb, 4);
             }
             consume(bo);
             if (two) {
                 park(b0, b1, b2, b3, b4);  // after consume(bo) in program order
                 if (i + 3 < nb) {
-                    const int kb = kw + kWaves * (i + 3);
+                    const int kb = kw + WPT * (i + 3);
                     b0 = ld(kb, 0); b1 = ld(kb, 1); b2 = ld(kb, 2); b3 = ld(kb, 3); b4 = ld(kb, 4);
                 }
-                consume(bo + kWaves);
+                consume(bo + WPT);
             }
         }
     }
 
-    // Sum the partial results of each tile's four waves.
+    // Sum the partial results of each tile's waves.
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
@@ -565,8 +566,9 @@ void decode_mma_kernel(Batch bt) {
         const float *rt = red + wave * NP * 64;  // the tile's first wave
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const float v = rt[(0 * NP + i) * 64 + lane] + rt[(1 * NP + i) * 64 + lane] +
-                            rt[(2 * NP + i) * 64 + lane] + rt[(3 * NP + i) * 64 + lane];
+            float v = rt[i * 64 + lane];
+#pragma unroll
+            for (int j = 1; j < WPT; ++j) v += rt[(j * NP + i) * 64 + lane];
             // token and row of acc[i]: pair rows (32x32 C layout) or token rows (16x16)
             const int tt = NP == 8 ? 4 * (lane >> 4) + (i & 3) : 4 * (i >> 1) + 2 * half + (i & 1);
             const int nn = NP == 8 ? n0 + 16 * (i >> 2) + (lane & 15) : n;
@@ -684,17 +686,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     }
 }
 
-// Tiles per workgroup: two for up to 8 tokens (eight waves, 2 per SIMD, on one
-// staged copy), one for 9..16 (whose staged passes fill most of the LDS).
-template <int NP>
-constexpr int mma_tiles() { return NP == 8 ? 1 : 2; }
-
+// Workgroups of eight waves (two per SIMD) on one staged copy of the
+// activations: two tiles of four waves for up to 8 tokens, four tiles of two
+// waves for 9..16 (passes of four super-blocks, so that the image still fits).
 template <int NP>
 hipError_t launch_np(Batch &b, int M, hipStream_t stream) {
-    constexpr int T = mma_tiles<NP>();
+    constexpr int T = NP == 8 ? 4 : 2, WPT = NP == 8 ? 2 : 4;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP, T>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP, T, WPT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -705,10 +705,10 @@ hipError_t launch_np(Batch &b, int M, hipStream_t stream) {
         b.p[i].tile_begin = groups;
         b.p[i].tiles = (tiles + T - 1) / T;
         groups += b.p[i].tiles;
-        lds = max(lds, lds_bytes(M, chunk_blocks(b.p[i].K / kBlockWeights), kWaves * T));
+        lds = max(lds, lds_bytes(M, pass_blocks(M), T * WPT));
     }
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_mma_kernel<NP, T>), dim3(groups), dim3(kThreads * T), lds, stream, sealed(b));
+    hipLaunchKernelGGL((decode_mma_kernel<NP, T, WPT>), dim3(groups), dim3(64 * T * WPT), lds, stream, sealed(b));
     return hipGetLastError();
 }
 
@@ -801,7 +801,7 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             while (k < st.count && !(st.s[k].x == sb.p[i].x && st.s[k].K == sb.p[i].K)) ++k;
             if (k == st.count) {
                 const int KB = sb.p[i].K / kBlockWeights;
-                const int CB = chunk_blocks(KB);
+                const int CB = pass_blocks(M);
                 st.s[k].x = sb.p[i].x;
                 st.s[k].K = sb.p[i].K;
                 offs[k] = img_bytes;
@@ -816,10 +816,12 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         int blocks = 0;
         for (int k = 0; k < st.count; ++k) {
             const int KB = st.s[k].K / kBlockWeights;
-            const int CB = chunk_blocks(KB);
+            const int CB = pass_blocks(M);
             st.s[k].img = reinterpret_cast<uint8_t *>(ws) + offs[k];
             st.s[k].blk_begin = blocks;
-            blocks += (KB + CB - 1) / CB * M * CB * 32 / 256;
+            // one thread per 8 values of a (token, sub-block) of every pass; the
+            // threads of a last partial block return at once
+            blocks += ((KB + CB - 1) / CB * M * CB * 32 + 255) / 256;
         }
         for (int i = 0; i < sb.count; ++i) sb.p[i].part = reinterpret_cast<float *>(st.s[which[i]].img);
         if (M > 8)
