@@ -40,7 +40,11 @@ def _inputs(M, N, K, tag):
 # Shapes span several workgroup tiles and ragged tails in N, M and K/256.
 DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 130, 5120),
                  (2, 64, 768), (3, 129, 1280), (4, 200, 3072), (5, 63, 2048), (8, 96, 4096),
-                 (9, 70, 512), (16, 100, 5120), (16, 33, 8192), (1, 40, 17408)]
+                 (9, 70, 512), (16, 100, 5120), (16, 33, 8192), (1, 40, 17408),
+                 # workgroups of two tiles (<= 8 tokens) or four (9..16 tokens) with the last
+                 # tiles past N, one-block and three-block rows, long rows in passes of four
+                 (6, 33, 1280), (7, 65, 256), (12, 97, 1024), (13, 161, 2304), (15, 40, 256),
+                 (10, 33, 768), (11, 50, 17408)]
 
 
 @pytest.mark.parametrize("path", [DEC, GEMV])
