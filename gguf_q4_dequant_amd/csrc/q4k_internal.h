@@ -65,30 +65,13 @@ __device__ __forceinline__ int find_problem(const Batch &bt, int g) {
 }
 
 // The problem's fields, requested together (one round trip) rather than each
-// where it is first used.
+// where it is first used.  They are read as the fields they are, so that the
+// compiler still knows the pointers (read from the argument segment) address
+// global memory and keeps global (not flat) loads through them.
 __device__ __forceinline__ DevProblem load_problem(const Batch &bt, int p) {
-    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    struct Raw {
-        u32x8 a;
-        u32x4 b;
-        u32x2 c;
-    };
-    static_assert(sizeof(DevProblem) == 56 && sizeof(Raw) == 64, "DevProblem read as 8 + 4 + 2 dwords");
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(&bt.p[p]);
-    uint32_t raw[14];
-    const u32x8 a = *reinterpret_cast<const u32x8 *>(src);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
-    const u32x2 c = *reinterpret_cast<const u32x2 *>(src + 12);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) raw[i] = a[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[8 + i] = b[i];
-    raw[12] = c[0];
-    raw[13] = c[1];
-    DevProblem P;
-    __builtin_memcpy(&P, raw, sizeof(P));
+    const DevProblem P = bt.p[p];
+    asm volatile("" ::"s"(P.w), "s"(P.x), "s"(P.y), "s"(P.part), "s"(P.N), "s"(P.K), "s"(P.tile_begin),
+                 "s"(P.tiles), "s"(P.splits));
     return P;
 }
 
