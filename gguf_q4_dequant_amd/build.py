@@ -15,25 +15,24 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in ordinary VGPRs: the small-M decode kernels scale every
-    # result with VALU instructions, and results kept in the accumulation
-    # registers cost one extra read instruction per value
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# Per source file: MFMA results in ordinary VGPRs for the small-M decode
+# kernels, which scale every result with VALU instructions (results kept in
+# the accumulation registers cost one extra read instruction each).  The
+# prefill kernels keep the compiler's choice.
+EXTRA_FLAGS = {
+    "q4k_decode_mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -43,6 +42,26 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
     if out.strip() and verbose:
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libq4k.so."""
+    import concurrent.futures
+    import tempfile
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIBRARY + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="q4k_build_") as objdir:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+            jobs.append((obj, [hipcc, *HIPCC_FLAGS, *extra, "-c", "-o", obj, src]))
+        workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for _, cmd in jobs]:
+                f.result()
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in jobs]], verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 
