@@ -77,6 +77,14 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// v of lane (lane ^ M) within each group of 32 lanes: ds_swizzle in bit mode
+// (and-mask 31, xor-mask M), which needs no per-lane address arithmetic.
+template <int M>
+__device__ __forceinline__ float xor32(float v) {
+    static_assert(M > 0 && M < 32, "xor within 32 lanes");
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (M << 10) | 0x1F));
+}
+
 // Decoded per-row scales of one super-block: dsc[j] = d * sc_j (times 1/16
 // for odd j, whose quants enter the products as 16q), dm[j] = dmin * m_j.
 __device__ __forceinline__ void block_scales(const uint4 hd, float dsc[8], float dm[8]) {
@@ -261,10 +269,13 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
         mx = fmaxf(mx, fabsf(xv[i]));
         sm += xv[i];
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    sm += __shfl_xor(sm, 1);
-    sm += __shfl_xor(sm, 2);
+    mx = fmaxf(mx, xor32<1>(mx));
+    mx = fmaxf(mx, xor32<2>(mx));
+    mx = fmaxf(mx, xor32<4>(mx));
+    mx = fmaxf(mx, xor32<8>(mx));
+    mx = fmaxf(mx, xor32<16>(mx));
+    sm += xor32<1>(sm);
+    sm += xor32<2>(sm);
     // scale 2^e with e = 14 - floor(log2 mx), limited so 2^e and 2^(24-e) are normal
     const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
     int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
@@ -398,10 +409,13 @@ __device__ __forceinline__ void stage_group16(const float4 a, const float4 b, in
         mx = fmaxf(mx, fabsf(xv[i]));
         sm += xv[i];
     }
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    sm += __shfl_xor(sm, 1);
-    sm += __shfl_xor(sm, 2);
+    mx = fmaxf(mx, xor32<1>(mx));
+    mx = fmaxf(mx, xor32<2>(mx));
+    mx = fmaxf(mx, xor32<4>(mx));
+    mx = fmaxf(mx, xor32<8>(mx));
+    mx = fmaxf(mx, xor32<16>(mx));
+    sm += xor32<1>(sm);
+    sm += xor32<2>(sm);
     const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
     int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
     e = max(-103, min(127, e));
@@ -610,13 +624,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     const int N = P.N, K = P.K;
     const int KB = K >> 8;
     const int wpt = wide_wpt(KB, WAVES);
-    const int T = WAVES / wpt;
+    const int lg = __builtin_ctz(wpt);  // wpt is a power of two: shifts, not divisions
+    const int T = WAVES >> lg;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
     const int col = lane & 31, half = lane >> 5;
-    const int tl = wave / wpt, kw = wave - tl * wpt;  // tile within the group, K lane
+    const int tl = wave >> lg, kw = wave & (wpt - 1);  // tile within the group, K lane
     const int n0 = ((g - P.tile_begin) * T + tl) * kCols;
     const bool active = n0 < N;  // the last group of a product may be short
 
@@ -654,7 +669,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     // 0..31 for the first block, 32..63 for the second) and both blocks, into
     // registers.  (Requesting the second block only after the first arrived,
     // to overlap its transfer with the first block's arithmetic, was slower.)
-    const int nb = active && KB > kw ? (KB - kw + wpt - 1) / wpt : 0;
+    const int nb = active && KB > kw ? (KB - kw + wpt - 1) >> lg : 0;
     for (int i0 = 0; i0 < nb; i0 += 2) {
         const int bi = min(i0 + half, nb - 1);  // a lone last block is staged twice
         const float4 *src =

@@ -56,12 +56,14 @@ __device__ __forceinline__ int find_problem(const Batch &bt, int g) {
     static_assert(kMaxBatch == 32, "table read as two 16-entry vectors");
     const int16v t0 = *reinterpret_cast<const int16v *>(bt.tb);
     const int16v t1 = *reinterpret_cast<const int16v *>(bt.tb + 16);
-    int p = 0;
+    // (t - g - 1) >> 31 (unsigned) is 1 exactly when t <= g (t, g >= 0): plain
+    // integer arithmetic on uniform values, so it stays on the scalar unit.
+    uint32_t p = 0;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) p += g >= t0[i] ? 1 : 0;
+    for (int i = 1; i < 16; ++i) p += static_cast<uint32_t>(t0[i] - g - 1) >> 31;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p += g >= t1[i] ? 1 : 0;
-    return __builtin_amdgcn_readfirstlane(p);  // uniform: keeps the problem's fields in scalar loads
+    for (int i = 0; i < 16; ++i) p += static_cast<uint32_t>(t1[i] - g - 1) >> 31;
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(p));  // uniform: the fields stay in scalar loads
 }
 
 // The problem's fields, requested together (one round trip) rather than each
