@@ -26,9 +26,15 @@ Also reported in the same line:
   * ``layer_sweep``: one Qwen3-14B-shaped layer at M = 1 .. 1024 (microseconds
     per batched launch, weight GB/s, TFLOP/s, kernel family);
   * ``cross_check_*``: agreement of the timed kernels with a second kernel
-    family on the last layer (max |difference| / max |value|).
+    family on the last layer (max |difference| / max |value|);
+  * ``launch_groupings``: the decode pass with one launch per projection, with
+    the dependency groups {q,k,v}, {o}, {gate,up}, {down}, and per layer;
+  * ``other_workloads``: the 1024x1024 GEMV (latency), the Llama-3.2-3B-shaped
+    prefill chunk at M = 32 and the Qwen3-14B-shaped pass at M = 1, 4, 16
+    (graph replays, weight GB/s against the HBM bound).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-prefill] [--no-cpu] [--no-sweep]
+                       [--no-others]
 """
 from __future__ import annotations
 
@@ -57,7 +63,9 @@ def log(*a):
 class Pass:
     """Device-resident inputs of one workload at one M, and its launch list."""
 
-    def __init__(self, wl, M, dev):
+    def __init__(self, wl, M, dev, weights_from=None):
+        """weights_from: another Pass of the same workload whose device weights
+        are reused (same seeds, so the same bytes) instead of uploaded again."""
         import torch
         import q4k_inputs as qi
         from q4k_inputs.workloads import PROJ_ID, X_ROLE
@@ -72,9 +80,12 @@ class Pass:
         self.layers = []
         for li in range(wl.layers):
             probs = []
-            for name, N, K in wl.layer:
-                w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, li, PROJ_ID[name]))
-                wd = torch.from_numpy(w).to(dev)
+            for pi, (name, N, K) in enumerate(wl.layer):
+                if weights_from is not None:
+                    wd = weights_from.layers[li][pi][0]
+                else:
+                    w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, li, PROJ_ID[name]))
+                    wd = torch.from_numpy(w).to(dev)
                 if name not in self.y:
                     self.y[name] = torch.empty((M, N), dtype=torch.float32, device=dev)
                 probs.append((wd, self.x[X_ROLE[name]], self.y[name]))
@@ -82,8 +93,12 @@ class Pass:
         self.head = None
         if wl.lm_head is not None:
             name, N, K = wl.lm_head
-            w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, -1, PROJ_ID[name]))
-            self.head = (torch.from_numpy(w).to(dev), self.x[X_ROLE[name]],
+            if weights_from is not None:
+                wh = weights_from.head[0]
+            else:
+                w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, -1, PROJ_ID[name]))
+                wh = torch.from_numpy(w).to(dev)
+            self.head = (wh, self.x[X_ROLE[name]],
                          torch.empty((M, N), dtype=torch.float32, device=dev))
         self.weight_bytes = wl.weight_bytes()
         self.flops = 2 * M * wl.weights()
@@ -299,6 +314,69 @@ def layer_sweep(q4k, dev, reps=5, sets=2):
             "weight_bytes": wbytes, "weight_copies": sets, "points": points}
 
 
+def launch_groupings(ps, q4k, steps, warmup):
+    """The decode pass under three launch groupings, graph replays: one launch
+    per projection, the dependency groups {q,k,v}, {o}, {gate,up}, {down} (the
+    order a real layer can run in), and one batched call per layer (the
+    headline).  The lm_head is one launch in each."""
+    groups = {"per_projection": [[i] for i in range(7)],
+              "dependency_groups": [[0, 1, 2], [3], [4, 5], [6]],
+              "per_layer": [list(range(7))]}
+    out = {}
+    for label, parts in groups.items():
+        calls = [q4k.prepare_batched([probs[i] for i in part]) for probs in ps.layers for part in parts]
+        calls.append(q4k.prepare_batched([ps.head]))
+        ms = _time_replays(_capture(lambda st: [c(st) for c in calls]), steps, warmup)
+        out[label] = {"launches_per_step": len(calls), "us_per_step": round(ms * 1e3, 2),
+                      "weight_GBps": round(ps.weight_bytes / (ms * 1e-3) / 1e9, 1)}
+        del calls
+    return out
+
+
+def pass_figures(ps, q4k, steps, warmup, bound):
+    """One workload pass (one batched call per layer, plus the lm_head) as graph
+    replays: time, weight GB/s, TFLOP/s and the fraction of its bound."""
+    ms, _ = time_pass(ps, q4k, steps, warmup)
+    gbps = ps.weight_bytes / (ms * 1e-3) / 1e9
+    tflops = ps.flops / (ms * 1e-3) / 1e12
+    frac = gbps / HBM_PEAK_GBS if bound == "hbm" else tflops / FP16_PEAK_TFLOPS
+    return {"workload": ps.wl.name, "M": ps.M, "layers": ps.wl.layers, "us_per_step": round(ms * 1e3, 2),
+            "weight_GBps": round(gbps, 1), "TFLOPs": round(tflops, 2), "bound": bound,
+            "roofline_frac": round(frac, 4)}
+
+
+def other_workloads(q4k, dev, steps, warmup):
+    """The other configurations of the workload list: the single 1024x1024 GEMV
+    (0.59 MB: cache-resident and launch-bound, so its latency only), the
+    Llama-3.2-3B-shaped prefill chunk at M = 32 (HBM-bound, 114 flop/B) and
+    the Qwen3-14B-shaped pass (40 layers + lm_head) at M = 1, 4, 16."""
+    import torch
+    from q4k_inputs.workloads import WORKLOADS
+    out = {}
+    g = Pass(WORKLOADS["gemv_1024x1024_m1"], 1, dev)
+    g.prepare(q4k)
+    reps = 64  # back-to-back launches in one graph: the replay's own cost is spread out
+    ms = _time_replays(_capture(lambda st: [g.calls[0](st) for _ in range(reps)]), steps, warmup) / reps
+    out["gemv_1024x1024_m1"] = {"us_per_launch": round(ms * 1e3, 2), "launches_per_graph": reps,
+                                "note": "0.59 MB of weights: cache-resident, launch-bound"}
+    del g
+    p3 = Pass(WORKLOADS["llama3.2-3b_prefill_m32"], 32, dev)
+    out["llama3.2-3b_prefill_m32"] = pass_figures(p3, q4k, steps, warmup, "hbm")
+    del p3
+    torch.cuda.empty_cache()
+    wl = WORKLOADS["qwen3-14b_sweep"]
+    base = None
+    for M in (1, 4, 16):
+        ps = Pass(wl, M, dev, weights_from=base)
+        if base is None:
+            base = ps
+        out[f"qwen3-14b_decode_m{M}"] = pass_figures(ps, q4k, steps, warmup, "hbm")
+        log(f"qwen3-14b pass at M={M}: {out[f'qwen3-14b_decode_m{M}']}")
+    del base, ps
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(ps, budget_s=10.0):
     """Oracle (as written, OpenMP over output columns) on a bounded sample: the
     pass's projections in order, repeated, until about budget_s of CPU time."""
@@ -339,6 +417,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the launch groupings and the other workloads of the list")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy three times (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -394,6 +474,9 @@ def main():
     }
     out["lm_head_argmax"] = time_head_argmax(ps, q4k, args.steps, args.warmup)
     log(f"lm_head argmax: {out['lm_head_argmax']}")
+    if not args.no_others:
+        out["launch_groupings"] = launch_groupings(ps, q4k, args.steps, args.warmup)
+        log(f"launch groupings: {out['launch_groupings']}")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(ps)
         log(f"cpu baseline: {out['cpu_baseline']}")
@@ -421,6 +504,10 @@ def main():
                          "avg_launch_us": round(ms_pl * 1e3, 2)}}
         log(f"prefill: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
             f"-> {ach:.1f} TFLOP/s; cross-check {xcheck_p:.2e}")
+    if not args.no_others:
+        t = time.time()
+        out["other_workloads"] = other_workloads(q4k, dev, min(args.steps, 10), args.warmup)
+        log(f"other workloads ({time.time() - t:.1f} s): {out['other_workloads']}")
     if not args.no_sweep:
         t = time.time()
         out["layer_sweep"] = layer_sweep(q4k, dev)

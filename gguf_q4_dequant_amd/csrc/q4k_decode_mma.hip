@@ -598,6 +598,7 @@ void decode_mma_kernel(Batch bt) {
 // activations of its own super-blocks (one group of 8 per lane for a pair),
 // so no wave waits for another before the final sum.
 constexpr int kWideWaves = 16;
+constexpr int kCus = 256;  // MI355X compute units
 constexpr int kWideMaxGroups = 512;  // about two rounds of one workgroup per CU
 
 // Waves per tile: the power of two (at most the workgroup's WAVES) that
@@ -774,7 +775,18 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         // Sixteen waves per workgroup (one per CU) when the launch fits in
         // about two rounds; otherwise four-wave workgroups, several per CU,
         // which keep every CU busy across rounds whatever the row length.
-        if (wide_groups(b, kWideWaves) <= kWideMaxGroups) return launch_wide<kWideWaves>(b, order, stream);
+        const int g16 = wide_groups(b, kWideWaves);
+        if (g16 <= kWideMaxGroups) {
+            // Less than one round of sixteen-wave workgroups and no row longer
+            // than eight super-blocks: four-wave workgroups of one tile each
+            // spread the launch over four times as many CUs (a lone
+            // projection, or a group such as {q, k, v}).
+            bool short_rows = g16 < kCus;
+            for (int i = 0; i < b.count; ++i)
+                if (wide_wpt(b.p[i].K / kBlockWeights, kWideWaves) > 4) short_rows = false;
+            if (short_rows) return launch_wide<4>(b, order, stream);
+            return launch_wide<kWideWaves>(b, order, stream);
+        }
         return launch_wide<4>(b, order, stream);
     }
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
