@@ -787,6 +787,14 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             if (short_rows) return launch_wide<4>(b, order, stream);
             return launch_wide<kWideWaves>(b, order, stream);
         }
+        // Several rounds: four-wave workgroups (two super-blocks per wave) for
+        // rows of up to eight super-blocks, eight-wave ones for longer rows, so
+        // that fewer pairs run one after another in each wave (Qwen3-14B-shaped
+        // layer 42 -> 40.7 us; the Llama-3.2-1B lm_head prefers four, 29.6
+        // against 32.8 us).
+        int max_kb = 0;
+        for (int i = 0; i < b.count; ++i) max_kb = max(max_kb, b.p[i].K / kBlockWeights);
+        if (max_kb > 8) return launch_wide<8>(b, order, stream);
         return launch_wide<4>(b, order, stream);
     }
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
