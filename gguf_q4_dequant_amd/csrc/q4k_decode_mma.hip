@@ -18,8 +18,11 @@
 //   * Activations are split into two binary16 rows, x' = hi + lo with
 //     hi = rn(x'), lo = rn(x' - hi) (about 22 significant bits), after scaling
 //     each super-block of each token by a power of two 2^e that puts its
-//     largest magnitude in [2^14, 2^15).  Token t uses A rows 2t (hi) and
-//     2t+1 (lo); the other rows of the 32 are don't-care.
+//     largest magnitude in [2^14, 2^15).  Up to 8 tokens (pair rows): token t
+//     uses A rows 2t (hi) and 2t+1 (lo); the other rows of the 32 are
+//     don't-care.  9..16 tokens (token rows): v_mfma_f32_16x16x32_f16 with
+//     the tokens as the 16 A rows, the hi and the lo operand in two MFMAs
+//     accumulating into one result (see mma_block_rows).
 //   * Two MFMAs give one sub-block's sum_k x'_tk q_k * 2^-24 for 32 rows; the
 //     per-row scale d*sc_j (d*sc_j/16 for high nibbles) is applied to that
 //     fp32 result, the factor 2^(24-e) once per super-block, and the min term
@@ -33,11 +36,13 @@
 //     uses v_mfma_f32_16x16x32_f16 instead: one MFMA covers a whole 32-weight
 //     sub-block for 16 rows of W, with hi in the even and lo in the odd rows
 //     of A (see mma_block16).
-//   * Kernels: for M = 1, workgroups of sixteen waves (four for launches of
-//     more than about two rounds), each wave owning about two
-//     super-blocks of one 32-row tile and staging its own activations; for
-//     2 <= M <= 16 four waves per 32-row tile, staging the activations of all
-//     tokens in passes over K.  In both, the waves of a tile add their
+//   * Kernels: for M = 1, workgroups of sixteen waves (four or eight for
+//     launches of more than about two rounds, four for small launches of
+//     short rows), each wave owning about two super-blocks of one 32-row tile
+//     and staging its own activations; for 2 <= M <= 16, eight-wave
+//     workgroups on two tiles of four waves (up to 8 tokens) or four tiles of
+//     two waves (9..16), sharing one staged copy of the activations of all
+//     tokens, pass by pass over K.  In both, the waves of a tile add their
 //     partial sums through LDS (no second kernel).
 #include "q4k_internal.h"
 
