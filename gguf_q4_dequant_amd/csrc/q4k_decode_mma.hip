@@ -624,6 +624,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][2 * 64];
     __shared__ float xsumw[WAVES][2 * 8];
     __shared__ float xmulw[WAVES][2];
+    __shared__ float red[WAVES * 64];  // partial sums (own array: one barrier before the final sum)
     const int g = static_cast<int>(blockIdx.x);
     const int p = find_problem(bt, g);
     const DevProblem P = load_problem(bt, p);
@@ -695,8 +696,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
         }
     }
 
-    __syncthreads();
-    float *red = reinterpret_cast<float *>(wslots);
     red[wave * 64 + lane] = acc[0];
     __syncthreads();
     if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
