@@ -17,18 +17,17 @@
 //     step's work (x stores, W dequantization and stores, fragment reads), so
 //     that the matrix cores keep working while the rest goes on; each slot's
 //     loads for the step after are issued as soon as the slot is consumed.
-//   * M <= 64: 32x128 tiles, four waves of 32x32, a register ring eight
-//     k-steps deep, and K cut into chunks of at most eight blocks (one
-//     workgroup each, partial tiles summed in chunk order by a second kernel),
-//     so that short and long K even out and each CU holds several workgroups.
+//   * M <= 64: 32x128 tiles, four waves of 32x32 (32x64 tiles, two waves,
+//     when the batch has too few 32x128 tiles), a register ring four k-steps
+//     deep, and K cut into chunks of at most eight blocks (one workgroup each,
+//     partial tiles summed in chunk order by a second kernel), so that short
+//     and long K even out and each CU holds several workgroups.
 //   * Long rows are cut into K chunks on the 256x256 tiles too: beyond 16
 //     blocks up to 512 tokens, beyond 48 blocks above that.
 //
 // Tile order: workgroup i runs on XCD i % 8, so consecutive tiles are dealt
 // out XCD by XCD: each XCD receives a contiguous run of tiles in which the
 // N tiles of one M tile (same rows of x) are adjacent and share that XCD's L2.
-#include <type_traits>
-
 #include "q4k_internal.h"
 
 namespace q4k {
@@ -40,11 +39,8 @@ constexpr int kXcds = 8;
 // Tile shape: BM rows of x by BN rows of W per workgroup, 2*BN threads (two
 // per W row for dequantization), waves in a WM x WN grid each owning a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-template <int BM_, int BN_, int WM_, int WN_, int R_, bool XF32_>
+template <int BM_, int BN_, int WM_, int WN_, int R_>
 struct Shape {
-    // x read as float32 and rounded to binary16 by the kernel itself (no
-    // pre-pass): worth it when few x rows are read per W tile.
-    static constexpr bool kXF32 = XF32_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
     static constexpr int kThreads = 2 * BN;
@@ -60,18 +56,29 @@ struct Shape {
     static_assert(R == 1 || (TA == 1 && TB == 1), "ring pipeline: one MFMA block per wave");
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
-using BigTile = Shape<256, 256, 2, 4, 1, false>;
+using BigTile = Shape<256, 256, 2, 4, 1>;
 // Up to one 128-row tile of tokens: 128x256 tiles, eight waves of 64x64, the
 // same loop with half the MFMAs and x per step.
-using MidTile = Shape<128, 256, 2, 4, 1, false>;
+using MidTile = Shape<128, 256, 2, 4, 1>;
 // Qwen3-8B-shaped layer: M = 65..128 144 -> 104..107 us; at M = 160..256
 // two tile rows of 128 cost more than one of 256 (147 -> 184 us at M = 160).
 constexpr int kMidTileMaxM = 128;
 // Few tokens (the W stream dominates and the output tiles alone would leave
-// about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads eight
-// steps (two blocks) ahead.
-using SmallTile = Shape<32, 128, 1, 4, 8, true>;
+// about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads four
+// steps (one block) ahead, at most 168 VGPRs so that three waves share a
+// SIMD.  (Eight steps ahead, with the kernel rounding float32 x itself,
+// needs 233 VGPRs, two waves per SIMD: Qwen3-14B-shaped layer at M = 32 and
+// 64 109 and 197 us, against 98 and 165 us.)
+using SmallTile = Shape<32, 128, 1, 4, 4>;
+// The same with 64-row W tiles (two waves), twice the workgroups, for
+// batches whose 32x128 tiles would not fill three workgroups per CU
+// (Llama-3.2-3B-shaped pass at M = 32: 1100 -> 1047 us; on the Qwen3-14B
+// layer, with enough tiles, it loses: 98 -> 106 us).  Every output sums its
+// k in the same order on both shapes, so they agree bit for bit.
+using NarrowTile = Shape<32, 64, 1, 2, 4>;
 constexpr int kSmallTileMaxM = 64;
+constexpr int kSmallWaves = 3;  // waves per SIMD (launch bound) of both
+constexpr int kNarrowBelow = kSmallWaves * 256;  // 32x128 tiles in the batch
 
 // Split K: a problem whose K/256 exceeds `above` is cut into
 // ceil(K/256 / chunk) near-equal chunks, one workgroup each; a second kernel
@@ -257,32 +264,11 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // t/2 of the W tile (16 quant bytes: 16 weights of each of the two
     // sub-blocks of this k-step).
     const _Float16 *xcol = XH + static_cast<size_t>(kb0) * kBlockWeights + 8 * (t & 7);
-    const float *xcolf = P.x + static_cast<size_t>(kb0) * kBlockWeights + 8 * (t & 7);
     const int xr0 = tm0 + (t >> 3);
-    // A raw x chunk: 8 binary16 values, or (kXF32) the 8 float32 values.
-    struct XPair {
-        uint4 a, b;
-    };
-    using XRaw = typename std::conditional<S::kXF32, XPair, uint4>::type;
-    auto x_chunk = [&](int j, int s) -> XRaw {
+    // 16 bytes (8 binary16 values) of x row xr0 + XROWS*j (clamped) at step s.
+    auto x_chunk = [&](int j, int s) -> uint4 {
         const size_t row = static_cast<size_t>(min(xr0 + S::XROWS * j, M - 1));
-        if constexpr (S::kXF32) {
-            const float *src = xcolf + row * K + static_cast<size_t>(s) * kBK;
-            return XPair{*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 4)};
-        } else {
-            return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
-        }
-    };
-    // The 16 bytes of binary16 x that a raw chunk becomes (nearest even).
-    auto x_bits = [&](const XRaw &v) -> uint4 {
-        if constexpr (S::kXF32) {
-            const float4 a = __builtin_bit_cast(float4, v.a), b = __builtin_bit_cast(float4, v.b);
-            const half8 h = {(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
-                             (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
-            return __builtin_bit_cast(uint4, h);
-        } else {
-            return v;
-        }
+        return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
     };
     const int wr = t >> 1, wh = t & 1;
     const uint8_t *wrow = W + (static_cast<size_t>(min(tn0 + wr, N - 1)) * KB + kb0) * kBlockBytes;
@@ -297,7 +283,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // never used): the loads stay unconditional, so the waits before a slot
     // is used count only the newer requests.
     constexpr int R = S::R;
-    XRaw xr[R][S::XC];
+    uint4 xr[R][S::XC];
     uint4 wq[R], whd[R];
     RowScales rs;
     auto load_x = [&](int r, int s_req) {
@@ -322,7 +308,7 @@ __global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, Ge
     // every step, so that the step has no branch.
     auto store_x = [&](int r, uint4 *A) {
 #pragma unroll
-        for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = x_bits(xr[r][j]);
+        for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = xr[r][j];
     };
     // Scales of sub-blocks 2g (low nibbles, k 0..31) and 2g+1 (high nibbles,
     // k 32..63) of this thread's W row: quant byte l of the group -> k = l and
@@ -581,6 +567,7 @@ struct Plan {
     int order[kMaxBatch];
     int xcd_first[kXcds + 1];
     int grid;
+    int tiles;              // workgroups with work (grid rounds up to whole XCD ranges)
     size_t partial_floats;  // [splits][M][N] per split problem
 };
 
@@ -644,6 +631,7 @@ void make_plan(const Batch &b, SplitRule rule, Plan &pl) {
     int longest = 0;
     for (int c = 0; c < kXcds; ++c) longest = max(longest, pl.xcd_first[c + 1] - pl.xcd_first[c]);
     pl.grid = longest * kXcds;
+    pl.tiles = tiles;
 }
 
 // Launch one tile shape (after the binary16 copies of x are queued).
@@ -711,15 +699,16 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     const bool small = b.M <= kSmallTileMaxM;
     Plan pl;
     const bool mid = !small && b.M <= kMidTileMaxM;
-    if (small)
+    bool narrow = false;
+    if (small) {
         make_plan<SmallTile>(b, kSmallSplit, pl);
-    else if (mid)
+        narrow = pl.tiles < kNarrowBelow;
+        if (narrow) make_plan<NarrowTile>(b, kSmallSplit, pl);
+    } else if (mid)
         make_plan<MidTile>(b, kMidSplit, pl);
     else
         make_plan<BigTile>(b, b.M <= kMidMaxM ? kMidSplit : kBigSplit, pl);
-    // Workspace: the binary16 activations (unless the tile reads float32 x
-    // itself), then the split-K partial sums.
-    if (small && SmallTile::kXF32) halves = 0;
+    // Workspace: the binary16 activations, then the split-K partial sums.
     const size_t part_off = (halves * sizeof(_Float16) + 255) & ~static_cast<size_t>(255);
     float *wsp = nullptr;
     hipError_t err = workspace(stream, part_off + pl.partial_floats * sizeof(float), &wsp);
@@ -728,10 +717,6 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(wsp) + part_off);
 
     const _Float16 *xh[kMaxBatch];
-    if (small && SmallTile::kXF32) {
-        for (int i = 0; i < b.count; ++i) xh[i] = nullptr;
-        return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
-    }
     CvtBatch cb;
     cb.count = 0;
     int cblocks = 0;
@@ -750,7 +735,8 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     if (err != hipSuccess) return err;
 
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
-    if (small) return launch_gemm<SmallTile, 2>(pl, xh, part, stream);
+    if (narrow) return launch_gemm<NarrowTile, kSmallWaves>(pl, xh, part, stream);
+    if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);
 }
