@@ -10,8 +10,8 @@
 //
 // Two tile shapes, both through double-buffered LDS:
 //   * M > 128: 256x256 tiles, eight waves (two per SIMD), each owning a
-//     128x64 block of the output tile (65 <= M <= 128: 128x256 tiles, blocks
-//     of 64x64, the same loop with half the MFMAs and x per step; each output
+//     128x64 block of the output tile (65 <= M <= 128: 128x128 tiles, four
+//     waves of 64x64, the same loop with half the MFMAs and x per step; each output
 //     sums its k in the same order, so the two shapes agree bit for bit).  A k-step runs in four phases, one per
 //     16-deep k slice, in which the slice's MFMAs alternate with the next
 //     step's work (x stores, W dequantization and stores, fragment reads), so
@@ -57,11 +57,14 @@ struct Shape {
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
 using BigTile = Shape<256, 256, 2, 4, 1>;
-// Up to one 128-row tile of tokens: 128x256 tiles, eight waves of 64x64, the
-// same loop with half the MFMAs and x per step.
-using MidTile = Shape<128, 256, 2, 4, 1>;
-// Qwen3-8B-shaped layer: M = 65..128 144 -> 104..107 us; at M = 160..256
-// two tile rows of 128 cost more than one of 256 (147 -> 184 us at M = 160).
+// Up to one 128-row tile of tokens: 128x128 tiles, four waves of 64x64, the
+// same loop with half the MFMAs and x per step; 64 KB of LDS, so two
+// workgroups share a CU.  (Qwen3-8B-shaped layer: M = 65..128 144 ->
+// 104..107 us against 256x256 tiles; Qwen3-14B-shaped layer at M = 128
+// 190..192 us with 128x256 tiles, one workgroup per CU, 173..177 us with
+// these.)  At M = 160..256 two tile rows of 128 cost more than one of 256
+// (147 -> 184 us at M = 160, 128x256 tiles).
+using MidTile = Shape<128, 128, 2, 2, 1>;
 constexpr int kMidTileMaxM = 128;
 // Few tokens (the W stream dominates and the output tiles alone would leave
 // about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads four

@@ -58,7 +58,7 @@ def test_decode_family_matches_oracle(path, M, N, K):
 
 PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 2048), (200, 300, 256),
                   (17, 45, 1280), (1, 128, 1024), (256, 129, 3072),
-                  # 128x256 tiles up to 128 tokens, 256x256 above; up to 512 tokens rows
+                  # 128x128 tiles up to 128 tokens, 256x256 above; up to 512 tokens rows
                   # longer than 16 blocks are cut
                   (80, 300, 13056), (130, 70, 17408), (100, 300, 4352), (512, 64, 5120),
                   (65, 40, 768), (128, 257, 2048), (129, 64, 1024),
