@@ -212,16 +212,18 @@ def test_batch_of_32_problems(M):
 @pytest.mark.parametrize("M", [17, 32, 64])
 def test_small_tile_shapes_agree(M):
     """Up to 64 tokens the prefill family uses 32x128 tiles, or 32x64 tiles
-    when a batch has fewer than 768 of the larger ones.  Three N = 16384,
-    K = 4096 problems (256 large tiles each) go through one batched call
-    (32x128) and through three single calls (32x64 each): every output must
-    agree bit for bit, and sampled columns match the oracle."""
+    when a batch has fewer than 768 of the larger ones.  Three K = 4096
+    problems of about 16384 rows (ragged N: 256 large tiles each, the last one
+    short) go through one batched call (32x128) and through three single calls
+    (32x64 each): every output must agree bit for bit, and sampled columns,
+    the last ones included, match the oracle."""
     import torch
-    N, K = 16384, 4096
+    K = 4096
+    Ns = (16347, 16384, 16291)
     x = to_dev(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 720, M)))
     hosts, probs = [], []
-    for i in range(3):
-        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 721, i))
+    for i, N in enumerate(Ns):
+        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 721, i, N))
         hosts.append(w)
         probs.append((to_dev(w), x, torch.empty((M, N), dtype=torch.float32, device=device())))
     q4k.matmul_batched(probs)
@@ -229,9 +231,11 @@ def test_small_tile_shapes_agree(M):
     torch.cuda.synchronize()
     for i, ((_, _, y), ys) in enumerate(zip(probs, singles)):
         assert torch.equal(y, ys), f"problem {i}"
-    cols = np.arange(5, N, 811)
-    y_ref, s = oracle.matmul_cols(hosts[1], x.cpu().numpy(), N, K, cols)
-    check_close(probs[1][2].cpu().numpy()[:, cols], y_ref, s, PREFILL_TOL, "sampled columns")
+    for i in (0, 2):
+        N = Ns[i]
+        cols = np.concatenate([np.arange(5, N, 811), np.arange(N - 40, N)])
+        y_ref, s = oracle.matmul_cols(hosts[i], x.cpu().numpy(), N, K, cols)
+        check_close(probs[i][2].cpu().numpy()[:, cols], y_ref, s, PREFILL_TOL, f"problem {i} sampled columns")
 
 
 @pytest.mark.parametrize("path,Ms", [(DEC, (1, 3, 16)), (PRE, (32, 40, 100)), (GEMV, (1, 3))])
