@@ -75,8 +75,8 @@ constexpr int kMidTileMaxM = 128;
 using SmallTile = Shape<32, 128, 1, 4, 4>;
 // The same with 64-row W tiles (two waves), twice the workgroups, for
 // batches whose 32x128 tiles would not fill three workgroups per CU
-// (Llama-3.2-3B-shaped pass at M = 32: 1100 -> 1047 us; on the Qwen3-14B
-// layer, with enough tiles, it loses: 98 -> 106 us).  Every output sums its
+// (Llama-3.2-3B-shaped pass at M = 32: 1100 -> 1050..1090 us; on the
+// Qwen3-14B layer, with enough tiles, it would lose: 98 -> 106 us).  Every output sums its
 // k in the same order on both shapes, so they agree bit for bit.
 using NarrowTile = Shape<32, 64, 1, 2, 4>;
 constexpr int kSmallTileMaxM = 64;
@@ -223,8 +223,10 @@ __device__ __forceinline__ WordWeights dequant_word(uint32_t w, float a_lo, floa
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 
-template <class S, int MINB>
-__global__ __launch_bounds__(S::kThreads, MINB) void prefill_kernel(Batch bt, GemmArgs ga) {
+// WAVES_PER_EU: HIP's second launch bound, the number of waves per SIMD the
+// kernel's registers must leave room for.
+template <class S, int WAVES_PER_EU>
+__global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batch bt, GemmArgs ga) {
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];  // 16-byte slots
     // buffer b: the x tile (BM x 64 halves) then the W tile (BN x 64 halves)
     auto As = [&](int b) { return lds4 + b * (S::BM + S::BN) * 8; };
@@ -638,11 +640,11 @@ void make_plan(const Batch &b, SplitRule rule, Plan &pl) {
 }
 
 // Launch one tile shape (after the binary16 copies of x are queued).
-template <class S, int MINB>
+template <class S, int WAVES_PER_EU>
 hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
     static bool attr_set = false;  // per process; the attribute is a property of the function
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel<S, MINB>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel<S, WAVES_PER_EU>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(S::kLds));
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -658,7 +660,7 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
             part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<S, MINB>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, sealed(pl.sb), ga);
+    hipLaunchKernelGGL((prefill_kernel<S, WAVES_PER_EU>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, sealed(pl.sb), ga);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.partial_floats == 0) return err;
     Batch red;
