@@ -14,8 +14,9 @@
 namespace q4k {
 namespace {
 
-constexpr int kChunk = 4096;  // logits per workgroup of the first pass
 constexpr int kThreads = 256;
+constexpr int kPerThread = 4;                    // logits per thread, requested together
+constexpr int kChunk = kThreads * kPerThread;    // logits per workgroup of the first pass
 
 __device__ __forceinline__ void take_better(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) {
@@ -41,9 +42,21 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const float *y, int N,
     const int c = static_cast<int>(blockIdx.x), m = static_cast<int>(blockIdx.y);
     const float *row = y + static_cast<size_t>(m) * N;
     const int n0 = c * kChunk, n1 = min(n0 + kChunk, N);
+    // All of a thread's loads first (coalesced across the workgroup), then the
+    // comparisons: one memory round trip per workgroup.
+    float x[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        const int n = n0 + static_cast<int>(threadIdx.x) + j * kThreads;
+        x[j] = n < n1 ? row[n] : -INFINITY;
+    }
     float v = -INFINITY;
     int i = INT_MAX;
-    for (int n = n0 + static_cast<int>(threadIdx.x); n < n1; n += kThreads) take_better(v, i, row[n], n);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        const int n = n0 + static_cast<int>(threadIdx.x) + j * kThreads;
+        if (n < n1) take_better(v, i, x[j], n);
+    }
     wave_best(v, i);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
