@@ -66,6 +66,8 @@ def _load():
     lib.q4k_oracle_dequant.restype = ctypes.c_int
     lib.q4k_oracle_dequant_f64.argtypes = [u8p, i64, i64, f64p]
     lib.q4k_oracle_dequant_f64.restype = ctypes.c_int
+    lib.q4k_oracle_factored_abs.argtypes = [u8p, i64, i64, f64p]
+    lib.q4k_oracle_factored_abs.restype = ctypes.c_int
     lib.q4k_oracle_threads.argtypes = [ctypes.c_int]
     lib.q4k_oracle_threads.restype = ctypes.c_int
     lib.q4k_oracle_matmul.argtypes = [u8p, f32p, i64, i64, i64, f64p, f64p, ctypes.c_int]
@@ -140,6 +142,19 @@ def dequant_exact(w: np.ndarray, K: int) -> np.ndarray:
     rc = _load().q4k_oracle_dequant_f64(_ptr(w2), w2.shape[0], K, _ptr(out))
     if rc != 0:
         raise RuntimeError(f"q4k_oracle_dequant_f64 failed ({rc})")
+    return out
+
+
+def factored_abs(w: np.ndarray, K: int) -> np.ndarray:
+    """[N, K] doubles |d*sc_j*q| + |dmin*m_j| per weight: the magnitude of the two
+    terms whose difference is the weight (>= |w|, equal where either is 0).  A
+    product evaluated as d*sc*(sum x*q) - dmin*m*(sum x) rounds in proportion to
+    sum_k |x_k| * factored_abs[n, k], its error scale."""
+    w2 = _check_w(w, K)
+    out = np.empty((w2.shape[0], K), np.float64)
+    rc = _load().q4k_oracle_factored_abs(_ptr(w2), w2.shape[0], K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"q4k_oracle_factored_abs failed ({rc})")
     return out
 
 

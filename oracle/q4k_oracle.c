@@ -190,6 +190,31 @@ int q4k_oracle_dequant_f64(const uint8_t *w, int64_t rows, int64_t K, double *ou
     return 0;
 }
 
+/* Factored magnitudes, [rows, K] doubles: for weight t of a block (sub-block
+ * j), |d*sc_j*q[t]| + |dmin*m_j|, the size of the two terms whose difference
+ * is the weight.  A kernel that forms sum_j d*sc_j*(sum x*q) - dmin*m_j*(sum x)
+ * makes rounding errors in proportion to sum |x| times these, not to
+ * sum |x*w|; where the two terms cancel (w = 0 with d*sc*q = dmin*m) only
+ * this magnitude stays positive.  Exact in double, as for the weights. */
+int q4k_oracle_factored_abs(const uint8_t *w, int64_t rows, int64_t K, double *out)
+{
+    if (K % QK != 0 || rows < 0 || K < 0)
+        return -2;
+    int64_t row_bytes = (K / QK) * BLOCK_BYTES;
+    double d, dmin;
+    uint8_t sc[8], mn[8], q[256];
+    for (int64_t n = 0; n < rows; ++n) {
+        for (int64_t b = 0; b < K / QK; ++b) {
+            q4k_oracle_decode_block(w + n * row_bytes + b * BLOCK_BYTES, &d, &dmin, sc, mn, q);
+            for (int t = 0; t < QK; ++t) {
+                int j = t / 32;
+                out[n * K + b * QK + t] = fabs(d * (double)sc[j] * (double)q[t]) + fabs(dmin * (double)mn[j]);
+            }
+        }
+    }
+    return 0;
+}
+
 int q4k_oracle_dequant(const uint8_t *w, int64_t rows, int64_t K, float *out)
 {
     if (K % QK != 0 || rows < 0 || K < 0)

@@ -12,6 +12,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "q4k
 Q_RULES = {
     "twice_subblock_plus_parity": lambda t: 2 * (t // 32) + (t % 2),
     "all_one": lambda t: 1,
+    "all_three": lambda t: 3,
     "all_zero": lambda t: 0,
     "t_mod_16": lambda t: t % 16,
 }

@@ -94,6 +94,37 @@ def test_closed_forms_written_in_fixture(golden_blocks):
     np.testing.assert_array_equal(by["E"], (-(t % 16) - 1).astype(np.float32))
     # F: (1 + 3*2^-11) - 2^-24 rounds to the binary32 tie 1 + 3*2^-11 (even fraction)
     np.testing.assert_array_equal(by["F"], np.full(256, 1 + 3 * 2.0 ** -11, np.float32))
+    # G: both terms equal, every weight exactly zero; H: d one binary16 step up
+    np.testing.assert_array_equal(by["G"], np.zeros(256, np.float32))
+    np.testing.assert_array_equal(by["H"], (3 * (j + 1) * 2.0 ** -13).astype(np.float32))
+
+
+def test_factored_magnitude_closed_forms(golden_blocks):
+    """|d*sc_j*q| + |dmin*m_j| per weight, from the chosen fields with exact
+    rationals; never below |w|, equal to it where one term is zero."""
+    for g in golden_blocks:
+        d = half_bits_to_fraction(g.dbits)
+        dmin = half_bits_to_fraction(g.mbits)
+        want = [abs(d * g.sc[t // 32] * g.q[t]) + abs(dmin * g.m[t // 32]) for t in range(256)]
+        got = oracle.factored_abs(g.raw.reshape(1, 144), 256)[0]
+        assert [Fraction(float(v)) for v in got] == want, g.name
+    by = {g.name: g for g in golden_blocks}
+    t = np.arange(256)
+    j = t // 32
+    # G: w = 0 everywhere, yet each term is 3(j+1)/8
+    np.testing.assert_array_equal(oracle.factored_abs(by["G"].raw, 256)[0], 3 * (j + 1) / 4)
+    # C: all quants zero, so the magnitude is dmin*m_j = |w|
+    np.testing.assert_array_equal(oracle.factored_abs(by["C"].raw, 256)[0],
+                                  np.abs(oracle.dequant_exact(by["C"].raw, 256)[0]))
+    w = qi.random_q4k(23, 768, seed=41)
+    f = oracle.factored_abs(w, 768)
+    e = oracle.dequant_exact(w, 768)
+    assert np.all(f >= np.abs(e))
+    # random blocks: sub-blocks whose m_j is zero have magnitude |w| exactly
+    mn = np.stack([oracle.decode_block(b)[3] for b in w.reshape(-1, 144)]).reshape(23, 3, 8)
+    zero_m = np.repeat(mn == 0, 32, axis=2).reshape(23, 768)
+    assert zero_m.any()
+    np.testing.assert_array_equal(f[zero_m], np.abs(e[zero_m]))
 
 
 def test_exact_dequant_matches_closed_forms(golden_blocks):
