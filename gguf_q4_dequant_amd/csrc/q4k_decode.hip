@@ -15,16 +15,19 @@
 //
 // Activations.  The workgroup stages its chunk of x in LDS (each block padded
 // by four floats so that the eight blocks a wave reads at once sit in
-// different banks), and with it the 32-element sums X[m, j] of every
-// sub-block j, reduced across lanes while staging.
+// different banks).
 //
-// Arithmetic (weight w = d*sc_j*q - dmin*m_j on sub-block j):
-//   y[m,n] = sum_j ( d*sc_j * sum_{l in j} x[m,l]*q[l]  -  dmin*m_j * X[m,j] ).
-// The quants are widened with the byte-to-float converts: the low nibbles of a
-// dword are masked in place (0x0F0F0F0F) and the high nibbles are masked
-// without shifting (0xF0F0F0F0, i.e. 16*q), the 1/16 being folded into the
-// scale of the odd sub-block.  Every step is exact except the fp32 roundings
-// of the sums, so a one-hot x reproduces the f32 weight bit for bit.
+// Arithmetic: the definition itself.  Each weight w = d*sc_j*q - dmin*m_j is
+// formed once in fp32 by one fused multiply-add, fma(d*sc_j, q, -dmin*m_j):
+// both products are exact in fp32 (at most 21 and 17 significant bits), so
+// this is the exact weight rounded once, the f32 weight.  Then
+// y[m,n] = sum_l x[m,l]*w[l] with fp32 FMAs.  The quants are widened with
+// the byte-to-float converts: the low nibbles of a dword are masked in place
+// (0x0F0F0F0F) and the high nibbles without shifting (0xF0F0F0F0, i.e. 16*q),
+// the 1/16 being folded into the scale of the odd sub-block (exact: a power
+// of two).  Because every weight is formed before it meets x, weights that
+// are zero contribute exactly zero (a row of cancelling terms d*sc*q =
+// dmin*m gives y = 0), and a one-hot x reproduces the f32 weight bit for bit.
 #include "q4k_internal.h"
 
 namespace q4k {
@@ -57,11 +60,10 @@ __device__ __forceinline__ void load_block(Block &blk, const uint8_t *src) {
 }
 
 // Accumulate one block's contribution for MT activation rows.
-// xs: this block's 256 x values per row (row stride xs_stride floats);
-// xsum: its 8 sub-block sums per row (row stride xsum_stride).
+// xs: this block's 256 x values per row (row stride xs_stride floats).
 template <int MT>
-__device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int xs_stride,
-                                          const float *xsum, int xsum_stride, int mt, float (&yacc)[MT]) {
+__device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int xs_stride, int mt,
+                                          float (&yacc)[MT]) {
     const uint4 hd = blk.v[0];
     const float d = half_bits_to_float(hd.x & 0xFFFFu);
     const float dmin = half_bits_to_float(hd.x >> 16);
@@ -71,15 +73,15 @@ __device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int
     const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
     const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
     const float d16 = d * 0.0625f;  // high nibbles are read as 16*q
-    float a[8], c[8];
+    float a[8], c[8];  // weight = fma(a, q (or 16q), c): c holds -dmin*m
     a[0] = d * byte0(scA);   a[1] = d16 * byte1(scA);
     a[2] = d * byte2(scA);   a[3] = d16 * byte3(scA);
     a[4] = d * byte0(scB);   a[5] = d16 * byte1(scB);
     a[6] = d * byte2(scB);   a[7] = d16 * byte3(scB);
-    c[0] = dmin * byte0(mnA); c[1] = dmin * byte1(mnA);
-    c[2] = dmin * byte2(mnA); c[3] = dmin * byte3(mnA);
-    c[4] = dmin * byte0(mnB); c[5] = dmin * byte1(mnB);
-    c[6] = dmin * byte2(mnB); c[7] = dmin * byte3(mnB);
+    c[0] = -dmin * byte0(mnA); c[1] = -dmin * byte1(mnA);
+    c[2] = -dmin * byte2(mnA); c[3] = -dmin * byte3(mnA);
+    c[4] = -dmin * byte0(mnB); c[5] = -dmin * byte1(mnB);
+    c[6] = -dmin * byte2(mnB); c[7] = -dmin * byte3(mnB);
 
     // The nibble masks come from an opaque scalar move: with the constants in
     // view the compiler narrows each byte to a 4-bit field extract and loses
@@ -94,41 +96,36 @@ __device__ __forceinline__ void block_dot(const Block &blk, const float *xs, int
         const uint32_t qd[8] = {blk.v[1 + 2 * i].x, blk.v[1 + 2 * i].y, blk.v[1 + 2 * i].z,
                                 blk.v[1 + 2 * i].w, blk.v[2 + 2 * i].x, blk.v[2 + 2 * i].y,
                                 blk.v[2 + 2 * i].z, blk.v[2 + 2 * i].w};
-        float ql[32], qh[32];
+        const float al = a[2 * i], ah = a[2 * i + 1], cl = c[2 * i], ch = c[2 * i + 1];
+        float wl[32], wh[32];  // the f32 weights of the two sub-blocks
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const uint32_t lo = qd[u] & lo_mask;
             const uint32_t hi = qd[u] & hi_mask;
-            ql[4 * u + 0] = byte0(lo); ql[4 * u + 1] = byte1(lo);
-            ql[4 * u + 2] = byte2(lo); ql[4 * u + 3] = byte3(lo);
-            qh[4 * u + 0] = byte0(hi); qh[4 * u + 1] = byte1(hi);
-            qh[4 * u + 2] = byte2(hi); qh[4 * u + 3] = byte3(hi);
+            wl[4 * u + 0] = __builtin_fmaf(al, byte0(lo), cl); wl[4 * u + 1] = __builtin_fmaf(al, byte1(lo), cl);
+            wl[4 * u + 2] = __builtin_fmaf(al, byte2(lo), cl); wl[4 * u + 3] = __builtin_fmaf(al, byte3(lo), cl);
+            wh[4 * u + 0] = __builtin_fmaf(ah, byte0(hi), ch); wh[4 * u + 1] = __builtin_fmaf(ah, byte1(hi), ch);
+            wh[4 * u + 2] = __builtin_fmaf(ah, byte2(hi), ch); wh[4 * u + 3] = __builtin_fmaf(ah, byte3(hi), ch);
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             if (m < mt) {
                 const float4 *xl = reinterpret_cast<const float4 *>(xs + m * xs_stride + 64 * i);
-                float al0 = 0.f, al1 = 0.f, ah0 = 0.f, ah1 = 0.f;
+                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
                 for (int v = 0; v < 8; ++v) {
                     const float4 xa = xl[v];
                     const float4 xb = xl[8 + v];
-                    al0 = __builtin_fmaf(xa.x, ql[4 * v + 0], al0);
-                    al1 = __builtin_fmaf(xa.y, ql[4 * v + 1], al1);
-                    al0 = __builtin_fmaf(xa.z, ql[4 * v + 2], al0);
-                    al1 = __builtin_fmaf(xa.w, ql[4 * v + 3], al1);
-                    ah0 = __builtin_fmaf(xb.x, qh[4 * v + 0], ah0);
-                    ah1 = __builtin_fmaf(xb.y, qh[4 * v + 1], ah1);
-                    ah0 = __builtin_fmaf(xb.z, qh[4 * v + 2], ah0);
-                    ah1 = __builtin_fmaf(xb.w, qh[4 * v + 3], ah1);
+                    s0 = __builtin_fmaf(xa.x, wl[4 * v + 0], s0);
+                    s1 = __builtin_fmaf(xa.y, wl[4 * v + 1], s1);
+                    s0 = __builtin_fmaf(xa.z, wl[4 * v + 2], s0);
+                    s1 = __builtin_fmaf(xa.w, wl[4 * v + 3], s1);
+                    s2 = __builtin_fmaf(xb.x, wh[4 * v + 0], s2);
+                    s3 = __builtin_fmaf(xb.y, wh[4 * v + 1], s3);
+                    s2 = __builtin_fmaf(xb.z, wh[4 * v + 2], s2);
+                    s3 = __builtin_fmaf(xb.w, wh[4 * v + 3], s3);
                 }
-                const float *xsm = xsum + m * xsum_stride + 2 * i;
-                float t = yacc[m];
-                t = __builtin_fmaf(a[2 * i], al0 + al1, t);
-                t = __builtin_fmaf(a[2 * i + 1], ah0 + ah1, t);
-                t = __builtin_fmaf(-c[2 * i], xsm[0], t);
-                t = __builtin_fmaf(-c[2 * i + 1], xsm[1], t);
-                yacc[m] = t;
+                yacc[m] += (s0 + s1) + (s2 + s3);
             }
         }
     }
@@ -140,7 +137,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
     constexpr int kChunk = kLanesPerRow * BPL;
     constexpr int kXsRow = kChunk * kXBlockStride;  // floats per staged activation row
     __shared__ __attribute__((aligned(16))) float xs[MT * kXsRow];
-    __shared__ float xsum[MT * kChunk * 8];
 
     const int p = find_problem(bt, static_cast<int>(blockIdx.x));
     const DevProblem P = load_problem(bt, p);
@@ -188,21 +184,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
             X + static_cast<size_t>(m0 + m) * K + static_cast<size_t>(b_begin) * 256)[r];
     }
 
-    // 2. Stage x and the sub-block sums (8 consecutive float4 = one sub-block,
-    //    held by 8 consecutive lanes, summed with shuffles).
+    // 2. Stage x.
 #pragma unroll
     for (int j = 0; j < kXPer; ++j) {
         const int f = tid + j * kThreads;
         const int m = f / nf4;
         const int r = f - m * nf4;
-        float t = (xv[j].x + xv[j].y) + (xv[j].z + xv[j].w);
-        t += __shfl_xor(t, 1);
-        t += __shfl_xor(t, 2);
-        t += __shfl_xor(t, 4);
         if (f < mt * nf4) {
             const int bl = r >> 6;
             *reinterpret_cast<float4 *>(xs + m * kXsRow + bl * kXBlockStride + 4 * (r & 63)) = xv[j];
-            if ((r & 7) == 0) xsum[m * kChunk * 8 + (r >> 3)] = t;
         }
     }
     __syncthreads();
@@ -214,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Batch bt) {
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
         const int bl = s + kLanesPerRow * j;
-        if (bl < nb) block_dot<MT>(blk[j], xs + bl * kXBlockStride, kXsRow, xsum + bl * 8, kChunk * 8, mt, yacc);
+        if (bl < nb) block_dot<MT>(blk[j], xs + bl * kXBlockStride, kXsRow, mt, yacc);
     }
 
     // 4. Sum the row's eight lanes; write y, or this chunk's partial sums.
