@@ -5,6 +5,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/q4k.h"
 #include "q4k_internal.h"
@@ -57,28 +58,29 @@ struct Buffer {
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<std::pair<int, uintptr_t>, int>, Buffer> g_ws;
+// Buffers replaced by larger ones.  They are never freed: a HIP graph
+// captured while one was current keeps its address, and its replays must
+// still find the memory there.
+std::vector<void *> g_retired;
 
-// Grow `b` to at least `bytes`.
-hipError_t grow(Buffer &b, size_t bytes, hipStream_t stream) {
+// Grow `b` to at least `bytes` (at least twice its old size, in 64 KB
+// steps).  No synchronization: the old buffer stays valid for whatever was
+// queued or captured with it.
+hipError_t grow(Buffer &b, size_t bytes) {
     if (b.bytes >= bytes) return hipSuccess;
-    hipError_t err;
-    if (b.ptr) {
-        // kernels queued on this stream may still use the old buffer
-        err = hipStreamSynchronize(stream);
-        if (err != hipSuccess) return err;
-        (void)hipFree(b.ptr);
-        b.ptr = nullptr;
-        b.bytes = 0;
-    }
-    const size_t want = (bytes + 0xFFFF) & ~static_cast<size_t>(0xFFFF);
-    err = hipMalloc(&b.ptr, want);
-    if (err != hipSuccess) {
-        b.ptr = nullptr;
-        return err;
-    }
+    size_t want = bytes > 2 * b.bytes ? bytes : 2 * b.bytes;
+    want = (want + 0xFFFF) & ~static_cast<size_t>(0xFFFF);
+    void *p = nullptr;
+    const hipError_t err = hipMalloc(&p, want);
+    if (err != hipSuccess) return err;
+    if (b.ptr) g_retired.push_back(b.ptr);
+    b.ptr = p;
     b.bytes = want;
     return hipSuccess;
 }
+
+std::mutex g_attr_mutex;
+std::map<std::pair<int, const void *>, hipError_t> g_attr;
 
 }  // namespace
 
@@ -90,10 +92,23 @@ hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot
     if (err != hipSuccess) return err;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Buffer &b = g_ws[std::make_pair(std::make_pair(dev, reinterpret_cast<uintptr_t>(stream)), slot)];
-    err = grow(b, bytes, stream);
+    err = grow(b, bytes);
     if (err != hipSuccess) return err;
     *scratch = static_cast<float *>(b.ptr);
     return hipSuccess;
+}
+
+hipError_t allow_dynamic_lds(const void *kernel, int bytes) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lock(g_attr_mutex);
+    const auto key = std::make_pair(dev, kernel);
+    const auto it = g_attr.find(key);
+    if (it != g_attr.end()) return it->second;
+    err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    g_attr[key] = err;
+    return err;
 }
 
 namespace {

@@ -712,13 +712,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
 template <int NP>
 hipError_t launch_np(Batch &b, int M, hipStream_t stream) {
     constexpr int T = NP == 8 ? 4 : 2, WPT = NP == 8 ? 2 : 4;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(decode_mma_kernel<NP, T, WPT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t ae = allow_dynamic_lds(reinterpret_cast<const void *>(decode_mma_kernel<NP, T, WPT>), 160 * 1024);
+    if (ae != hipSuccess) return ae;
     int groups = 0, lds = 0;
     for (int i = 0; i < b.count; ++i) {
         const int tiles = (b.p[i].N + kCols - 1) / kCols;

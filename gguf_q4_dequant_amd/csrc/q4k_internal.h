@@ -83,12 +83,19 @@ hipError_t launch_decode(Batch &b, hipStream_t stream);
 hipError_t launch_prefill(Batch &b, hipStream_t stream);
 hipError_t launch_decode_mma(Batch &b, hipStream_t stream);
 
-// Library-owned device scratch, per (device, stream, slot), grown on demand
-// (growing synchronizes the stream first), with no guaranteed contents.
-// Slot 0 belongs to the product kernels; slot 1 holds the logits of an
-// argmax call while the product under it uses slot 0.  A null pointer is
-// returned for a zero-byte request.
+// Library-owned device scratch, per (device, stream, slot), grown on demand,
+// with no guaranteed contents.  Growing never frees the buffer it replaces
+// (kernels queued earlier, or a HIP graph captured earlier, may still use
+// it); retired buffers stay allocated until the process ends, and sizes at
+// least double, so they never total more than the live buffer.  Slot 0
+// belongs to the product kernels; slot 1 holds the logits of an argmax call
+// (or the gate and up products of a SwiGLU call) while the product under it
+// uses slot 0.  A null pointer is returned for a zero-byte request.
 hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot = 0);
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (device, kernel); thread-safe.  Returns the first call's result.
+hipError_t allow_dynamic_lds(const void *kernel, int bytes);
 
 // Row-wise argmax of y [M, N] (lowest index among equal maxima; NaN never
 // wins, an all-NaN row gives index 0 and value NaN).  part holds one

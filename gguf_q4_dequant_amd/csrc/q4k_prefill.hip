@@ -642,13 +642,9 @@ void make_plan(const Batch &b, SplitRule rule, Plan &pl) {
 // Launch one tile shape (after the binary16 copies of x are queued).
 template <class S, int WAVES_PER_EU>
 hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
-    static bool attr_set = false;  // per process; the attribute is a property of the function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel<S, WAVES_PER_EU>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(S::kLds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(prefill_kernel<S, WAVES_PER_EU>),
+                                      static_cast<int>(S::kLds));
+    if (e != hipSuccess) return e;
     if (pl.grid == 0) return hipSuccess;
     GemmArgs ga;
     for (int c = 0; c <= kXcds; ++c) ga.xcd_first[c] = pl.xcd_first[c];
@@ -682,17 +678,21 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
 }  // namespace
 
 hipError_t launch_prefill(Batch &b, hipStream_t stream) {
-    // Distinct activations, their binary16 copies in the workspace.
+    // Distinct activations, their binary16 copies in the workspace.  A copy
+    // is keyed on (x, K): problems may share an x pointer with different K,
+    // and each then reads M rows of its own K values.
     const float *xs[kMaxBatch];
+    int xk[kMaxBatch];
     size_t offs[kMaxBatch];
     int nx = 0;
     size_t halves = 0;
     int which[kMaxBatch];
     for (int i = 0; i < b.count; ++i) {
         int k = 0;
-        while (k < nx && !(xs[k] == b.p[i].x)) ++k;
+        while (k < nx && !(xs[k] == b.p[i].x && xk[k] == b.p[i].K)) ++k;
         if (k == nx) {
             xs[nx] = b.p[i].x;
+            xk[nx] = b.p[i].K;
             offs[nx] = halves;
             halves += (static_cast<size_t>(b.M) * b.p[i].K + 127) & ~static_cast<size_t>(127);
             ++nx;
@@ -726,12 +726,10 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     cb.count = 0;
     int cblocks = 0;
     for (int k = 0; k < nx; ++k) {
-        int kk = 0;
-        while (b.p[kk].x != xs[k]) ++kk;
         CvtSeg &sg = cb.s[cb.count++];
         sg.src = xs[k];
         sg.dst = xh_base + offs[k];
-        sg.n4 = static_cast<size_t>(b.M) * b.p[kk].K / 4;
+        sg.n4 = static_cast<size_t>(b.M) * xk[k] / 4;
         sg.blk_begin = cblocks;
         cblocks += static_cast<int>((sg.n4 + 1023) / 1024);
     }

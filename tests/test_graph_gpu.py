@@ -62,3 +62,51 @@ def test_graph_replays_match_eager():
         for y, e in zip(outs, eager):
             assert torch.equal(y, e), f"replay {rep} differs from the eager result"
         del junk
+
+
+def test_graph_survives_workspace_growth_on_its_stream():
+    """A graph captured on a stream keeps the library workspace it was captured
+    with: a later, larger eager call on the same stream grows the workspace,
+    and replays of the graph must still read and write valid memory and give
+    the eager results (the replaced buffer is retired, never freed)."""
+    import gguf_q4_dequant_amd as q4k
+    q4k.library()
+    wp, xp = _dev_inputs(64, 700, 3072, 20)   # prefill: binary16 x + split-K partials in the workspace
+    wd, xd = _dev_inputs(8, 300, 2048, 21)    # small-M decode: staged activations in the workspace
+    small = [q4k.prepare_batched([(wp, xp, torch.empty(64, 700, device="cuda"))]),
+             q4k.prepare_batched([(wd, xd, torch.empty(8, 300, device="cuda"))])]
+    outs = [c._keep[0][2] for c in small]
+    wb, xb = _dev_inputs(512, 4096, 8192, 22)  # much larger workspace needs, same stream
+    big = q4k.prepare_batched([(wb, xb, torch.empty(512, 4096, device="cuda"))])
+    wb2, xb2 = _dev_inputs(16, 9000, 8192, 23)
+    big2 = q4k.prepare_batched([(wb2, xb2, torch.empty(16, 9000, device="cuda"))])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in small:
+            c(side)
+        side.synchronize()
+        eager = [y.clone() for y in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in small:
+                c(side)
+        big(side)   # grows the stream's workspace past what the graph holds
+        big2(side)
+        side.synchronize()
+    torch.cuda.synchronize()
+    junk = [torch.full((1 << 22,), 3.0, device="cuda") for _ in range(4)]  # fresh allocations
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in outs:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(outs, eager):
+            assert torch.equal(y, e), f"replay {rep} after workspace growth differs from the eager result"
+        with torch.cuda.stream(side):
+            big(side)  # eager work on the capture stream between replays
+        torch.cuda.synchronize()
+    del junk
