@@ -156,11 +156,28 @@ def matmul(w, x, y=None, path: int = PATH_AUTO, stream=None):
             raise ValueError("pass y, or w shaped [N, K/256*144]")
         y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.float32, device=x.device)
     M, N, K = _check_operands(w, x, y)
-    rc = library().q4k_matmul_path(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, int(path),
-                                   _stream_handle(stream))
+    lib = library()
+    if int(path) == PATH_AUTO:
+        rc = lib.q4k_matmul(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, _stream_handle(stream))
+    else:
+        rc = lib.q4k_matmul_path(w.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, int(path),
+                                 _stream_handle(stream))
     if rc != OK:
         raise Q4KError(rc, "q4k_matmul")
     return y
+
+
+def _check_outputs(x, index, value, M):
+    """index int32 [M] and value float32 [M], contiguous, on x's device: the
+    library writes them from the GPU and cannot check any of this itself."""
+    import torch
+    if index.dtype != torch.int32 or value.dtype != torch.float32 or index.numel() < M or value.numel() < M:
+        raise ValueError("index must be int32 [M] and value float32 [M]")
+    for name, t in (("index", index), ("value", value)):
+        if not t.is_cuda or t.device != x.device:
+            raise ValueError(f"{name} must be a device tensor on {x.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
 
 
 def matmul_argmax(w, x, N: Optional[int] = None, index=None, value=None, stream=None):
@@ -186,8 +203,7 @@ def matmul_argmax(w, x, N: Optional[int] = None, index=None, value=None, stream=
         index = torch.empty(M, dtype=torch.int32, device=x.device)
     if value is None:
         value = torch.empty(M, dtype=torch.float32, device=x.device)
-    if index.dtype != torch.int32 or value.dtype != torch.float32 or index.numel() < M or value.numel() < M:
-        raise ValueError("index must be int32 [M] and value float32 [M]")
+    _check_outputs(x, index, value, M)
     rc = library().q4k_matmul_argmax(w.data_ptr(), x.data_ptr(), M, N, K, index.data_ptr(),
                                      value.data_ptr(), _stream_handle(stream))
     if rc != OK:
@@ -237,7 +253,11 @@ def matmul_batched(problems: Sequence[Tuple], path: int = PATH_AUTO, stream=None
         elif m != M:
             raise ValueError("all problems of a batch share M")
         arr[i] = _Problem(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
-    rc = library().q4k_matmul_batched_path(arr, len(problems), M, int(path), _stream_handle(stream))
+    lib = library()
+    if int(path) == PATH_AUTO:
+        rc = lib.q4k_matmul_batched(arr, len(problems), M, _stream_handle(stream))
+    else:
+        rc = lib.q4k_matmul_batched_path(arr, len(problems), M, int(path), _stream_handle(stream))
     if rc != OK:
         raise Q4KError(rc, "q4k_matmul_batched")
     return [p[2] for p in problems]
@@ -263,10 +283,16 @@ class PreparedBatch:
                 raise ValueError("all problems of a batch share M")
             self._arr[i] = _Problem(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k)
         self.M, self.count, self.path = M, len(problems), int(path)
-        self._fn = library().q4k_matmul_batched_path
+        lib = library()
+        if self.path == PATH_AUTO:
+            fn = lib.q4k_matmul_batched
+            self._call = lambda st: fn(self._arr, self.count, self.M, st)
+        else:
+            fn = lib.q4k_matmul_batched_path
+            self._call = lambda st: fn(self._arr, self.count, self.M, self.path, st)
 
     def __call__(self, stream=None) -> None:
-        rc = self._fn(self._arr, self.count, self.M, self.path, _stream_handle(stream))
+        rc = self._call(_stream_handle(stream))
         if rc != OK:
             raise Q4KError(rc, "q4k_matmul_batched")
 

@@ -84,3 +84,20 @@ def test_argument_errors_before_any_device_call(lib):
     assert q4k.raw_matmul_batched([(A, A, A, 4, 256), (A, A, A, 4, 100)], 1) == q4k.ERR_BAD_DIM
     assert q4k.raw_matmul_batched([(0, 0, 0, 0, 256)] * 3, 1) == q4k.OK
     assert lib.q4k_matmul_batched(None, 1, 1, None) == q4k.ERR_NULL
+
+
+def test_argmax_output_tensors_are_checked_before_any_call():
+    """The library writes index/value from the GPU and cannot check them: the
+    binding rejects host, foreign-device or non-contiguous output tensors."""
+    import torch
+    x = torch.zeros((2, 256))
+    ok_index = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        q4k._check_outputs(x, ok_index, torch.zeros(2), 2)
+    with pytest.raises(ValueError, match="int32"):
+        q4k._check_outputs(x, torch.zeros(2, dtype=torch.int64), torch.zeros(2), 2)
+    with pytest.raises(ValueError, match="int32"):
+        q4k._check_outputs(x, torch.zeros(1, dtype=torch.int32), torch.zeros(2), 2)
+    # a CPU w/x never reaches the library either
+    with pytest.raises(ValueError, match="device tensors"):
+        q4k.matmul_argmax(torch.zeros((4, 144), dtype=torch.uint8), x, index=ok_index)

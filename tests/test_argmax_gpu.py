@@ -139,3 +139,22 @@ def test_argmax_argument_errors():
     torch.cuda.synchronize()
     y = q4k.matmul(w, x).cpu().numpy()
     assert idx[:2].cpu().numpy().tolist() == np.argmax(y, axis=1).tolist()
+
+
+def test_argmax_rejects_host_and_strided_outputs():
+    """index/value on the host, or strided, are refused before the library is
+    called (it would write them from the GPU)."""
+    import torch
+    dev = device()
+    w = to_dev(qi.random_q4k(8, 256, seed=6))
+    x = torch.ones((2, 256), device=dev)
+    with pytest.raises(ValueError, match="device tensor"):
+        q4k.matmul_argmax(w, x, index=torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):
+        q4k.matmul_argmax(w, x, value=torch.zeros(2))
+    with pytest.raises(ValueError, match="contiguous"):
+        q4k.matmul_argmax(w, x, index=torch.zeros(4, dtype=torch.int32, device=dev)[::2])
+    index, value = q4k.matmul_argmax(w, x)
+    torch.cuda.synchronize()
+    y = q4k.matmul(w, x).cpu().numpy()
+    assert index.cpu().numpy().tolist() == np.argmax(y, axis=1).tolist()

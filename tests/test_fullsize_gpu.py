@@ -35,7 +35,8 @@ def _layer_case(wl, M, layer, ncols=96):
     for (name, N, K, w, x), (_, _, y) in zip(hosts, probs):
         cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, ncols)]))
         y_ref, s = oracle.matmul_cols(w, x, N, K, cols)
-        check_close(y.cpu().numpy()[:, cols], y_ref, s, tol, f"{wl.name} M={M} layer {layer} {name}")
+        got = y[:, torch.from_numpy(cols).to(y.device)].cpu().numpy()
+        check_close(got, y_ref, s, tol, f"{wl.name} M={M} layer {layer} {name}")
 
 
 def _lm_head_case(wl, M, ncols=128):
@@ -48,7 +49,8 @@ def _lm_head_case(wl, M, ncols=128):
     cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(M).integers(0, N, ncols)]))
     y_ref, s = oracle.matmul_cols(w, x, N, K, cols)
     tol = DECODE_TOL if M <= 16 else PREFILL_TOL
-    check_close(y.cpu().numpy()[:, cols], y_ref, s, tol, f"{wl.name} lm_head M={M}")
+    got = y[:, torch.from_numpy(cols).to(y.device)].cpu().numpy()
+    check_close(got, y_ref, s, tol, f"{wl.name} lm_head M={M}")
 
 
 def test_gemv_1024_full():
@@ -77,7 +79,17 @@ def test_llama32_3b_prefill_chunk_layer():
 
 def test_qwen3_8b_long_prefill_layer():
     wl = WORKLOADS["qwen3-8b_prefill_m1024"]
-    _layer_case(wl, 1024, 0, ncols=24)
+    _layer_case(wl, 1024, 0, ncols=96)
+
+
+def test_qwen3_14b_long_prefill_layer_and_lm_head():
+    """M = 1024 on the Qwen3-14B shapes: all seven projections of a layer in one
+    batched call (the K = 17408 down projection is cut into K chunks and summed
+    by the second kernel), the last layer too, and the 151936-row lm_head."""
+    wl = WORKLOADS["qwen3-14b_sweep"]
+    _layer_case(wl, 1024, 0, ncols=64)
+    _layer_case(wl, 1024, wl.layers - 1, ncols=32)
+    _lm_head_case(wl, 1024, ncols=64)
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
