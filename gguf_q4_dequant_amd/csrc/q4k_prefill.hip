@@ -1,8 +1,9 @@
 // Prefill family: Q4_K dequant-matmul on the gfx950 matrix cores for many
 // tokens (M >= 32).
 //
-//   1. x (fp32) is rounded once to binary16 (nearest even) into the library
-//      workspace by a small pre-pass (each distinct x of a batch once).
+//   1. x (fp32) is scaled per row by a power of two and rounded once to
+//      binary16 (nearest even) into the library workspace by a small pre-pass
+//      (each distinct x of a batch once); the fp32 results are scaled back.
 //   2. W is dequantized to binary16 on the way to the matrix cores: every
 //      weight w = d*sc_j*q - dmin*m_j is rounded once (nearest even) from its
 //      exact value by the mixed-precision FMA.
@@ -117,36 +118,89 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
-// ---- pre-pass: x (fp32) -> binary16, nearest even --------------------------
+// ---- pre-pass: x (fp32) -> binary16, nearest even, scaled per row --------
+// Each row m of x is scaled by a power of two 2^e_m that puts its largest
+// magnitude in [2^14, 2^15), then rounded once to binary16.  Scaling by a
+// power of two is exact, so wherever x's own binary16 rounding is normal this
+// is that rounding times 2^e_m; rows of very large values no longer overflow
+// binary16 and rows of very small ones keep eleven significant bits instead
+// of binary16's fixed subnormal quantum.  The factor 2^-e_m that undoes the
+// scaling is stored after the binary16 rows and applied to the fp32 result
+// (also exact).  A copy is laid out as
+//   [M][K] binary16 (padded to 128 values) | [M] float factors (padded).
+__host__ __device__ inline size_t xh_halves(int M, int K) {
+    return (static_cast<size_t>(M) * K + 127) & ~static_cast<size_t>(127);
+}
+__host__ __device__ inline size_t xh_copy_halves(int M, int K) {
+    return xh_halves(M, K) + ((2 * static_cast<size_t>(M) + 127) & ~static_cast<size_t>(127));
+}
+
 struct CvtSeg {
-    const float *src;
-    _Float16 *dst;
-    size_t n4;      // float4 count
-    int blk_begin;  // first workgroup of this segment
+    const float *src;  // [M, K] f32
+    _Float16 *dst;     // the copy, laid out as above
+    int K;
+    int row_begin;     // first workgroup of this segment (one workgroup per row)
 };
 struct CvtBatch {
     CvtSeg s[kMaxBatch];
     int count;
+    int M;
 };
 
-__global__ __launch_bounds__(256) void convert_x_kernel(CvtBatch cb) {
+constexpr int kCvtThreads = 256;
+constexpr int kCvtRegs = 24;  // float4 per thread kept in registers: rows up to 24576 values read once
+
+__global__ __launch_bounds__(kCvtThreads) void convert_x_kernel(CvtBatch cb) {
+    __shared__ float wmax[kCvtThreads / 64];
     int p = 0;
     for (int i = 1; i < cb.count; ++i)
-        if (static_cast<int>(blockIdx.x) >= cb.s[i].blk_begin) p = i;
+        if (static_cast<int>(blockIdx.x) >= cb.s[i].row_begin) p = i;
     const CvtSeg &S = cb.s[p];
-    const size_t base = static_cast<size_t>(static_cast<int>(blockIdx.x) - S.blk_begin) * 256 * 4;
+    const int row = static_cast<int>(blockIdx.x) - S.row_begin;
+    const int n4 = S.K >> 2;
+    const int t = threadIdx.x;
+    const float4 *src = reinterpret_cast<const float4 *>(S.src + static_cast<size_t>(row) * S.K);
+    uint2 *dst = reinterpret_cast<uint2 *>(S.dst + static_cast<size_t>(row) * S.K);
+    auto amax4 = [](float m, float4 v) {
+        return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    };
+    // The row's largest magnitude (NaN compares false and is ignored).
+    float4 v[kCvtRegs];
+    float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const size_t i = base + threadIdx.x + 256 * j;
-        if (i < S.n4) {
-            const float4 v = reinterpret_cast<const float4 *>(S.src)[i];
-            const half2v lo = {(_Float16)v.x, (_Float16)v.y};
-            const half2v hi = {(_Float16)v.z, (_Float16)v.w};
-            uint2 o;
-            o.x = __builtin_bit_cast(uint32_t, lo);
-            o.y = __builtin_bit_cast(uint32_t, hi);
-            reinterpret_cast<uint2 *>(S.dst)[i] = o;
+    for (int j = 0; j < kCvtRegs; ++j) {
+        const int f = t + kCvtThreads * j;
+        if (f < n4) {
+            v[j] = src[f];
+            mx = amax4(mx, v[j]);
         }
+    }
+    for (int f = t + kCvtThreads * kCvtRegs; f < n4; f += kCvtThreads) mx = amax4(mx, src[f]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((t & 63) == 0) wmax[t >> 6] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kCvtThreads / 64; ++w) mx = fmaxf(mx, wmax[w]);
+    // e = 14 - floor(log2 mx), within [-100, 100] so that 2^e and 2^-e are
+    // normal; a row whose largest magnitude is infinite is not scaled.
+    const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
+    const int e = E == 255 ? 0 : max(-100, min(100, 141 - E));
+    const float up = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+    auto cvt = [&](float4 a) {
+        const half2v lo = {(_Float16)(a.x * up), (_Float16)(a.y * up)};
+        const half2v hi = {(_Float16)(a.z * up), (_Float16)(a.w * up)};
+        return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    };
+#pragma unroll
+    for (int j = 0; j < kCvtRegs; ++j) {
+        const int f = t + kCvtThreads * j;
+        if (f < n4) dst[f] = cvt(v[j]);
+    }
+    for (int f = t + kCvtThreads * kCvtRegs; f < n4; f += kCvtThreads) dst[f] = cvt(src[f]);
+    if (t == 0) {
+        float *factor = reinterpret_cast<float *>(S.dst + xh_halves(cb.M, S.K));
+        factor[row] = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
     }
 }
 
@@ -517,13 +571,15 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, acc[a][b][r]);
+                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, m, acc[a][b][r]);
                 }
             }
         }
     };
+    // Undo the per-row scaling of x (a power of two: exact).
+    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
     if (splits == 1) {
-        for_each_out([&](size_t e, float v) { P.y[e] = v; });
+        for_each_out([&](size_t e, int m, float v) { P.y[e] = v * xfac[m]; });
         return;
     }
     // Split K: store this chunk's partial tile ([splits][M][N] in the
@@ -532,7 +588,7 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
     // release it needs writes back the whole L2 of its XCD each time, which
     // costs far more than the second launch.)
     float *part = P.part + static_cast<size_t>(sidx) * M * N;
-    for_each_out([&](size_t e, float v) { part[e] = v; });
+    for_each_out([&](size_t e, int m, float v) { part[e] = v * xfac[m]; });
 }
 
 // y = sum over chunks of the partial sums, in chunk order, for split problems
@@ -694,7 +750,7 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
             xs[nx] = b.p[i].x;
             xk[nx] = b.p[i].K;
             offs[nx] = halves;
-            halves += (static_cast<size_t>(b.M) * b.p[i].K + 127) & ~static_cast<size_t>(127);
+            halves += xh_copy_halves(b.M, b.p[i].K);
             ++nx;
         }
         which[i] = k;
@@ -724,16 +780,17 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     const _Float16 *xh[kMaxBatch];
     CvtBatch cb;
     cb.count = 0;
+    cb.M = b.M;
     int cblocks = 0;
     for (int k = 0; k < nx; ++k) {
         CvtSeg &sg = cb.s[cb.count++];
         sg.src = xs[k];
         sg.dst = xh_base + offs[k];
-        sg.n4 = static_cast<size_t>(b.M) * xk[k] / 4;
-        sg.blk_begin = cblocks;
-        cblocks += static_cast<int>((sg.n4 + 1023) / 1024);
+        sg.K = xk[k];
+        sg.row_begin = cblocks;
+        cblocks += b.M;
     }
-    hipLaunchKernelGGL(convert_x_kernel, dim3(cblocks), dim3(256), 0, stream, cb);
+    hipLaunchKernelGGL(convert_x_kernel, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 

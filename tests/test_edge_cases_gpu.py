@@ -230,3 +230,24 @@ def test_c_abi_entry_points_with_raw_addresses():
         check_close(y.cpu().numpy(), y_ref, s, tol, f"q4k_matmul M={M}")
         assert torch.equal(y, y2), f"q4k_matmul_batched M={M}"
         check_close(y3.cpu().numpy(), y_ref[:, N2:], s[:, N2:], tol, f"q4k_matmul_batched tail M={M}")
+
+
+@pytest.mark.parametrize("path,M", [(PRE, 33), (PRE, 100), (PRE, 300), (DEC, 1), (DEC, 5), (DEC, 12), (GEMV, 1),
+                                    (GEMV, 3)])
+def test_rows_of_very_different_magnitude(path, M):
+    """Rows of x are N(0, 1) times 10^e with e spread evenly from -7 (far below
+    the binary16 normal range) to 5 (above its largest finite value, 65504);
+    one-row calls run once at each end.  Every family scales activations by
+    powers of two before any binary16 rounding, so each row meets its bound."""
+    N, K = 130, 2304
+    w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 940, M))
+    x0 = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 941, M))
+    tol = PREFILL_TOL if path == PRE else DECODE_TOL
+    spreads = [np.array([-7.0]), np.array([5.0])] if M == 1 else [np.round(np.linspace(-7, 5, M))]
+    for e in spreads:
+        x = (x0 * (10.0 ** e).astype(np.float32)[:, None]).astype(np.float32)
+        if M > 1:
+            assert np.abs(x).max() > 65504 and np.abs(x[0]).max() < 6.1e-5
+        y = _run(w, x, N, path)
+        y_ref, s = oracle.matmul(w, x, N, K)
+        check_close(y, y_ref, s, tol, f"path {path} M={M} exponents {e.min():g}..{e.max():g}")
