@@ -38,6 +38,8 @@ ERR_DEVICE = -5
 ERR_ALLOC = -6
 ERR_FORMAT = -7
 ERR_IO = -8
+ERR_SCRATCH = -9
+NOALLOC_SCRATCH_BYTES = 128 << 20
 GGUF_TYPE_Q4_K = 12
 
 PATH_AUTO = 0
@@ -47,6 +49,7 @@ PATH_GEMV = 3
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
+            "q4k_matmul_batched_noalloc",
             "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_gguf_list", "q4k_select_path", "q4k_strerror",
             "q4k_version")
 
@@ -88,6 +91,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_batched.restype = ci
     lib.q4k_matmul_batched_path.argtypes = [ctypes.POINTER(_Problem), ci, ci, ci, vp]
     lib.q4k_matmul_batched_path.restype = ci
+    lib.q4k_matmul_batched_noalloc.argtypes = [ctypes.POINTER(_Problem), ci, ci, vp]
+    lib.q4k_matmul_batched_noalloc.restype = ci
     lib.q4k_matmul_argmax.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp]
     lib.q4k_matmul_argmax.restype = ci
     lib.q4k_matmul_swiglu.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
@@ -316,6 +321,18 @@ def raw_matmul_batched(items: Iterable[Tuple[int, int, int, int, int]], M: int,
     for i, (w, x, y, n, k) in enumerate(items):
         arr[i] = _Problem(w, x, y, n, k)
     return library().q4k_matmul_batched_path(arr, len(items), M, path, stream)
+
+
+def raw_matmul_batched_noalloc(items: Iterable[Tuple[int, int, int, int, int]], M: int,
+                               stream: Optional[int] = None) -> int:
+    """Direct call of q4k_matmul_batched_noalloc (no device allocation; scratch
+    from the library's fixed per-GPU array); items are (w_ptr, x_ptr, y_ptr, N,
+    K); returns the status."""
+    items = list(items)
+    arr = (_Problem * max(len(items), 1))()
+    for i, (w, x, y, n, k) in enumerate(items):
+        arr[i] = _Problem(w, x, y, n, k)
+    return library().q4k_matmul_batched_noalloc(arr, len(items), M, stream)
 
 
 def gguf_tensors(path) -> list:

@@ -82,19 +82,57 @@ hipError_t grow(Buffer &b, size_t bytes) {
 std::mutex g_attr_mutex;
 std::map<std::pair<int, const void *>, hipError_t> g_attr;
 
+// ---- fixed scratch of the allocation-free entry point ----------------------
+// Device memory for q4k_matmul_batched_noalloc: a file-scope device array,
+// one copy per GPU at its own address, held until the process ends.  Host
+// code never uses the array's name as an address: each device's address is
+// looked up once (hipGetSymbolAddress, with that device current) and kept.
+constexpr size_t kScratchBytes = static_cast<size_t>(Q4K_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // per device; null until looked up
+
+hipError_t scratch_address(int dev, void **ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Set for the duration of an allocation-free call on this thread: every
+// workspace request of the kernels it launches is served from `scratch`.
+thread_local bool t_noalloc = false;
+
 }  // namespace
 
-hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot) {
-    *scratch = nullptr;
+hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch_out, int slot) {
+    *scratch_out = nullptr;
     if (bytes == 0) return hipSuccess;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
+    if (t_noalloc) {
+        // slot 0 only: the allocation-free entry runs the plain products
+        if (slot != 0 || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidValue;
+        if (bytes > kScratchBytes) return hipErrorOutOfMemory;  // reported as Q4K_ERR_SCRATCH
+        void *p = nullptr;
+        err = scratch_address(dev, &p);
+        if (err != hipSuccess) return err;
+        *scratch_out = static_cast<float *>(p);
+        return hipSuccess;
+    }
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Buffer &b = g_ws[std::make_pair(std::make_pair(dev, reinterpret_cast<uintptr_t>(stream)), slot)];
     err = grow(b, bytes);
     if (err != hipSuccess) return err;
-    *scratch = static_cast<float *>(b.ptr);
+    *scratch_out = static_cast<float *>(b.ptr);
     return hipSuccess;
 }
 
@@ -176,6 +214,18 @@ int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int p
     return q4k::run(problems, count, M, path, stream);
 }
 
+int q4k_matmul_batched_noalloc(const q4k_problem *problems, int count, int M, hipStream_t stream) {
+    // Same checks, policy and kernels as q4k_matmul_batched; only the
+    // workspace differs (the fixed per-device scratch instead of the
+    // library's growing per-stream buffers), so nothing is allocated.
+    struct Guard {
+        Guard() { q4k::t_noalloc = true; }
+        ~Guard() { q4k::t_noalloc = false; }
+    } guard;
+    const int rc = q4k::run(problems, count, M, Q4K_PATH_AUTO, stream);
+    return rc == Q4K_ERR_ALLOC ? Q4K_ERR_SCRATCH : rc;
+}
+
 int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K, int *index, float *value,
                       hipStream_t stream) {
     if (M < 0 || N < 0 || K < 0) return Q4K_ERR_BAD_DIM;
@@ -215,6 +265,7 @@ const char *q4k_strerror(int status) {
     case Q4K_ERR_ALLOC: return "device workspace allocation failed";
     case Q4K_ERR_FORMAT: return "not a GGUF file (version 2 or 3), or a malformed one";
     case Q4K_ERR_IO: return "file could not be opened or read";
+    case Q4K_ERR_SCRATCH: return "the call needs more device scratch than the fixed no-allocation buffer holds";
     default: return "unknown status";
     }
 }

@@ -66,7 +66,9 @@ enum q4k_status {
     Q4K_ERR_DEVICE = -5,  /* no usable HIP device, or not a gfx950 device */
     Q4K_ERR_ALLOC = -6,   /* the library could not allocate its device workspace */
     Q4K_ERR_FORMAT = -7,  /* not a GGUF file of version 2 or 3, or a malformed / truncated one */
-    Q4K_ERR_IO = -8       /* the file could not be opened or read */
+    Q4K_ERR_IO = -8,      /* the file could not be opened or read */
+    Q4K_ERR_SCRATCH = -9  /* q4k_matmul_batched_noalloc: the call needs more than the
+                             Q4K_NOALLOC_SCRATCH_BYTES of fixed device scratch */
 };
 
 /* y = x . dequant(W)^T for one packed weight matrix.
@@ -88,6 +90,30 @@ typedef struct q4k_problem {
  * layer).  `problems` is a HOST array that is only read during the call.
  * Problems may share x; no y may overlap any x, W or another y. */
 int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, results (bit for bit) and kernels as
+ * q4k_matmul_batched; the only difference is where the kernels' scratch
+ * lives (binary16 copies of x and split-K partial sums of the prefill
+ * family, staged activations of 2..16-token decode, split-K partials of the
+ * fp32 GEMV family): not in the library's growing per-stream workspace but
+ * in one fixed device array of Q4K_NOALLOC_SCRATCH_BYTES per GPU, created
+ * with the library's code on that GPU and held until the process ends.  The
+ * call makes no hipMalloc, hipFree or other allocating call.
+ *   Scratch needed, roughly: prefill (M > 16) 2*M*K bytes per distinct (x, K)
+ *   plus 4*splits*M*N per problem whose K is split (K > 12288 at M > 512);
+ *   2..16 tokens: about 4.3*M*K bytes per distinct (x, K); M = 1: none.
+ *   128 MiB covers, for example, a Qwen3-8B-shaped layer at M = 1024 or the
+ *   17408-deep down projection alone at M = 1024.
+ *   Errors: as for q4k_matmul_batched, and Q4K_ERR_SCRATCH (nothing enqueued)
+ *   when the call needs more scratch than the array holds.
+ *   Every call on one GPU shares that GPU's array and leaves it holding its
+ *   last contents (no kernel relies on them: each writes what it reads
+ *   first).  Calls whose kernels overlap on one GPU (different streams, or
+ *   different host threads) race on the array; serialize them. */
+#define Q4K_NOALLOC_SCRATCH_BYTES (128u << 20)
+int q4k_matmul_batched_noalloc(const q4k_problem *problems, int count, int M, hipStream_t stream);
 
 /* Greedy selection over the product, with the argmax on the device: for each
  * row m of x
