@@ -1,40 +1,46 @@
 """Benchmark of the packed Q4_K dequant-matmul on one MI355X.
 
-Headline (``value``): decode weight GB/s at M = 1 on the Llama-3.2-1B-shaped
-decode pass (16 layers of q, k, v, o, gate, up, down plus the 128256 x 2048
-lm_head, all Q4_K, 695.1 MB of packed weights).  One step is one full pass:
-16 batched launches (one per layer, its seven projections) and one lm_head
-launch, on one stream, with every layer's weights in its own HBM buffers
-(the pass is far larger than the 256 MB last-level cache).  The pass is
-captured once in a HIP graph and replayed, so the host's per-call Python work
-does not pace the GPU; every replay runs all 17 launches in full.  Inputs are
-seeded synthetic data generated on the host and uploaded before timing.
+Headline (``value``): decode weight GB/s at M = 1 on the Qwen3-14B-shaped pass,
+the largest M = 1 workload (40 layers of q, k, v, o, gate, up, down plus the
+151936 x 5120 lm_head, all Q4_K, 7869.4 MB of packed weights).  One step is
+one full pass: 40 batched launches (one per layer, its seven projections) and
+one lm_head launch, on one stream, with every layer's weights in its own HBM
+buffers (the pass is far larger than the 256 MB last-level cache).  The pass
+is captured once in a HIP graph and replayed, so the host's per-call Python
+work does not pace the GPU; every replay runs all 41 launches in full.
+Inputs are seeded synthetic data generated on the host and uploaded before
+timing.
 
 Also reported in the same line:
   * ``roofline``: the dominant kernel (the per-layer batched decode launch):
     algorithmic bytes per launch / its average duration, timed with HIP events
-    around graph replays of the 16 layer launches alone, on the replay stream,
+    around graph replays of the layer launches alone, on the replay stream,
     against 8 TB/s; ``traffic`` is the HBM bytes per launch recorded from
     FETCH_SIZE / WRITE_SIZE counters in profiles/ (null if the kernel changed);
-  * ``prefill_m1024``: prefill TFLOP/s on the Qwen3-8B-shaped M = 1024 pass
-    (36 layers, one batched launch per layer) against the 2.5 PFLOP/s dense
-    binary16 matrix-core peak;
+  * ``prefill_m1024``: prefill TFLOP/s of the Qwen3-14B-shaped pass at
+    M = 1024 (40 layers + lm_head) against the 2.5 PFLOP/s dense binary16
+    matrix-core peak, and ``prefill_m1024_qwen3_8b`` the same for the
+    Qwen3-8B-shaped pass (36 layers);
   * ``lm_head_argmax``: the lm_head alone and with greedy selection on the
-    device (one token id per step instead of 128256 logits), graph replays;
-  * ``cpu_baseline``: the CPU oracle timed on a bounded sample of the decode
-    workload on the host's cores (the only use of the oracle here);
+    device (one token id per step instead of the logits), graph replays;
+  * ``cpu_baseline``: the CPU oracle on bounded samples on the host's cores:
+    the headline pass (GB/s), the 1024x1024 GEMV at one thread, and the
+    M = 1024 pass extrapolated from sampled columns (the only use of the
+    oracle here);
+  * ``llama3.2-1b_decode_m1``: the Llama-3.2-1B-shaped decode pass (16 layers
+    + lm_head) with its own roofline, lm_head selection and launch groupings
+    (one launch per projection, the dependency groups {q,k,v}, {o},
+    {gate,up}, {down}, and per layer);
   * ``layer_sweep``: one Qwen3-14B-shaped layer at M = 1 .. 1024 (microseconds
     per batched launch, weight GB/s, TFLOP/s, kernel family);
   * ``cross_check_*``: agreement of the timed kernels with a second kernel
     family on the last layer (max |difference| / max |value|);
-  * ``launch_groupings``: the decode pass with one launch per projection, with
-    the dependency groups {q,k,v}, {o}, {gate,up}, {down}, and per layer;
   * ``other_workloads``: the 1024x1024 GEMV (latency), the Llama-3.2-3B-shaped
-    prefill chunk at M = 32 and the Qwen3-14B-shaped pass at M = 1, 4, 16
+    prefill chunk at M = 32 and the Qwen3-14B-shaped pass at M = 4, 16
     (graph replays, weight GB/s against the HBM bound).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-prefill] [--no-cpu] [--no-sweep]
-                       [--no-others]
+                       [--no-others] [--only PIECE]
 """
 from __future__ import annotations
 
@@ -345,11 +351,12 @@ def pass_figures(ps, q4k, steps, warmup, bound):
             "roofline_frac": round(frac, 4)}
 
 
-def other_workloads(q4k, dev, steps, warmup):
+def other_workloads(q4k, dev, steps, warmup, base14=None):
     """The other configurations of the workload list: the single 1024x1024 GEMV
     (0.59 MB: cache-resident and launch-bound, so its latency only), the
     Llama-3.2-3B-shaped prefill chunk at M = 32 (HBM-bound, 114 flop/B) and
-    the Qwen3-14B-shaped pass (40 layers + lm_head) at M = 1, 4, 16."""
+    the Qwen3-14B-shaped pass (40 layers + lm_head) at M = 4 and 16 (M = 1 is
+    the headline)."""
     import torch
     from q4k_inputs.workloads import WORKLOADS
     out = {}
@@ -362,36 +369,63 @@ def other_workloads(q4k, dev, steps, warmup):
     del g
     p3 = Pass(WORKLOADS["llama3.2-3b_prefill_m32"], 32, dev)
     out["llama3.2-3b_prefill_m32"] = pass_figures(p3, q4k, steps, warmup, "hbm")
+    log(f"llama3.2-3b pass at M=32: {out['llama3.2-3b_prefill_m32']}")
     del p3
     torch.cuda.empty_cache()
     wl = WORKLOADS["qwen3-14b_sweep"]
-    base = None
-    for M in (1, 4, 16):
-        ps = Pass(wl, M, dev, weights_from=base)
-        if base is None:
-            base = ps
+    for M in (4, 16):
+        ps = Pass(wl, M, dev, weights_from=base14)
         out[f"qwen3-14b_decode_m{M}"] = pass_figures(ps, q4k, steps, warmup, "hbm")
         log(f"qwen3-14b pass at M={M}: {out[f'qwen3-14b_decode_m{M}']}")
-    del base, ps
+        del ps
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(ps, budget_s=10.0):
-    """Oracle (as written, OpenMP over output columns) on a bounded sample: the
-    pass's projections in order, repeated, until about budget_s of CPU time."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(ps, budget_s=10.0, prefill_wl=None):
+    """The oracle as written (plain C, OpenMP over output columns) on the
+    host's cores, on bounded samples:
+      * value: the headline pass's projections in order, repeated until about
+        budget_s of oracle time (packed weight GB/s, the headline's unit);
+      * single_thread_gemv_1024: the 1024x1024 GEMV at one thread (us per call);
+      * prefill_m1024_extrapolated: one layer's seven projections and the
+        lm_head at M = 1024 on 128 sampled output columns each, scaled by
+        N/128 per projection and by the layer count: seconds per full pass
+        (labelled extrapolated: a full pass is ~29 TFLOP of naive loops).
+    The weight bytes are the pass's own (copied back from the device)."""
     import oracle
     import q4k_inputs as qi
-    from q4k_inputs.workloads import PROJ_ID, X_ROLE
+    from q4k_inputs.workloads import PROJ_ID, WORKLOADS, X_ROLE
     threads = len(os.sched_getaffinity(0))
     used = oracle.threads_used(threads)
+    host_w = {}
+
+    def weights(li, pi):
+        if (li, pi) not in host_w:
+            t = ps.head[0] if li < 0 else ps.layers[li][pi][0]
+            host_w[(li, pi)] = t.cpu().numpy()
+        return host_w[(li, pi)]
+
     done_bytes, t_total, calls, passes = 0, 0.0, 0, 0
-    order = [(0, p) for p in ps.wl.layer] + ([(-1, ps.wl.lm_head)] if ps.wl.lm_head else []) + \
-        [(l, p) for l in range(1, ps.wl.layers) for p in ps.wl.layer]
+    order = [(0, pi, p) for pi, p in enumerate(ps.wl.layer)]
+    if ps.wl.lm_head:
+        order.append((-1, 0, ps.wl.lm_head))
+    order += [(l, pi, p) for l in range(1, ps.wl.layers) for pi, p in enumerate(ps.wl.layer)]
     x_host = {r: v.cpu().numpy() for r, v in ps.x.items()}
     while t_total < budget_s:
-        for li, (name, N, K) in order:
-            w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, ps.wl.ident, li, PROJ_ID[name]))
+        for li, pi, (name, N, K) in order:
+            w = weights(li, pi)
             t = time.perf_counter()
             oracle.matmul(w, x_host[X_ROLE[name]], N, K, threads=used)
             t_total += time.perf_counter() - t
@@ -401,11 +435,88 @@ def cpu_baseline(ps, budget_s=10.0):
                 break
         else:
             passes += 1
-    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used,
-            "kind": "oracle",
-            "sample": f"{calls} projection calls of the same pass ({passes} full passes of "
-                      f"{len(order)}), {done_bytes / 1e6:.1f} MB packed weights at M={ps.M}, "
-                      f"{t_total:.1f} s of oracle time"}
+    out = {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{calls} projection calls of the {ps.wl.name} pass at M={ps.M} in order "
+                     f"({passes} full passes of {len(order)}), {done_bytes / 1e6:.1f} MB of packed weights, "
+                     f"{t_total:.1f} s of oracle time"}
+    host_w.clear()
+    # one thread, the 1024x1024 GEMV
+    wg = WORKLOADS["gemv_1024x1024_m1"]
+    _, N, K = wg.layer[0]
+    w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wg.ident, 0, PROJ_ID["w"]))
+    x = qi.random_x(1, K, seed=qi.tensor_seed(qi.BASE_SEED, wg.ident, 1, 1000))
+    oracle.matmul(w, x, N, K, threads=1)
+    reps, t = 0, time.perf_counter()
+    while time.perf_counter() - t < 1.0:
+        oracle.matmul(w, x, N, K, threads=1)
+        reps += 1
+    out["single_thread_gemv_1024"] = {"us_per_call": round((time.perf_counter() - t) / reps * 1e6, 1),
+                                      "calls": reps, "threads": 1}
+    oracle.threads_used(threads)
+    # M = 1024 on the largest workload, extrapolated from sampled columns
+    if prefill_wl is not None:
+        M, ncols = 1024, 128
+        rng = np.random.default_rng(1)
+        xs = {}
+        total_s, sample_s, projs = 0.0, 0.0, list(prefill_wl.layer) + ([prefill_wl.lm_head] if prefill_wl.lm_head else [])
+        for i, (name, N, K) in enumerate(projs):
+            r = X_ROLE[name]
+            if r not in xs:
+                xs[r] = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, prefill_wl.ident, M, 1000 + r))
+            li = -1 if name == "lm_head" else 0
+            w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, prefill_wl.ident, li, PROJ_ID[name]))
+            cols = np.sort(rng.choice(N, ncols, replace=False))
+            t = time.perf_counter()
+            oracle.matmul_cols(w, xs[r], N, K, cols, threads=used)
+            dt = time.perf_counter() - t
+            sample_s += dt
+            total_s += dt * N / ncols * (1 if name == "lm_head" else prefill_wl.layers)
+        flops = 2 * M * prefill_wl.weights()
+        out["prefill_m1024_extrapolated"] = {
+            "workload": prefill_wl.name, "M": M, "seconds_per_pass": round(total_s, 1),
+            "TFLOPs": round(flops / total_s / 1e12, 5), "kind": "extrapolated",
+            "sample": f"{ncols} sampled output columns of each of the {len(projs)} projections of one layer "
+                      f"and the lm_head at M={M} ({sample_s:.1f} s), scaled by N/{ncols} and by "
+                      f"{prefill_wl.layers} layers"}
+    return out
+
+
+def layer_roofline(ps, ms_layer, kernel, profile):
+    """Roofline entry of the per-layer batched launch: its algorithmic bytes
+    (packed W, x read once per distinct activation, y written) per launch over
+    its average duration, against the HBM peak."""
+    achieved = ps.layer_bytes / (ms_layer * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(profile),
+            "kernel": kernel, "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)}
+
+
+def prefill_pass(q4k, dev, wl, steps, weights_from=None):
+    """A whole M = 1024 pass (one batched call per layer, then the lm_head),
+    eager calls: TFLOP/s, and the roofline of the per-layer launch (x
+    conversion + GEMM) against the binary16 matrix-core peak."""
+    t = time.time()
+    pp = Pass(wl, 1024, dev, weights_from=weights_from)
+    import torch
+    torch.cuda.synchronize()
+    log(f"prefill inputs for {wl.name} ready ({pp.weight_bytes / 1e6:.1f} MB) in {time.time() - t:.1f} s")
+    ms_p, ms_pl = time_pass(pp, q4k, steps, 1, graph=False)
+    xcheck_p = cross_check(pp, q4k)
+    tflops = pp.flops / (ms_p * 1e-3) / 1e12
+    ach = pp.layer_flops / (ms_pl * 1e-3) / 1e12
+    res = {"workload": wl.name, "M": 1024, "layers": wl.layers, "lm_head": wl.lm_head is not None,
+           "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_p, 4), "steps": steps,
+           "frac_of_peak": round(tflops / FP16_PEAK_TFLOPS, 4),
+           "dtype": "binary16 operands (x scaled per row, w rounded once), fp32 accumulate",
+           "cross_check_vs_decode_family": xcheck_p,
+           "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4),
+                        "kernel": "per-layer batched launch (convert_x_kernel + prefill_kernel)",
+                        "flops_per_launch": pp.layer_flops, "avg_launch_us": round(ms_pl * 1e3, 2)}}
+    log(f"prefill {wl.name}: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
+        f"-> {ach:.1f} TFLOP/s; cross-check {xcheck_p:.2e}")
+    return res, pp
 
 
 def main():
@@ -418,7 +529,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-others", action="store_true",
-                    help="skip the launch groupings and the other workloads of the list")
+                    help="skip the Llama-3.2-1B pass, the launch groupings and the other workloads of the list")
+    ap.add_argument("--only", default=None,
+                    help="run one piece only, for profiling: qwen3-14b_m1, llama1b_m1, prefill_m32, "
+                         "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy three times (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -445,8 +559,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {src.numel() * 4} bytes")
         del src, dst
+    if args.only:
+        return run_only(args, q4k, dev)
 
-    wl = WORKLOADS["llama3.2-1b_decode_m1"]
+    # Headline: the Qwen3-14B-shaped pass at M = 1, the largest M = 1 workload.
+    wl = WORKLOADS["qwen3-14b_sweep"]
     t = time.time()
     ps = Pass(wl, 1, dev)
     torch.cuda.synchronize()
@@ -454,60 +571,58 @@ def main():
     ms_step, ms_layer = time_pass(ps, q4k, args.steps, args.warmup)
     xcheck = cross_check(ps, q4k)
     value = ps.weight_bytes / (ms_step * 1e-3) / 1e9
-    achieved = ps.layer_bytes / (ms_layer * 1e-3) / 1e9
-    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.1f} GB/s; layer launch {ms_layer * 1e3:.2f} us "
-        f"-> {achieved:.1f} GB/s; cross-check {xcheck:.2e}")
+    log(f"decode {wl.name} M=1: {ms_step * 1e3:.1f} us/step, {value:.1f} GB/s; layer launch "
+        f"{ms_layer * 1e3:.2f} us; cross-check {xcheck:.2e}")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "x as hi+lo binary16 pair (scaled per super-block) times exact 4-bit quants on the "
+                 "matrix cores, fp32 scales and accumulation",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": 1, "layers": wl.layers,
+        "config": {"workload": "qwen3-14b_decode_m1", "M": 1, "layers": wl.layers,
+                   "projections": "q,k,v,o,gate,up,down per layer + lm_head 151936x5120, all Q4_K",
                    "launches": "one batched call per layer (q,k,v,o,gate,up,down) + lm_head, "
                                "replayed as one HIP graph per step",
                    "weight_bytes": ps.weight_bytes, "cross_check_vs_fp32_gemv": xcheck},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("decode_wide_llama1b_layer_m1"),
-                     "kernel": "decode_wide_kernel (per-layer batched launch)",
-                     "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)},
+        "roofline": layer_roofline(ps, ms_layer, "decode_wide_kernel<8> (per-layer batched launch)",
+                                   "decode_wide_qwen3_14b_layer_m1"),
     }
     out["lm_head_argmax"] = time_head_argmax(ps, q4k, args.steps, args.warmup)
     log(f"lm_head argmax: {out['lm_head_argmax']}")
-    if not args.no_others:
-        out["launch_groupings"] = launch_groupings(ps, q4k, args.steps, args.warmup)
-        log(f"launch groupings: {out['launch_groupings']}")
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(ps)
+        out["cpu_baseline"] = cpu_baseline(ps, prefill_wl=wl if not args.no_prefill else None)
         log(f"cpu baseline: {out['cpu_baseline']}")
-    del ps
-    torch.cuda.empty_cache()
 
     if not args.no_prefill:
-        wl3 = WORKLOADS["qwen3-8b_prefill_m1024"]
-        t = time.time()
-        pp = Pass(wl3, 1024, dev)
-        torch.cuda.synchronize()
-        log(f"prefill inputs ready ({pp.weight_bytes / 1e6:.1f} MB) in {time.time() - t:.1f} s")
-        ms_p, ms_pl = time_pass(pp, q4k, args.prefill_steps, 1, graph=False)
-        xcheck_p = cross_check(pp, q4k)
-        tflops = pp.flops / (ms_p * 1e-3) / 1e12
-        ach = pp.layer_flops / (ms_pl * 1e-3) / 1e12
-        out["prefill_m1024"] = {
-            "workload": wl3.name, "value": round(tflops, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms_p, 4), "steps": args.prefill_steps, "dtype": "f16 operands, f32 accumulate",
-            "cross_check_vs_decode_family": xcheck_p,
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4),
-                         "traffic": recorded_traffic("prefill_qwen3_8b_layer_m1024"),
-                         "kernel": "prefill per-layer batched launch (x conversion + prefill_kernel)",
-                         "avg_launch_us": round(ms_pl * 1e3, 2)}}
-        log(f"prefill: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
-            f"-> {ach:.1f} TFLOP/s; cross-check {xcheck_p:.2e}")
+        out["prefill_m1024"], pp = prefill_pass(q4k, dev, wl, args.prefill_steps, weights_from=ps)
+        del pp
+        torch.cuda.empty_cache()
     if not args.no_others:
-        t = time.time()
-        out["other_workloads"] = other_workloads(q4k, dev, min(args.steps, 10), args.warmup)
-        log(f"other workloads ({time.time() - t:.1f} s): {out['other_workloads']}")
+        out["other_workloads"] = other_workloads(q4k, dev, min(args.steps, 10), args.warmup, base14=ps)
+    del ps
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        res, pp = prefill_pass(q4k, dev, WORKLOADS["qwen3-8b_prefill_m1024"], args.prefill_steps)
+        res["roofline"]["traffic"] = recorded_traffic("prefill_qwen3_8b_layer_m1024")
+        out["prefill_m1024_qwen3_8b"] = res
+        del pp
+        torch.cuda.empty_cache()
+    if not args.no_others:
+        wl1 = WORKLOADS["llama3.2-1b_decode_m1"]
+        p1 = Pass(wl1, 1, dev)
+        ms1, ml1 = time_pass(p1, q4k, args.steps, args.warmup)
+        out["llama3.2-1b_decode_m1"] = {
+            "workload": wl1.name, "M": 1, "layers": wl1.layers, "us_per_step": round(ms1 * 1e3, 2),
+            "weight_GBps": round(p1.weight_bytes / (ms1 * 1e-3) / 1e9, 1),
+            "roofline": layer_roofline(p1, ml1, "decode_wide_kernel<16> (per-layer batched launch)",
+                                       "decode_wide_llama1b_layer_m1"),
+            "cross_check_vs_fp32_gemv": cross_check(p1, q4k),
+            "lm_head_argmax": time_head_argmax(p1, q4k, args.steps, args.warmup),
+            "launch_groupings": launch_groupings(p1, q4k, args.steps, args.warmup)}
+        log(f"llama3.2-1b decode: {out['llama3.2-1b_decode_m1']}")
+        del p1
+        torch.cuda.empty_cache()
     if not args.no_sweep:
         t = time.time()
         out["layer_sweep"] = layer_sweep(q4k, dev)
@@ -515,6 +630,38 @@ def main():
             ", ".join(f"M={p['M']} {p['us']} us" for p in out["layer_sweep"]["points"]))
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
+
+
+def run_only(args, q4k, dev):
+    """One piece of the benchmark on its own (a short program to profile)."""
+    import torch
+    from q4k_inputs.workloads import WORKLOADS
+    wl14 = WORKLOADS["qwen3-14b_sweep"]
+    name = args.only
+    res = {}
+    if name in ("qwen3-14b_m1", "qwen3-14b_m4", "qwen3-14b_m16"):
+        ps = Pass(wl14, int(name.split("_m")[1]), dev)
+        ms, ml = time_pass(ps, q4k, args.steps, args.warmup)
+        res = {"us_per_step": ms * 1e3, "us_per_layer_launch": ml * 1e3}
+    elif name == "llama1b_m1":
+        ps = Pass(WORKLOADS["llama3.2-1b_decode_m1"], 1, dev)
+        ms, ml = time_pass(ps, q4k, args.steps, args.warmup)
+        res = {"us_per_step": ms * 1e3, "us_per_layer_launch": ml * 1e3}
+    elif name == "prefill_m32":
+        ps = Pass(WORKLOADS["llama3.2-3b_prefill_m32"], 32, dev)
+        ms, ml = time_pass(ps, q4k, args.steps, args.warmup)
+        res = {"us_per_step": ms * 1e3, "us_per_layer_launch": ml * 1e3}
+    elif name in ("qwen3-14b_m1024", "qwen3-8b_m1024"):
+        wl = wl14 if name.startswith("qwen3-14b") else WORKLOADS["qwen3-8b_prefill_m1024"]
+        r, _ = prefill_pass(q4k, dev, wl, args.prefill_steps)
+        res = {"ms_per_step": r["ms_per_step"], "TFLOPs": r["value"]}
+    elif name == "argmax":
+        ps = Pass(wl14, 1, dev)
+        res = time_head_argmax(ps, q4k, args.steps, args.warmup)
+    else:
+        raise SystemExit(f"unknown --only {name}")
+    torch.cuda.synchronize()
+    print(json.dumps({"only": name, **res}), flush=True)
 
 
 if __name__ == "__main__":
