@@ -657,7 +657,10 @@ def run_only(args, q4k, dev):
         res = {"ms_per_step": r["ms_per_step"], "TFLOPs": r["value"]}
     elif name == "argmax":
         ps = Pass(wl14, 1, dev)
-        res = time_head_argmax(ps, q4k, args.steps, args.warmup)
+        res = {"qwen3-14b": time_head_argmax(ps, q4k, args.steps, args.warmup)}
+        del ps
+        ps = Pass(WORKLOADS["llama3.2-1b_decode_m1"], 1, dev)
+        res["llama3.2-1b"] = time_head_argmax(ps, q4k, args.steps, args.warmup)
     else:
         raise SystemExit(f"unknown --only {name}")
     torch.cuda.synchronize()

@@ -237,6 +237,28 @@ int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K,
         return Q4K_ERR_ALIGN;
     const int dev_rc = q4k::check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
+    if (M == 1) {
+        // One token (greedy decoding): the selection is the product kernel's
+        // own epilogue; only one (value, row) pair per 32-row tile is written.
+        float *ws = nullptr;
+        hipError_t err = q4k::workspace(stream, q4k::wide_argmax_pairs(N) * 2 * sizeof(float), &ws, 1);
+        if (err != hipSuccess) return Q4K_ERR_ALLOC;
+        q4k::Batch b;
+        b.count = 1;
+        b.M = 1;
+        q4k::DevProblem &d = b.p[0];
+        d.w = static_cast<const uint8_t *>(w_packed);
+        d.x = x;
+        d.y = nullptr;
+        d.part = nullptr;
+        d.N = N;
+        d.K = K;
+        d.tile_begin = 0;
+        d.tiles = 0;
+        d.splits = 1;
+        err = q4k::launch_wide_argmax(b, ws, index, value, stream);
+        return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+    }
     // Logits, then the (value, index) partials, in workspace slot 1.
     const size_t logits = (static_cast<size_t>(M) * N + 3) & ~static_cast<size_t>(3);
     float *ws = nullptr;

@@ -44,6 +44,9 @@
 //     two waves (9..16), sharing one staged copy of the activations of all
 //     tokens, pass by pass over K.  In both, the waves of a tile add their
 //     partial sums through LDS (no second kernel).
+#include <limits.h>
+#include <math.h>
+
 #include "q4k_internal.h"
 
 namespace q4k {
@@ -614,9 +617,23 @@ __host__ __device__ inline int wide_wpt(int KB, int waves) {
     return w;
 }
 
+// (value, index) pairs of the greedy selection: a pair beats another if its
+// value is larger, or equal with a lower index, so any order of reduction
+// gives the lowest index among equal maxima; NaN compares false and never
+// wins.
+__device__ __forceinline__ void take_better(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
 // WAVES = 16 (one workgroup per CU: launches of about two rounds at most) or
-// 4 (several workgroups per CU: longer launches).
-template <int WAVES>
+// 4 (several workgroups per CU: longer launches).  ARGMAX: instead of y, each
+// tile writes the best (value, row) pair of its 32 rows to P.part (float2
+// per tile, tiles numbered from the problem's first), for the greedy
+// selection of an lm_head; the logits never reach memory.
+template <int WAVES, bool ARGMAX = false>
 __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     // Per wave: a weight slot, and the staged activations of a pair of
     // super-blocks with their sub-block sums and scale factors.
@@ -698,11 +715,78 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
 
     red[wave * 64 + lane] = acc[0];
     __syncthreads();
-    if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
-        float v = 0.f;
-        for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
-        const int n = n0 + col;
-        if (n < N) P.y[n] = v;
+    if constexpr (ARGMAX) {
+        if (active && kw == 0) {  // one wave per tile; lane l < 32 owns row n0 + l
+            float v = -INFINITY;
+            int i = INT_MAX;
+            const int n = n0 + col;
+            if (half == 0 && n < N) {
+                float s = 0.f;
+                for (int j = 0; j < wpt; ++j) s += red[(tl * wpt + j) * 64 + lane];
+                take_better(v, i, s, n);
+            }
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) {
+                const float v2 = __shfl_xor(v, o);
+                const int i2 = __shfl_xor(i, o);
+                take_better(v, i, v2, i2);
+            }
+            if (lane == 0)
+                reinterpret_cast<float2 *>(P.part)[(g - P.tile_begin) * T + tl] = make_float2(v, __int_as_float(i));
+        }
+        return;
+    } else {
+        if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
+            float v = 0.f;
+            for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
+            const int n = n0 + col;
+            if (n < N) P.y[n] = v;
+        }
+    }
+}
+
+// Greedy selection from the tile pairs of decode_wide_kernel<., true>: one
+// workgroup, index[0] = the best pair's row, value[0] its value (an all-NaN
+// row gives index 0 and value NaN).
+__global__ __launch_bounds__(1024) void argmax_tile_pairs(const float2 *pairs, int count, int *index, float *value) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
+    float v = -INFINITY;
+    int i = INT_MAX;
+    // Eight pairs per thread requested together (one round trip for up to
+    // 8192 tiles), then compared; longer lists continue in a loop.
+    constexpr int kPer = 8;
+    float2 p[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int c = static_cast<int>(threadIdx.x) + 1024 * j;
+        p[j] = c < count ? pairs[c] : make_float2(-INFINITY, __int_as_float(INT_MAX));
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) take_better(v, i, p[j].x, __float_as_int(p[j].y));
+    for (int c = static_cast<int>(threadIdx.x) + 1024 * kPer; c < count; c += 1024) {
+        const float2 q = pairs[c];
+        take_better(v, i, q.x, __float_as_int(q.y));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(v, o);
+        const int i2 = __shfl_xor(i, o);
+        take_better(v, i, v2, i2);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        sv[threadIdx.x >> 6] = v;
+        si[threadIdx.x >> 6] = i;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 16; ++w) take_better(v, i, sv[w], si[w]);
+        if (i == INT_MAX) {
+            i = 0;
+            v = NAN;
+        }
+        index[0] = i;
+        if (value) value[0] = v;
     }
 }
 
@@ -737,7 +821,7 @@ int wide_groups(const Batch &b, int waves) {
     return groups;
 }
 
-template <int WAVES>
+template <int WAVES, bool ARGMAX = false>
 hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
     Batch sb;
     sb.count = b.count;
@@ -754,11 +838,42 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
         groups += sb.p[i].tiles;
     }
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_wide_kernel<WAVES>, dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
+    hipLaunchKernelGGL((decode_wide_kernel<WAVES, ARGMAX>), dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
     return hipGetLastError();
 }
 
+// The waves per workgroup of an M = 1 launch (see launch_decode_mma).
+int wide_waves(const Batch &b) {
+    const int g16 = wide_groups(b, kWideWaves);
+    if (g16 <= kWideMaxGroups) {
+        bool short_rows = g16 < kCus;
+        for (int i = 0; i < b.count; ++i)
+            if (wide_wpt(b.p[i].K / kBlockWeights, kWideWaves) > 4) short_rows = false;
+        return short_rows ? 4 : kWideWaves;
+    }
+    int max_kb = 0;
+    for (int i = 0; i < b.count; ++i) max_kb = max(max_kb, b.p[i].K / kBlockWeights);
+    return max_kb > 8 ? 8 : 4;
+}
+
 }  // namespace
+
+// One pair per 32-row tile with rows (tiles past N write none).
+size_t wide_argmax_pairs(int N) { return static_cast<size_t>((N + kCols - 1) / kCols); }
+
+hipError_t launch_wide_argmax(Batch &b, float *pairs, int *index, float *value, hipStream_t stream) {
+    // one problem, one token: b.p[0]; pairs holds wide_argmax_pairs(N) float2
+    b.p[0].part = pairs;
+    const int order[1] = {0};
+    const int waves = wide_waves(b);
+    const hipError_t err = waves == 4   ? launch_wide<4, true>(b, order, stream)
+                           : waves == 8 ? launch_wide<8, true>(b, order, stream)
+                                        : launch_wide<kWideWaves, true>(b, order, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(argmax_tile_pairs, dim3(1), dim3(1024), 0, stream, reinterpret_cast<const float2 *>(pairs),
+                       static_cast<int>(wide_argmax_pairs(b.p[0].N)), index, value);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
     // Workgroups in order of decreasing K, so the longest ones start first.
@@ -774,27 +889,20 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         // Sixteen waves per workgroup (one per CU) when the launch fits in
         // about two rounds; otherwise four-wave workgroups, several per CU,
         // which keep every CU busy across rounds whatever the row length.
-        const int g16 = wide_groups(b, kWideWaves);
-        if (g16 <= kWideMaxGroups) {
-            // Less than one round of sixteen-wave workgroups and no row longer
-            // than eight super-blocks: four-wave workgroups of one tile each
-            // spread the launch over four times as many CUs (a lone
-            // projection, or a group such as {q, k, v}).
-            bool short_rows = g16 < kCus;
-            for (int i = 0; i < b.count; ++i)
-                if (wide_wpt(b.p[i].K / kBlockWeights, kWideWaves) > 4) short_rows = false;
-            if (short_rows) return launch_wide<4>(b, order, stream);
-            return launch_wide<kWideWaves>(b, order, stream);
+        //   Less than one round of sixteen-wave workgroups and no row longer
+        // than eight super-blocks: four-wave workgroups of one tile each
+        // spread the launch over four times as many CUs (a lone projection,
+        // or a group such as {q, k, v}).
+        //   Several rounds: four-wave workgroups (two super-blocks per wave)
+        // for rows of up to eight super-blocks, eight-wave ones for longer
+        // rows, so that fewer pairs run one after another in each wave
+        // (Qwen3-14B-shaped layer 42 -> 40.7 us; the Llama-3.2-1B lm_head
+        // prefers four, 29.6 against 32.8 us).
+        switch (wide_waves(b)) {
+        case 4: return launch_wide<4>(b, order, stream);
+        case 8: return launch_wide<8>(b, order, stream);
+        default: return launch_wide<kWideWaves>(b, order, stream);
         }
-        // Several rounds: four-wave workgroups (two super-blocks per wave) for
-        // rows of up to eight super-blocks, eight-wave ones for longer rows, so
-        // that fewer pairs run one after another in each wave (Qwen3-14B-shaped
-        // layer 42 -> 40.7 us; the Llama-3.2-1B lm_head prefers four, 29.6
-        // against 32.8 us).
-        int max_kb = 0;
-        for (int i = 0; i < b.count; ++i) max_kb = max(max_kb, b.p[i].K / kBlockWeights);
-        if (max_kb > 8) return launch_wide<8>(b, order, stream);
-        return launch_wide<4>(b, order, stream);
     }
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
     // caller forces this path) are done 16 at a time.

@@ -97,6 +97,13 @@ hipError_t workspace(hipStream_t stream, size_t bytes, float **scratch, int slot
 // per (device, kernel); thread-safe.  Returns the first call's result.
 hipError_t allow_dynamic_lds(const void *kernel, int bytes);
 
+// Greedy selection fused into the one-token product (decode_wide_kernel's
+// epilogue): every 32-row tile writes its best (value, row) pair, then one
+// small kernel picks the best pair.  b holds one problem with M = 1; pairs
+// has room for wide_argmax_pairs(N) float2.
+size_t wide_argmax_pairs(int N);
+hipError_t launch_wide_argmax(Batch &b, float *pairs, int *index, float *value, hipStream_t stream);
+
 // Row-wise argmax of y [M, N] (lowest index among equal maxima; NaN never
 // wins, an all-NaN row gives index 0 and value NaN).  part holds one
 // (value, index) pair per (row, chunk): argmax_partials(M, N) pairs.

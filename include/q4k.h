@@ -120,10 +120,14 @@ int q4k_matmul_batched_noalloc(const q4k_problem *problems, int count, int M, hi
  *     index[m] = the lowest n with y[m, n] == max over n of y[m, n],
  *     value[m] = that maximum,
  * where y = x . dequant(W)^T is computed exactly as q4k_matmul computes it
- * but kept in the library workspace and never returned.  This is the lm_head
- * of greedy decoding (the host-greedy lm_head of the rlx-llama32 crate page,
+ * (the same values, bit for bit) and never returned.  This is the lm_head of
+ * greedy decoding (the host-greedy lm_head of the rlx-llama32 crate page,
  * "Decode") with the selection moved to the device, so that a decode step
- * reads back one token id instead of N logits.
+ * reads back one token id instead of N logits.  For M == 1 the selection is
+ * the product kernel's own epilogue: each 32-row tile keeps its best
+ * (value, row) pair and one small kernel picks the best pair, so the logits
+ * never reach memory.  For M > 1 the logits go to the library workspace and
+ * two small kernels reduce them.
  *   w_packed, x: as for q4k_matmul.  index: DEVICE int32 [M].  value: DEVICE
  *   float32 [M], or NULL.  NaN logits never win; a row of only NaN logits
  *   gives index 0 and value NaN.

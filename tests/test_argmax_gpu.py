@@ -50,8 +50,12 @@ def _check_against_oracle(w, x, N, K, idx, tol):
     return decided
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 7, 512), (1, 5000, 2048), (3, 4097, 1024),
-                                   (16, 9000, 768), (20, 3000, 512), (1, 128256, 2048)])
+# One token runs the selection in the product kernel's epilogue (one pair per
+# 32-row tile): (1, 5000, 2048) on four-wave workgroups of several tiles,
+# (1, 2000, 8192) on sixteen-wave ones, (1, 128256, 2048) four-wave over
+# several rounds, the Qwen3-14B lm_head below on eight-wave ones.
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 7, 512), (1, 33, 256), (1, 5000, 2048), (1, 2000, 8192),
+                                   (3, 4097, 1024), (16, 9000, 768), (20, 3000, 512), (1, 128256, 2048)])
 def test_argmax_is_the_products_and_the_oracles(M, N, K):
     w, x = _inputs(M, N, K, 1)
     wd, xd = to_dev(w), to_dev(x)
@@ -158,3 +162,40 @@ def test_argmax_rejects_host_and_strided_outputs():
     torch.cuda.synchronize()
     y = q4k.matmul(w, x).cpu().numpy()
     assert index.cpu().numpy().tolist() == np.argmax(y, axis=1).tolist()
+
+
+def test_one_token_nan_and_graph_replays():
+    """The fused one-token path: a NaN activation makes every logit NaN (index 0,
+    value NaN); a clean row picks the product's first maximum, also replayed
+    from a HIP graph with eager work in between."""
+    import torch
+    N, K = 4000, 1024
+    w, x = _inputs(1, N, K, 5)
+    wd = to_dev(w)
+    xn = x.copy()
+    xn[0, 300] = np.nan
+    idx, val = q4k.matmul_argmax(wd, to_dev(xn))
+    torch.cuda.synchronize()
+    assert int(idx[0]) == 0 and np.isnan(float(val[0]))
+    xd = to_dev(x)
+    idx, val = q4k.matmul_argmax(wd, xd)
+    _check_against_product(wd, xd, idx, val)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gi = torch.empty(1, dtype=torch.int32, device=device())
+    gv = torch.empty(1, dtype=torch.float32, device=device())
+    with torch.cuda.stream(side):
+        q4k.matmul_argmax(wd, xd, index=gi, value=gv, stream=side)
+        side.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            q4k.matmul_argmax(wd, xd, index=gi, value=gv, stream=side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        gi.fill_(-5)
+        gv.fill_(0.0)
+        q4k.matmul_argmax(wd, to_dev(xn))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gi, idx) and torch.equal(gv, val)
