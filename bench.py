@@ -31,6 +31,9 @@ Also reported in the same line:
     + lm_head) with its own roofline, lm_head selection and launch groupings
     (one launch per projection, the dependency groups {q,k,v}, {o},
     {gate,up}, {down}, and per layer);
+  * ``swiglu_gate_up``: the Qwen3-14B-shaped gate/up pair with the SwiGLU
+    epilogue in the product kernels, against the two products alone, at
+    M = 1 and 1024;
   * ``layer_sweep``: one Qwen3-14B-shaped layer at M = 1 .. 1024 (microseconds
     per batched launch, weight GB/s, TFLOP/s, kernel family);
   * ``cross_check_*``: agreement of the timed kernels with a second kernel
@@ -382,6 +385,57 @@ def other_workloads(q4k, dev, steps, warmup, base14=None):
     return out
 
 
+def swiglu_figures(q4k, dev, steps, warmup):
+    """The gate/up pair of one Qwen3-14B-shaped layer (17408 x 5120 each) with the
+    SwiGLU epilogue (q4k_matmul_swiglu: silu(g) * u written by the product
+    kernels) against the same two products alone (one batched call writing g
+    and u), at M = 1 (graph replays) and M = 1024 (eager calls)."""
+    import torch
+    import q4k_inputs as qi
+    from q4k_inputs.workloads import PROJ_ID, WORKLOADS, X_ROLE
+    wl = WORKLOADS["qwen3-14b_sweep"]
+    (_, N, K), = [p for p in wl.layer if p[0] == "gate"]
+    wg = torch.from_numpy(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 0, PROJ_ID["gate"]))).to(dev)
+    wu = torch.from_numpy(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 0, PROJ_ID["up"]))).to(dev)
+    out = {"shape": [N, K], "weight_bytes": 2 * N * K // 256 * 144}
+    for M in (1, 1024):
+        x = torch.from_numpy(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, M, 1000 + X_ROLE["gate"]))).to(dev)
+        o = torch.empty((M, N), dtype=torch.float32, device=dev)
+        g = torch.empty_like(o)
+        u = torch.empty_like(o)
+        prods = q4k.prepare_batched([(wg, x, g), (wu, x, u)])
+        fused = lambda st: q4k.matmul_swiglu(wg, wu, x, out=o, stream=st)
+        if M == 1:
+            ms_f = _time_replays(_capture(fused), steps, warmup)
+            ms_p = _time_replays(_capture(lambda st: prods(st)), steps, warmup)
+        else:
+            def eager(fn, reps=max(3, steps // 4)):
+                for _ in range(2):
+                    fn(None)
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(reps):
+                    fn(None)
+                t1.record()
+                torch.cuda.synchronize()
+                return t0.elapsed_time(t1) / reps
+            ms_f, ms_p = eager(fused), eager(lambda st: prods(st))
+        torch.cuda.synchronize()
+        ref = g * torch.sigmoid(g) * u
+        dev_rel = float(((o - ref).abs().max() / ref.abs().max()).item())
+        rec = {"us_swiglu": round(ms_f * 1e3, 2), "us_products_only": round(ms_p * 1e3, 2),
+               "max_rel_diff_vs_products": dev_rel}
+        if M == 1:
+            rec["weight_GBps"] = round(out["weight_bytes"] / (ms_f * 1e-3) / 1e9, 1)
+        else:
+            rec["TFLOPs"] = round(2 * M * 2 * N * K / (ms_f * 1e-3) / 1e12, 1)
+        out[f"M{M}"] = rec
+        del x, o, g, u, prods
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -532,7 +586,7 @@ def main():
                     help="skip the Llama-3.2-1B pass, the launch groupings and the other workloads of the list")
     ap.add_argument("--only", default=None,
                     help="run one piece only, for profiling: qwen3-14b_m1, llama1b_m1, prefill_m32, "
-                         "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax")
+                         "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax, swiglu")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy three times (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -609,6 +663,9 @@ def main():
         del pp
         torch.cuda.empty_cache()
     if not args.no_others:
+        out["swiglu_gate_up"] = swiglu_figures(q4k, dev, args.steps, args.warmup)
+        log(f"swiglu: {out['swiglu_gate_up']}")
+        torch.cuda.empty_cache()
         wl1 = WORKLOADS["llama3.2-1b_decode_m1"]
         p1 = Pass(wl1, 1, dev)
         ms1, ml1 = time_pass(p1, q4k, args.steps, args.warmup)
@@ -655,6 +712,8 @@ def run_only(args, q4k, dev):
         wl = wl14 if name.startswith("qwen3-14b") else WORKLOADS["qwen3-8b_prefill_m1024"]
         r, _ = prefill_pass(q4k, dev, wl, args.prefill_steps)
         res = {"ms_per_step": r["ms_per_step"], "TFLOPs": r["value"]}
+    elif name == "swiglu":
+        res = swiglu_figures(q4k, dev, args.steps, args.warmup)
     elif name == "argmax":
         ps = Pass(wl14, 1, dev)
         res = {"qwen3-14b": time_head_argmax(ps, q4k, args.steps, args.warmup)}

@@ -26,6 +26,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 ok, -1 bad
 
+}  // namespace
+
 int check_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q4K_ERR_DEVICE;
@@ -40,6 +42,8 @@ int check_device() {
     }
     return st == 1 ? Q4K_OK : Q4K_ERR_DEVICE;
 }
+
+namespace {
 
 int check_problem(const void *w, const float *x, const float *y, int M, int N, int K) {
     if (M < 0 || N < 0 || K < 0) return Q4K_ERR_BAD_DIM;
@@ -169,6 +173,8 @@ int run(const q4k_problem *problems, int count, int M, int path, hipStream_t str
         if (rc != Q4K_OK) return rc;
         if (M == 0 || q.N == 0) continue;  // nothing to compute for this one
         DevProblem &d = b.p[b.count++];
+        d.w2 = nullptr;
+        d.n_out = q.N;
         d.w = static_cast<const uint8_t *>(q.w_packed);
         d.x = q.x;
         d.y = q.y;
@@ -247,6 +253,8 @@ int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K,
         b.count = 1;
         b.M = 1;
         q4k::DevProblem &d = b.p[0];
+        d.w2 = nullptr;
+        d.n_out = N;
         d.w = static_cast<const uint8_t *>(w_packed);
         d.x = x;
         d.y = nullptr;

@@ -633,8 +633,13 @@ __device__ __forceinline__ void take_better(float &v, int &i, float v2, int i2) 
 // tile writes the best (value, row) pair of its 32 rows to P.part (float2
 // per tile, tiles numbered from the problem's first), for the greedy
 // selection of an lm_head; the logits never reach memory.
-template <int WAVES, bool ARGMAX = false>
+//   PAIR: the batch is one gate/up pair (w2 set, virtual rows, see
+// DevProblem): each piece of a tile row is read from the gate or the up
+// matrix, and lane l < 16 of a tile, which then holds gate row n0/2 + l while
+// lane l + 16 holds the up row, writes y[n0/2 + l] = silu(g) * u.
+template <int WAVES, bool ARGMAX = false, bool PAIR = false>
 __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
+    static_assert(!(ARGMAX && PAIR), "selection over a gate/up pair is not a product of the library");
     // Per wave: a weight slot, and the staged activations of a pair of
     // super-blocks with their sub-block sums and scale factors.
     __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kStage];
@@ -668,13 +673,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * KB * kBlockBytes;
     const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
     uint32_t goff[5];
+    const uint8_t *pb[5];  // PAIR: each piece's own row pointer (gate or up matrix)
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
         const int f = min(lane + 64 * j, kStageChunks - 1);
-        goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
+        if constexpr (PAIR) {
+            const int v = (active ? n0 : 0) + min(f / 9, nr);
+            pb[j] = (pair_is_up(v) ? P.w2 : P.w) + static_cast<size_t>(pair_row(v, P.n_out)) * row_bytes + 16u * (f % 9);
+        } else {
+            goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
+        }
     }
     const bool has5 = lane + 256 < kStageChunks;
     auto ld = [&](int kb, int j) -> u32x4 {
+        if constexpr (PAIR) return *reinterpret_cast<const u32x4 *>(pb[j] + static_cast<uint32_t>(kb) * kBlockBytes);
         return *reinterpret_cast<const u32x4 *>(W + (static_cast<uint32_t>(kb) * kBlockBytes + goff[j]));
     };
     auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, u32x4 v4) {
@@ -735,6 +747,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
                 reinterpret_cast<float2 *>(P.part)[(g - P.tile_begin) * T + tl] = make_float2(v, __int_as_float(i));
         }
         return;
+    } else if constexpr (PAIR) {
+        if (active && kw == 0) {  // the whole wave: the shuffle needs every lane
+            float v = 0.f;
+            for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
+            const float u = __shfl_xor(v, 16);
+            const int n = (n0 >> 1) + (col & 15);
+            if (half == 0 && (col & 16) == 0 && n < P.n_out) P.y[n] = swiglu(v, u);
+        }
     } else {
         if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
             float v = 0.f;
@@ -821,7 +841,7 @@ int wide_groups(const Batch &b, int waves) {
     return groups;
 }
 
-template <int WAVES, bool ARGMAX = false>
+template <int WAVES, bool ARGMAX = false, bool PAIR = false>
 hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
     Batch sb;
     sb.count = b.count;
@@ -838,7 +858,7 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
         groups += sb.p[i].tiles;
     }
     if (groups == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_wide_kernel<WAVES, ARGMAX>), dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
+    hipLaunchKernelGGL((decode_wide_kernel<WAVES, ARGMAX, PAIR>), dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
     return hipGetLastError();
 }
 
@@ -898,6 +918,13 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         // rows, so that fewer pairs run one after another in each wave
         // (Qwen3-14B-shaped layer 42 -> 40.7 us; the Llama-3.2-1B lm_head
         // prefers four, 29.6 against 32.8 us).
+        if (b.count == 1 && b.p[0].w2) {  // a gate/up pair: the SwiGLU epilogue
+            switch (wide_waves(b)) {
+            case 4: return launch_wide<4, false, true>(b, order, stream);
+            case 8: return launch_wide<8, false, true>(b, order, stream);
+            default: return launch_wide<kWideWaves, false, true>(b, order, stream);
+            }
+        }
         switch (wide_waves(b)) {
         case 4: return launch_wide<4>(b, order, stream);
         case 8: return launch_wide<8>(b, order, stream);

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <math.h>
 
 namespace q4k {
 
@@ -19,8 +20,17 @@ constexpr int kMaxBatch = 32;
 // part points into the library workspace: the partial sums [splits][M][N]
 // when the problem's K is split across `splits` workgroups, or (small-M
 // matrix-core kernel) the staged activations of its x; otherwise unused.
+//
+// Gate/up pairs (w2 != null, the SwiGLU epilogue): w holds the gate rows and
+// w2 the up rows, n_out of each.  The kernels then run over N = 32 *
+// ceil(n_out / 16) virtual rows: virtual row v is row 16 * (v / 32) + v % 16
+// of the gate matrix when v % 32 < 16 and of the up matrix otherwise, so
+// every 32-row tile holds 16 gate rows and the same 16 up rows, and y
+// receives silu(g) * u, [M][n_out].  Virtual rows past n_out read the last
+// row and are never stored.
 struct DevProblem {
     const uint8_t *w;
+    const uint8_t *w2;
     const float *x;
     float *y;
     float *part;
@@ -29,7 +39,26 @@ struct DevProblem {
     int tile_begin;
     int tiles;
     int splits;
+    int n_out;
 };
+
+// Row of the gate (w) or up (w2) matrix that virtual row v reads, clamped to
+// n_out - 1, and which of the two it is.
+__host__ __device__ inline int pair_row(int v, int n_out) {
+    const int n = ((v >> 5) << 4) | (v & 15);
+    return n < n_out ? n : n_out - 1;
+}
+__host__ __device__ inline bool pair_is_up(int v) { return (v & 16) != 0; }
+__host__ __device__ inline int pair_rows(int n_out) { return 32 * ((n_out + 15) / 16); }
+
+// silu(g) * u with silu(g) = g / (1 + e^-g), e^-g = 2^(-g * log2 e) from the
+// hardware base-2 exponential and the quotient from the hardware reciprocal
+// (each about one ulp; a few ulp in all).  Large |g| saturate correctly:
+// e^-g -> inf gives 0, e^-g -> 0 gives g * u; NaN propagates.
+__device__ __forceinline__ float swiglu(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
 
 // Passed by value in the kernel-argument segment (well under its 4 KiB limit).
 // tb[i] repeats p[i].tile_begin (INT_MAX past count) as one contiguous table,
@@ -72,10 +101,14 @@ __device__ __forceinline__ int find_problem(const Batch &bt, int g) {
 // global memory and keeps global (not flat) loads through them.
 __device__ __forceinline__ DevProblem load_problem(const Batch &bt, int p) {
     const DevProblem P = bt.p[p];
-    asm volatile("" ::"s"(P.w), "s"(P.x), "s"(P.y), "s"(P.part), "s"(P.N), "s"(P.K), "s"(P.tile_begin),
-                 "s"(P.tiles), "s"(P.splits));
+    asm volatile("" ::"s"(P.w), "s"(P.w2), "s"(P.x), "s"(P.y), "s"(P.part), "s"(P.N), "s"(P.K),
+                 "s"(P.tile_begin), "s"(P.tiles), "s"(P.splits), "s"(P.n_out));
     return P;
 }
+
+// Q4K_OK if the current device is a usable gfx950, else Q4K_ERR_DEVICE
+// (cached per device).
+int check_device();
 
 // Enqueue the GEMV family / the matrix-core family for every problem of `b`.
 // Return hipSuccess or the launch error.

@@ -330,7 +330,10 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
         return *reinterpret_cast<const uint4 *>(xcol + row * K + static_cast<size_t>(s) * kBK);
     };
     const int wr = t >> 1, wh = t & 1;
-    const uint8_t *wrow = W + (static_cast<size_t>(min(tn0 + wr, N - 1)) * KB + kb0) * kBlockBytes;
+    const int vrow = min(tn0 + wr, N - 1);
+    const uint8_t *wrow =
+        P.w2 ? (pair_is_up(vrow) ? P.w2 : W) + (static_cast<size_t>(pair_row(vrow, P.n_out)) * KB + kb0) * kBlockBytes
+             : W + (static_cast<size_t>(vrow) * KB + kb0) * kBlockBytes;
 
     const int steps = kbn * 4;
     // Raw data of the next step, loaded while the current one runs on the
@@ -578,6 +581,33 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
     };
     // Undo the per-row scaling of x (a power of two: exact).
     const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
+    if (P.w2 && splits == 1) {
+        // Gate/up pairs: columns c and c ^ 16 of a 32-column block are the
+        // gate and up rows of one output, held by lanes l and l ^ 16 in the
+        // same registers.  Registers r and r + 1 (rows m and m + 1) are
+        // shared out: the gate lane sends its g of row m + 1 and takes u of
+        // row m, the up lane the reverse, so each lane finishes one output.
+        const int n_out = P.n_out;
+        const bool up = (lane & 16) != 0;
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a) {
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b) {
+                const int n = ((tn0 + S::TN * wn + 32 * b) >> 1) + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int m0 = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const float v0 = acc[a][b][r] * xfac[min(m0, M - 1)];
+                    const float v1 = acc[a][b][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float got = __shfl_xor(up ? v0 : v1, 16);
+                    const int m = up ? m0 + 1 : m0;
+                    if (m < M && n < n_out)
+                        P.y[static_cast<size_t>(m) * n_out + n] = up ? swiglu(got, v1) : swiglu(v0, got);
+                }
+            }
+        }
+        return;
+    }
     if (splits == 1) {
         for_each_out([&](size_t e, int m, float v) { P.y[e] = v * xfac[m]; });
         return;
@@ -592,10 +622,27 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
 }
 
 // y = sum over chunks of the partial sums, in chunk order, for split problems
-// (four outputs per thread).
+// (four outputs per thread; gate/up pairs: silu(g) * u of the two sums, one
+// output per thread).
 __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
     const int p = find_problem(bt, static_cast<int>(blockIdx.x));
     const DevProblem P = load_problem(bt, p);
+    if (P.w2) {
+        const size_t o = static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x;
+        const size_t outs = static_cast<size_t>(bt.M) * P.n_out;
+        if (o >= outs) return;
+        const size_t m = o / P.n_out;
+        const int n = static_cast<int>(o - m * P.n_out);
+        const size_t vg = m * P.N + (((n >> 4) << 5) | (n & 15));  // its gate row; up is 16 further
+        const size_t total = static_cast<size_t>(bt.M) * P.N;
+        float g = P.part[vg], u = P.part[vg + 16];
+        for (int c = 1; c < P.splits; ++c) {
+            g += P.part[static_cast<size_t>(c) * total + vg];
+            u += P.part[static_cast<size_t>(c) * total + vg + 16];
+        }
+        P.y[o] = swiglu(g, u);
+        return;
+    }
     const size_t e = (static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x) * 4;
     const size_t total = static_cast<size_t>(bt.M) * P.N;
     if (e >= total) return;
@@ -725,7 +772,8 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
         DevProblem &r = red.p[red.count++];
         r = d;
         r.tile_begin = blocks;
-        blocks += static_cast<int>((static_cast<size_t>(pl.sb.M) * d.N + 1023) / 1024);
+        blocks += d.w2 ? static_cast<int>((static_cast<size_t>(pl.sb.M) * d.n_out + 255) / 256)
+                       : static_cast<int>((static_cast<size_t>(pl.sb.M) * d.N + 1023) / 1024);
     }
     hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, sealed(red));
     return hipGetLastError();

@@ -141,9 +141,14 @@ int q4k_matmul_argmax(const void *w_packed, const float *x, int M, int N, int K,
  *     out[m, n] = silu(g[m, n]) * u[m, n],   silu(z) = z / (1 + exp(-z)),
  *     g = x . dequant(W_gate)^T,   u = x . dequant(W_up)^T,
  * the input of the down projection (the Qwen3 family on the pages uses a
- * SwiGLU MLP).  g and u are computed as one q4k_matmul_batched launch over
- * the shared x (same kernels, same results as q4k_matmul) and kept in the
- * library workspace; exp is the device math library's single precision exp.
+ * SwiGLU MLP).  For M == 1 and M > 16 the epilogue runs inside the product
+ * kernels: each 32-row tile of W holds 16 gate rows and the same 16 up rows,
+ * so g and u of one output meet in one lane (or its neighbour) and only
+ * silu(g) * u is written (with a split K, the second kernel that adds the K
+ * chunks applies it).  For 2 <= M <= 16, g and u are one batched product in
+ * the library workspace and a small kernel combines them.  g and u are the
+ * kernels' usual values; e^-g is the hardware base-2 exponential of
+ * -g*log2(e) and the quotient the hardware reciprocal (a few ulp).
  *   w_gate, w_up: DEVICE packed Q4_K [N, K/256*144] each.  x: DEVICE float32
  *   [M, K].  out: DEVICE float32 [M, N], overwritten; it must not overlap x or
  *   either W.  All four 16-byte aligned.
