@@ -11,6 +11,7 @@ silu(g) * u in numpy double precision to two of those products.  See the header 
 which passages it follows.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(the affine q4a functions by ``tests/test_oracle_q4a_pins.py``)
 (binary16 decoding against numpy over all 65536 patterns, hand-built blocks with
 closed-form weights, one-hot products, brute force on tiny inputs).  Binary
 compatibility with GGUF files written by other tools is parity unpinned: no such
@@ -72,6 +73,13 @@ def _load():
     lib.q4k_oracle_threads.restype = ctypes.c_int
     lib.q4k_oracle_matmul.argtypes = [u8p, f32p, i64, i64, i64, f64p, f64p, ctypes.c_int]
     lib.q4k_oracle_matmul.restype = ctypes.c_int
+    lib.q4k_oracle_q4a_dequant_f64.argtypes = [u8p, u8p, u8p, i64, i64, f64p]
+    lib.q4k_oracle_q4a_dequant_f64.restype = ctypes.c_int
+    lib.q4k_oracle_q4a_dequant.argtypes = [u8p, u8p, u8p, i64, i64, f32p]
+    lib.q4k_oracle_q4a_dequant.restype = ctypes.c_int
+    lib.q4k_oracle_q4a_matmul_cols.argtypes = [u8p, u8p, u8p, f32p, i64, i64, i64, ctypes.c_void_p, i64, f64p,
+                                               f64p, ctypes.c_int]
+    lib.q4k_oracle_q4a_matmul_cols.restype = ctypes.c_int
     for name in ("q4k_oracle_matmul_cols", "q4k_oracle_matmul_cols_f16"):
         fn = getattr(lib, name)
         fn.argtypes = [u8p, f32p, i64, i64, i64, ctypes.c_void_p, i64, f64p, f64p, ctypes.c_int]
@@ -214,3 +222,65 @@ def swiglu(w_gate: np.ndarray, w_up: np.ndarray, x: np.ndarray, N: int, K: int, 
     g, s_g = matmul(w_gate, x, N, K, threads)
     u, s_u = matmul(w_up, x, N, K, threads)
     return silu(g) * u, g, u, s_g, s_u
+
+
+# --- affine 4-bit group quantization (q4a) -----------------------------------
+# Layout (the mlx-rs pull request #356 page names this q4 format; its bytes are
+# read plainly, see q4k_oracle.c): q [N, K/8] uint32 (element k at bits
+# 4*(k%8) of word k/8), scales and biases [N, K/64] binary16,
+# w = s * q + b per group of 64.
+
+Q4A_GROUP = 64
+
+
+def _q4a_arrays(q, scales, biases, K):
+    if K % Q4A_GROUP != 0:
+        raise ValueError(f"K={K} is not a multiple of {Q4A_GROUP}")
+    q = np.ascontiguousarray(q).view(np.uint8).reshape(-1, K // 2)
+    scales = np.ascontiguousarray(scales).view(np.uint8).reshape(-1, K // 32)
+    biases = np.ascontiguousarray(biases).view(np.uint8).reshape(-1, K // 32)
+    if not (q.shape[0] == scales.shape[0] == biases.shape[0]):
+        raise ValueError("q, scales and biases disagree on N")
+    return q, scales, biases
+
+
+def q4a_dequant_exact(q, scales, biases, K: int) -> np.ndarray:
+    """Exact weights [N, K] as doubles."""
+    q, sc, bi = _q4a_arrays(q, scales, biases, K)
+    out = np.empty((q.shape[0], K), np.float64)
+    rc = _load().q4k_oracle_q4a_dequant_f64(_ptr(q), _ptr(sc), _ptr(bi), q.shape[0], K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"q4a dequant failed ({rc})")
+    return out
+
+
+def q4a_dequant(q, scales, biases, K: int) -> np.ndarray:
+    """f32 weights [N, K]: each exact weight rounded once."""
+    q, sc, bi = _q4a_arrays(q, scales, biases, K)
+    out = np.empty((q.shape[0], K), np.float32)
+    rc = _load().q4k_oracle_q4a_dequant(_ptr(q), _ptr(sc), _ptr(bi), q.shape[0], K, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"q4a dequant failed ({rc})")
+    return out
+
+
+def q4a_matmul_cols(q, scales, biases, x, N: int, K: int, cols, threads: int = 0):
+    """(y, s) of the q4a product restricted to the W rows in cols: [M, len(cols)]."""
+    q, sc, bi = _q4a_arrays(q, scales, biases, K)
+    if q.shape[0] != N:
+        raise ValueError("rows != N")
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, K)
+    cols = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+    M = x.shape[0]
+    y = np.empty((M, cols.size), np.float64)
+    s = np.empty((M, cols.size), np.float64)
+    rc = _load().q4k_oracle_q4a_matmul_cols(_ptr(q), _ptr(sc), _ptr(bi), _ptr(x), M, N, K, _ptr(cols), cols.size,
+                                            _ptr(y), _ptr(s), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"q4a matmul failed ({rc})")
+    return y, s
+
+
+def q4a_matmul(q, scales, biases, x, N: int, K: int, threads: int = 0):
+    """(y, s) of the full q4a product, [M, N]."""
+    return q4a_matmul_cols(q, scales, biases, x, N, K, np.arange(N), threads)

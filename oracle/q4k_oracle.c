@@ -342,3 +342,111 @@ int q4k_oracle_matmul_cols_f16(const uint8_t *w, const float *x, int64_t M, int6
 {
     return matmul_cols(w, x, M, N, K, cols, ncols, y, s, threads, 1);
 }
+
+/* ==========================================================================
+ * Affine 4-bit group quantization ("q4a"): the MLX-style q4 format that the
+ * mlx-rs pull request #356 page loads for its QuantizedLinear layers (weight
+ * keys with a `.scales` sibling, q4 and q8 checkpoints), with the group size
+ * of 64 that page uses as the default for its affine quantized caches.  The
+ * page names the format but does not print its bytes; the layout read here
+ * is the plain one:
+ *   q       [N][K/8] 32-bit little-endian words; element k of a row is the
+ *           4-bit field at bits 4*(k%8) .. 4*(k%8)+3 of word k/8
+ *   scales  [N][K/64] IEEE binary16 (little endian), one per group of 64
+ *   biases  [N][K/64] IEEE binary16
+ *   w[n,k] = s[n, k/64] * q[n,k] + b[n, k/64]
+ * s*q and b are multiples of 2^-24 (the binary16 quantum) below 2^20 and
+ * 2^16 in magnitude, so their sum is a multiple of 2^-24 below 2^21: exact
+ * in double (at most 45 bits).  Rounded once it is the f32 weight.
+ * ========================================================================== */
+
+/* Exact weights of one row of K values (K % 64 == 0). */
+static void q4a_row_exact(const uint8_t *qrow, const uint8_t *srow, const uint8_t *brow, int64_t K,
+                          double *out)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        const uint8_t *wb = qrow + 4 * (k / 8);
+        uint32_t word = (uint32_t)wb[0] | ((uint32_t)wb[1] << 8) | ((uint32_t)wb[2] << 16) |
+                        ((uint32_t)wb[3] << 24);
+        unsigned q = (word >> (4 * (k % 8))) & 15u;
+        int64_t g = k / 64;
+        double s = q4k_oracle_half_to_double((uint16_t)(srow[2 * g] | (srow[2 * g + 1] << 8)));
+        double b = q4k_oracle_half_to_double((uint16_t)(brow[2 * g] | (brow[2 * g + 1] << 8)));
+        out[k] = s * (double)q + b;
+    }
+}
+
+/* Exact weights [rows, K] as doubles.  Returns 0, or -2 for a bad shape. */
+int q4k_oracle_q4a_dequant_f64(const uint8_t *q, const uint8_t *scales, const uint8_t *biases,
+                               int64_t rows, int64_t K, double *out)
+{
+    if (K % 64 != 0 || rows < 0 || K < 0)
+        return -2;
+    for (int64_t n = 0; n < rows; ++n)
+        q4a_row_exact(q + n * (K / 2), scales + n * (K / 32), biases + n * (K / 32), K, out + n * K);
+    return 0;
+}
+
+/* f32 weights [rows, K]: the exact weight rounded once. */
+int q4k_oracle_q4a_dequant(const uint8_t *q, const uint8_t *scales, const uint8_t *biases,
+                           int64_t rows, int64_t K, float *out)
+{
+    if (K % 64 != 0 || rows < 0 || K < 0)
+        return -2;
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!tmp)
+        return -3;
+    for (int64_t n = 0; n < rows; ++n) {
+        q4a_row_exact(q + n * (K / 2), scales + n * (K / 32), biases + n * (K / 32), K, tmp);
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = (float)tmp[k];
+    }
+    free(tmp);
+    return 0;
+}
+
+/* The naive product over the W rows listed in cols, as q4k_oracle_matmul_cols:
+ *   y[m*ncols + c] = sum_k (double)x[m,k] * (double)w32[cols[c], k],
+ *   s[m*ncols + c] = sum_k |that product|,
+ * k ascending, w32 the f32 weight. */
+int q4k_oracle_q4a_matmul_cols(const uint8_t *q, const uint8_t *scales, const uint8_t *biases,
+                               const float *x, int64_t M, int64_t N, int64_t K, const int64_t *cols,
+                               int64_t ncols, double *y, double *s, int threads)
+{
+    if (K % 64 != 0 || M < 0 || N < 0 || K < 0 || ncols < 0)
+        return -2;
+    for (int64_t c = 0; c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N)
+            return -2;
+    set_threads(threads);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *wx = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        if (!wx) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t c = 0; c < ncols; ++c) {
+                int64_t n = cols[c];
+                q4a_row_exact(q + n * (K / 2), scales + n * (K / 32), biases + n * (K / 32), K, wx);
+                for (int64_t k = 0; k < K; ++k)
+                    wx[k] = (double)(float)wx[k];
+                for (int64_t m = 0; m < M; ++m) {
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t k = 0; k < K; ++k) {
+                        double p = (double)x[m * K + k] * wx[k];
+                        acc += p;
+                        mag += fabs(p);
+                    }
+                    y[m * ncols + c] = acc;
+                    if (s)
+                        s[m * ncols + c] = mag;
+                }
+            }
+        }
+        free(wx);
+    }
+    return failed ? -3 : 0;
+}

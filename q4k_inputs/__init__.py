@@ -112,3 +112,28 @@ def one_hot_x(M: int, K: int, positions) -> np.ndarray:
     x = np.zeros((M, K), np.float32)
     x[np.arange(M), np.asarray(positions)] = 1.0
     return x
+
+
+# --- affine 4-bit group quantization (q4a): q words, binary16 scales and biases
+Q4A_GROUP = 64
+Q4A_SCALE_RANGE = (0.002, 0.02)
+
+
+def random_q4a(N: int, K: int, seed):
+    """(q uint32 [N, K/8], scales float16 [N, K/64], biases float16 [N, K/64]).
+
+    Quant words are uniform random bits (so every 4-bit field is uniform on
+    0..15); per group of 64 the scale is U[0.002, 0.02] and the bias
+    -7.5 * scale * U[0.8, 1.2], both rounded to binary16 (the stored bits are
+    the ground truth): weights spread around zero as a group's affine
+    quantization of centred weights would (bias = the group's minimum,
+    scale = its range / 15)."""
+    if K % Q4A_GROUP != 0:
+        raise ValueError(f"K={K} is not a multiple of {Q4A_GROUP}")
+    rng = _rng(seed)
+    q = rng.bit_generator.random_raw((N * K // 8 + 1) // 2).view(np.uint32)[:N * K // 8].reshape(N, K // 8).copy() \
+        if N * K else np.zeros((N, K // 8), np.uint32)
+    g = N * (K // Q4A_GROUP)
+    s = rng.uniform(Q4A_SCALE_RANGE[0], Q4A_SCALE_RANGE[1], g)
+    b = -7.5 * s * rng.uniform(0.8, 1.2, g)
+    return q, s.astype(np.float16).reshape(N, K // Q4A_GROUP), b.astype(np.float16).reshape(N, K // Q4A_GROUP)
