@@ -34,6 +34,8 @@ Also reported in the same line:
   * ``swiglu_gate_up``: the Qwen3-14B-shaped gate/up pair with the SwiGLU
     epilogue in the product kernels, against the two products alone, at
     M = 1 and 1024;
+  * ``q4a_decode_m1``: the affine 4-bit group format (include/q4a.h) on the
+    Qwen3-14B-shaped layer at M = 1, weight GB/s against the HBM bound;
   * ``layer_sweep``: one Qwen3-14B-shaped layer at M = 1 .. 1024 (microseconds
     per batched launch, weight GB/s, TFLOP/s, kernel family);
   * ``cross_check_*``: agreement of the timed kernels with a second kernel
@@ -436,6 +438,38 @@ def swiglu_figures(q4k, dev, steps, warmup):
     return out
 
 
+def q4a_figures(q4k, dev, steps, warmup, sets=2):
+    """The affine 4-bit group format (q4a_matmul) on the Qwen3-14B-shaped layer
+    at M = 1: its seven projections as seven launches, graph replays
+    alternating `sets` copies of the weights (more than the last-level cache);
+    weight bytes are the quant words plus the binary16 scales and biases
+    (0.5625 B per weight, as Q4_K)."""
+    import torch
+    import q4k_inputs as qi
+    from q4k_inputs.workloads import PROJ_ID, WORKLOADS, X_ROLE
+    wl = WORKLOADS["qwen3-14b_sweep"]
+    xs, probs = {}, []
+    wbytes = 0
+    for name, N, K in wl.layer:
+        r = X_ROLE[name]
+        if r not in xs:
+            xs[r] = torch.from_numpy(qi.random_x(1, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 1, 1000 + r))).to(dev)
+        q, sc, bi = qi.random_q4a(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 0, PROJ_ID[name], 4))
+        ws = [(torch.from_numpy(q).to(dev), torch.from_numpy(sc).to(dev), torch.from_numpy(bi).to(dev))]
+        ws += [tuple(t.clone() for t in ws[0]) for _ in range(sets - 1)]
+        probs.append((ws, xs[r], torch.empty((1, N), dtype=torch.float32, device=dev)))
+        wbytes += q.nbytes + sc.nbytes + bi.nbytes
+
+    def layer(st, c):
+        for ws, x, y in probs:
+            q4k.q4a_matmul(*ws[c], x, y=y, stream=st)
+    ms = _time_replays(_capture(lambda st: [layer(st, c) for c in range(sets)]), steps, warmup) / sets
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    return {"workload": "qwen3-14b layer (q,k,v,o,gate,up,down) in the q4a layout, M=1, seven launches",
+            "weight_bytes": wbytes, "us_per_layer": round(ms * 1e3, 2), "weight_GBps": round(gbps, 1),
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -586,7 +620,7 @@ def main():
                     help="skip the Llama-3.2-1B pass, the launch groupings and the other workloads of the list")
     ap.add_argument("--only", default=None,
                     help="run one piece only, for profiling: qwen3-14b_m1, llama1b_m1, prefill_m32, "
-                         "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax, swiglu")
+                         "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax, swiglu, q4a")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy three times (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -665,6 +699,8 @@ def main():
     if not args.no_others:
         out["swiglu_gate_up"] = swiglu_figures(q4k, dev, args.steps, args.warmup)
         log(f"swiglu: {out['swiglu_gate_up']}")
+        out["q4a_decode_m1"] = q4a_figures(q4k, dev, args.steps, args.warmup)
+        log(f"q4a: {out['q4a_decode_m1']}")
         torch.cuda.empty_cache()
         wl1 = WORKLOADS["llama3.2-1b_decode_m1"]
         p1 = Pass(wl1, 1, dev)
@@ -712,6 +748,8 @@ def run_only(args, q4k, dev):
         wl = wl14 if name.startswith("qwen3-14b") else WORKLOADS["qwen3-8b_prefill_m1024"]
         r, _ = prefill_pass(q4k, dev, wl, args.prefill_steps)
         res = {"ms_per_step": r["ms_per_step"], "TFLOPs": r["value"]}
+    elif name == "q4a":
+        res = q4a_figures(q4k, dev, args.steps, args.warmup)
     elif name == "swiglu":
         res = swiglu_figures(q4k, dev, args.steps, args.warmup)
     elif name == "argmax":

@@ -49,7 +49,7 @@ PATH_GEMV = 3
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
-            "q4k_matmul_batched_noalloc",
+            "q4k_matmul_batched_noalloc", "q4a_matmul",
             "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_gguf_list", "q4k_select_path", "q4k_strerror",
             "q4k_version")
 
@@ -97,6 +97,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_argmax.restype = ci
     lib.q4k_matmul_swiglu.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
     lib.q4k_matmul_swiglu.restype = ci
+    lib.q4a_matmul.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.q4a_matmul.restype = ci
     lib.q4k_gguf_list.argtypes = [ctypes.c_char_p, ctypes.POINTER(GgufTensor), ci, ctypes.POINTER(ci)]
     lib.q4k_gguf_list.restype = ci
     lib.q4k_select_path.argtypes = [ci, ci, ci]
@@ -333,6 +335,49 @@ def raw_matmul_batched_noalloc(items: Iterable[Tuple[int, int, int, int, int]], 
     for i, (w, x, y, n, k) in enumerate(items):
         arr[i] = _Problem(w, x, y, n, k)
     return library().q4k_matmul_batched_noalloc(arr, len(items), M, stream)
+
+
+Q4A_GROUP = 64
+
+
+def q4a_matmul(w_q, scales, biases, x, y=None, stream=None):
+    """y[M, N] = x[M, K] . dequant(W)^T for W in the affine 4-bit group layout
+    of include/q4a.h: w_q uint32 [N, K/8] (or uint8 [N, K/2]), scales and
+    biases float16 [N, K/64], w = s * q + b per group of 64."""
+    import torch
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise TypeError("x must be float32 [M, K]")
+    M, K = x.shape
+    if K % Q4A_GROUP != 0:
+        raise Q4KError(ERR_BAD_DIM, f"K={K}")
+    if scales.dtype != torch.float16 or biases.dtype != torch.float16:
+        raise TypeError("scales and biases must be float16")
+    if w_q.dtype not in (torch.uint32, torch.int32, torch.uint8):
+        raise TypeError("w_q must hold 32-bit words (uint32/int32) or their bytes (uint8)")
+    N = scales.shape[0] if scales.dim() == 2 else scales.numel() // (K // Q4A_GROUP)
+    if w_q.numel() * w_q.element_size() != N * K // 2 or scales.numel() != N * K // 64 or \
+            biases.numel() != N * K // 64:
+        raise ValueError(f"w_q must hold N*K/2 = {N * K // 2} bytes and scales/biases N*K/64 = {N * K // 64} values")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or tuple(y.shape) != (M, N):
+        raise ValueError("y must be float32 [M, N]")
+    for name, t in (("w_q", w_q), ("scales", scales), ("biases", biases), ("x", x), ("y", y)):
+        if not t.is_cuda or t.device != x.device:
+            raise ValueError(f"{name} must be a device tensor on {x.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    rc = library().q4a_matmul(w_q.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(), y.data_ptr(),
+                              M, N, K, _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4a_matmul")
+    return y
+
+
+def raw_q4a_matmul(wq_ptr: int, s_ptr: int, b_ptr: int, x_ptr: int, y_ptr: int, M: int, N: int, K: int,
+                   stream: Optional[int] = None) -> int:
+    """Direct C-ABI call of q4a_matmul with raw device addresses; returns the status."""
+    return library().q4a_matmul(wq_ptr, s_ptr, b_ptr, x_ptr, y_ptr, M, N, K, stream)
 
 
 def gguf_tensors(path) -> list:

@@ -1,0 +1,51 @@
+/*
+ * q4a.h -- affine 4-bit group quantization ("q4a") in libq4k.so.
+ *
+ * The mlx-rs pull request #356 page loads q4 (and q8) QuantizedLinear
+ * weights, recognised by a `.scales` tensor beside each weight, and uses
+ * groups of 64 for its affine quantized caches.  The page prints no byte
+ * layout; the one implemented here is the plain reading:
+ *
+ *   w_q     [N][K/8]  32-bit little-endian words: element k of row n is the
+ *                     4-bit field q at bits 4*(k%8) .. 4*(k%8)+3 of word k/8
+ *   scales  [N][K/64] IEEE binary16 s, one per group of 64 consecutive k
+ *   biases  [N][K/64] IEEE binary16 b
+ *   w[n, k] = s[n, k/64] * q[n, k] + b[n, k/64]
+ *
+ * and the product is y[m, n] = sum_k x[m, k] * w[n, k], as for Q4_K (q4k.h).
+ * Each weight is formed once in fp32 by a fused multiply-add (the exact
+ * weight rounded once) and the sum is accumulated in fp32, so a group whose
+ * terms cancel (s*q == -b) contributes exactly zero.
+ */
+#ifndef Q4A_H
+#define Q4A_H
+
+#include "q4k.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4A_GROUP 64
+
+/* y = x . dequant(W)^T for W in the q4a layout above.
+ *   w_q: DEVICE, N*K/2 bytes, 16-byte aligned.  scales, biases: DEVICE,
+ *   N*K/64 binary16 each, 2-byte aligned.  x: DEVICE float32 [M, K],
+ *   y: DEVICE float32 [M, N], both 16-byte aligned; y is overwritten and must
+ *   not overlap the inputs.  Same stream, ownership and no-sync rules as
+ *   q4k_matmul.
+ *   The kernel streams W once per two tokens (it is meant for decoding, where
+ *   M is small); any M is accepted.
+ *   Errors: M, N or K negative, or K not a positive multiple of 64 when M and
+ *   N are positive: Q4K_ERR_BAD_DIM; a NULL pointer: Q4K_ERR_NULL; alignment:
+ *   Q4K_ERR_ALIGN; no gfx950 device: Q4K_ERR_DEVICE; launch failure:
+ *   Q4K_ERR_LAUNCH.  M == 0 or N == 0 is a no-op.  Nothing is enqueued on
+ *   error. */
+int q4a_matmul(const void *w_q, const void *scales, const void *biases, const float *x, float *y, int M, int N,
+               int K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4A_H */

@@ -5,6 +5,7 @@ strings, the version, the path policy and the argument checks, which reject
 bad arguments before any HIP call.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -13,13 +14,15 @@ import pytest
 import gguf_q4_dequant_amd as q4k
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q4k.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q4k_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q4[ak]_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +35,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("q4k_matmul", "q4k_matmul_batched", "q4k_strerror"):
+    assert len(HEADERS) >= 2
+    for required in ("q4k_matmul", "q4k_matmul_batched", "q4k_strerror", "q4a_matmul"):
         assert required in names
     assert set(names) == set(q4k.EXPORTED)
 
@@ -101,3 +105,17 @@ def test_argmax_output_tensors_are_checked_before_any_call():
     # a CPU w/x never reaches the library either
     with pytest.raises(ValueError, match="device tensors"):
         q4k.matmul_argmax(torch.zeros((4, 144), dtype=torch.uint8), x, index=ok_index)
+
+
+def test_q4a_argument_errors_before_any_device_call(lib):
+    A = 1 << 20
+    assert q4k.raw_q4a_matmul(A, A, A, A, A, 1, 4, 100) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul(A, A, A, A, A, 1, 4, 0) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul(A, A, A, A, A, -1, 4, 64) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul(0, A, A, A, A, 1, 4, 64) == q4k.ERR_NULL
+    assert q4k.raw_q4a_matmul(A, 0, A, A, A, 1, 4, 64) == q4k.ERR_NULL
+    assert q4k.raw_q4a_matmul(A + 8, A, A, A, A, 1, 4, 64) == q4k.ERR_ALIGN
+    assert q4k.raw_q4a_matmul(A, A + 1, A, A, A, 1, 4, 64) == q4k.ERR_ALIGN
+    assert q4k.raw_q4a_matmul(A, A, A, A + 4, A, 1, 4, 64) == q4k.ERR_ALIGN
+    assert q4k.raw_q4a_matmul(0, 0, 0, 0, 0, 0, 4, 64) == q4k.OK
+    assert q4k.raw_q4a_matmul(0, 0, 0, 0, 0, 3, 0, 64) == q4k.OK

@@ -1,0 +1,108 @@
+"""GPU parity of the affine 4-bit group format (q4a_matmul, include/q4a.h)
+against the oracle: element by element within 1e-5 * sum|x*w| (fp32
+arithmetic on exact weights), one-hot activations returning the f32 weights
+bit for bit, groups whose terms cancel returning exactly zero, and the
+full-size Qwen3-14B-shaped layer on sampled columns."""
+import numpy as np
+import pytest
+
+import gguf_q4_dequant_amd as q4k
+import oracle
+import q4k_inputs as qi
+from q4k_inputs.workloads import WORKLOADS
+from tests.gpu_helpers import DECODE_TOL, check_close, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(q, s, b):
+    return to_dev(q), to_dev(s), to_dev(b)
+
+
+def _run(q, s, b, x):
+    import torch
+    y = q4k.q4a_matmul(*_dev(q, s, b), to_dev(x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# Ragged N (1, 31, 33, 257: the last 32-row workgroup partly idle), K from a
+# single group to 128 groups (lanes of a wave with and without a second and
+# third half-group), one and two tokens per grid row, odd M.
+SHAPES = [(1, 1, 64), (1, 31, 128), (1, 33, 2048), (1, 1000, 5120), (2, 100, 1024), (3, 70, 192),
+          (5, 257, 4096), (16, 64, 8192), (33, 40, 640), (1, 96, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_q4a_matches_oracle(M, N, K):
+    q, s, b = qi.random_q4a(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 970, M, N, K))
+    x = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 971, M, N, K))
+    y = _run(q, s, b, x)
+    y_ref, S = oracle.q4a_matmul(q, s, b, x, N, K)
+    check_close(y, y_ref, S, DECODE_TOL, f"q4a M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_q4a_one_hot_returns_f32_weights(M):
+    N, K = 70, 512
+    q, s, b = qi.random_q4a(N, K, seed=972)
+    ks = [0, 1, 7, 8, 63, 64, 255, 511][:M] if M > 1 else [101]
+    x = qi.one_hot_x(len(ks), K, ks)
+    y = _run(q, s, b, x)
+    assert np.array_equal(y, oracle.q4a_dequant(q, s, b, K)[:, ks].T)
+
+
+def test_q4a_cancelling_groups_and_hand_built_words():
+    """Rows whose groups are s = 1, b = -2, q = 2 (every weight 0) give exactly
+    0 whatever x; a row of the hand-derived ramp words (s = 0.5, b = -3,
+    q = k % 16) gives its closed form under one-hot x."""
+    N, K = 40, 256
+    q, s, b = qi.random_q4a(N, K, seed=973)
+    q[5, :] = 0x22222222
+    s[5, :] = np.float16(1.0)
+    b[5, :] = np.float16(-2.0)
+    q[6, :] = np.array([0x76543210, 0xFEDCBA98] * (K // 16), np.uint32)
+    s[6, :] = np.float16(0.5)
+    b[6, :] = np.float16(-3.0)
+    x = qi.random_x(3, K, seed=974)
+    y = _run(q, s, b, x)
+    assert np.all(y[:, 5] == 0)
+    y_ref, S = oracle.q4a_matmul(q, s, b, x, N, K)
+    check_close(y, y_ref, S, DECODE_TOL, "cancelling rows")
+    ks = list(range(0, K, 9))
+    y1 = _run(q, s, b, qi.one_hot_x(len(ks), K, ks))
+    assert np.array_equal(y1[:, 6], np.array([(k % 16) / 2 - 3 for k in ks], np.float32))
+
+
+@pytest.mark.parametrize("name", ["q", "k", "o", "gate", "down"])
+def test_q4a_qwen3_14b_layer_shapes(name):
+    """The Qwen3-14B-shaped projections at M = 1, sampled columns."""
+    wl = WORKLOADS["qwen3-14b_sweep"]
+    (_, N, K), = [p for p in wl.layer if p[0] == name]
+    q, s, b = qi.random_q4a(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 975, N, K))
+    x = qi.random_x(1, K, seed=qi.tensor_seed(qi.BASE_SEED, 976, K))
+    y = _run(q, s, b, x)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N).integers(0, N, 200)]))
+    y_ref, S = oracle.q4a_matmul_cols(q, s, b, x, N, K, cols)
+    check_close(y[:, cols], y_ref, S, DECODE_TOL, f"q4a {name}")
+
+
+def test_q4a_errors_leave_y_untouched_and_weights_unchanged():
+    import torch
+    dev = device()
+    N, K = 64, 256
+    q, s, b = qi.random_q4a(N, K, seed=977)
+    qd, sd, bd = _dev(q, s, b)
+    x = torch.ones((2, K), device=dev)
+    y = torch.full((2, N), 7.0, device=dev)
+    assert q4k.raw_q4a_matmul(qd.data_ptr(), sd.data_ptr(), bd.data_ptr(), x.data_ptr(), y.data_ptr(), 2, N, 100) \
+        == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul(qd.data_ptr() + 4, sd.data_ptr(), bd.data_ptr(), x.data_ptr(), y.data_ptr(), 2, N, K) \
+        == q4k.ERR_ALIGN
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    y1 = q4k.q4a_matmul(qd, sd, bd, x)
+    y2 = q4k.q4a_matmul(qd, sd, bd, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert np.array_equal(qd.cpu().numpy(), q) and np.array_equal(sd.cpu().numpy(), s)
