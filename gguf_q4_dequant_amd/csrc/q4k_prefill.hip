@@ -148,9 +148,15 @@ struct CvtBatch {
 };
 
 constexpr int kCvtThreads = 256;
-constexpr int kCvtRegs = 24;  // float4 per thread kept in registers: rows up to 24576 values read once
 
+// REGS float4 per thread stay in registers between the maximum and the
+// conversion: rows of up to REGS * 1024 values are read once (longer rows
+// read their tail a second time).  The launch picks the smallest REGS that
+// holds its longest row, so short rows keep the register count (and with it
+// the number of resident workgroups) low.
+template <int REGS>
 __global__ __launch_bounds__(kCvtThreads) void convert_x_kernel(CvtBatch cb) {
+    constexpr int kCvtRegs = REGS;
     __shared__ float wmax[kCvtThreads / 64];
     int p = 0;
     for (int i = 1; i < cb.count; ++i)
@@ -665,6 +671,212 @@ __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
     }
 }
 
+// ---- up to 32 tokens: W dequantized straight into the MFMA operands ------
+// Few tokens make the product a stream of W: every W byte should cross the
+// chip once and be touched as little as possible on the way.  Workgroups of
+// four waves own 128 rows of W (32 per wave) and one K chunk, for all
+// tokens at once (one 32-row MFMA tile):
+//   * W: each wave reads its 32 rows' super-block as contiguous 16-byte pieces
+//     (the 144-byte rows back to back), parks the packed bytes in its own LDS
+//     slot, and every lane then picks up its row's header and quant bytes and
+//     dequantizes them by the mixed-precision FMA (each weight rounded once
+//     from its exact value, as the larger tiles do) straight into the B
+//     operand of v_mfma_f32_32x32x16_f16: lane l feeds row l % 32, k-half
+//     l / 32 of each 16-deep slice.  Packed bytes through LDS are a quarter
+//     of binary16 weights.
+//   * x: the binary16 copy (scaled per row, see above), one super-block of all
+//     32 token rows per step, moved by 16-byte global-to-LDS loads with no
+//     registers held (row m's 16-byte chunk c at position 32m + (c ^ (m & 15)),
+//     so each group of 16 lanes reading one chunk of 16 rows hits distinct
+//     banks), double-buffered: step b + 1's x and W are requested before step
+//     b's MFMAs.
+//   * Partial tiles of split K are summed by split_sum_kernel, as for the other
+//     tiles.  Rows of x past M re-read row M - 1 and are never stored.
+constexpr int kSkWaves = 4;
+// 32-row tiles per wave, sharing each x fragment.  One: two (half the LDS
+// reads of x per weight, 142 + 32 registers, half the workgroups) took the
+// Llama-3.2-3B-shaped layer at M = 32 from 39.2 to 44.2 us.
+constexpr int kSkTiles = 1;
+constexpr int kSkRows = 32 * kSkTiles;                     // W rows per wave
+constexpr int kSkSlot = kSkRows * kBlockBytes;             // one super-block of a wave's rows
+constexpr int kSkPieces = kSkSlot / 16;                    // 16-byte pieces of a slot
+constexpr int kSkLoads = (kSkPieces + 63) / 64;            // pieces per lane
+constexpr int kSkXBytes = 32 * kBlockWeights * 2;          // one super-block of x: 32 rows of binary16
+constexpr int kSkinnyMaxM = 32;
+struct SkinnyTile {  // the plan needs the tile's extent only
+    static constexpr int BM = 32, BN = kSkWaves * kSkRows;
+};
+// K chunks of at most four super-blocks (Llama-3.2-3B-shaped layer at
+// M = 32: 36.6 us, against 40.7 with six and 38.9 with eight; the larger
+// Qwen3-14B-shaped layer prefers eight, 89.2 against 93.6 us, but a rule by
+// batch size would make a problem's result depend on its batch).
+constexpr SplitRule kSkinnySplit = {4, 0};
+
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(Batch bt, GemmArgs ga) {
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][kSkXBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t wslot[kSkWaves][kSkSlot];
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+    const int tile = ga.xcd_first[xcd] + static_cast<int>(blockIdx.x) / kXcds;
+    if (tile >= ga.xcd_first[xcd + 1]) return;
+    const int p = find_problem(bt, tile);
+    const DevProblem P = load_problem(bt, p);
+    const _Float16 *__restrict__ XH = ga.xh[p];
+    const int N = P.N, K = P.K, M = bt.M;
+    const int KB = K >> 8;
+    const int splits = P.splits;
+    const int local = (tile - P.tile_begin) / splits;
+    const int sidx = tile - P.tile_begin - local * splits;
+    const int kb0 = sidx * KB / splits;
+    const int kbn = (sidx + 1) * KB / splits - kb0;  // >= 1
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int h = lane >> 5;  // k-half of each slice this lane feeds
+    const int n0 = local * SkinnyTile::BN + kSkRows * wave;  // this wave's first row
+
+    // Piece j of this lane: piece f = lane + 64 j of the wave's rows, bytes
+    // 16 * (f % 9) of row f / 9 (pieces past the slot re-read a valid piece
+    // and are not parked).  Row pointers already at kb0.
+    const uint8_t *wp[kSkLoads];
+    const size_t row_bytes = static_cast<size_t>(KB) * kBlockBytes;
+#pragma unroll
+    for (int j = 0; j < kSkLoads; ++j) {
+        const int f = min(lane + 64 * j, kSkPieces - 1);
+        const int v = min(n0 + f / 9, N - 1);
+        const uint8_t *base = P.w2 ? (pair_is_up(v) ? P.w2 : P.w) + static_cast<size_t>(pair_row(v, P.n_out)) * row_bytes
+                                   : P.w + static_cast<size_t>(v) * row_bytes;
+        wp[j] = base + static_cast<size_t>(kb0) * kBlockBytes + 16 * (f % 9);
+    }
+    auto ldw = [&](int b, u32x4s (&v)[kSkLoads]) {
+#pragma unroll
+        for (int j = 0; j < kSkLoads; ++j)
+            v[j] = *reinterpret_cast<const u32x4s *>(wp[j] + static_cast<size_t>(b) * kBlockBytes);
+    };
+    auto park = [&](const u32x4s (&v)[kSkLoads]) {
+        u32x4s *d = reinterpret_cast<u32x4s *>(wslot[wave]);
+#pragma unroll
+        for (int j = 0; j < kSkLoads; ++j)
+            if (kSkPieces % 64 == 0 || lane + 64 * j < kSkPieces) d[lane + 64 * j] = v[j];
+    };
+    // x of block b (1024 pieces of 16 bytes, 256 per wave) into buffer buf.
+    auto stage_x = [&](int b, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pos0 = 256 * wave + 64 * i;  // this instruction's first position
+            const int pos = pos0 + lane;
+            const int m = pos >> 5, c = (pos & 31) ^ (m & 15);
+            const _Float16 *src = XH + static_cast<size_t>(min(m, M - 1)) * K +
+                                  static_cast<size_t>(kb0 + b) * kBlockWeights + 8 * c;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src),
+                                             reinterpret_cast<uint4 *>(xbuf[buf] + 16 * pos0), 16, 0, 0);
+        }
+    };
+
+    float16v acc[kSkTiles];
+#pragma unroll
+    for (int tt = 0; tt < kSkTiles; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tt][r] = 0.f;
+    const int arow = lane & 31;  // A row (token) this lane feeds, and its W row in each tile
+    // One super-block from the wave's slot and x buffer xb: every x fragment
+    // is read once and multiplies the wave's tiles.
+    auto compute = [&](const uint8_t *xb) {
+        const uint4 *xa = reinterpret_cast<const uint4 *>(xb) + arow * 32;
+        const int sw = arow & 15;
+        RowScales rs[kSkTiles];
+#pragma unroll
+        for (int tt = 0; tt < kSkTiles; ++tt)
+            decode_header(*reinterpret_cast<const uint4 *>(wslot[wave] + (32 * tt + arow) * kBlockBytes), rs[tt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s0 = 4 * i;
+            const half8 x0 = __builtin_bit_cast(half8, xa[(2 * s0 + h) ^ sw]);
+            const half8 x1 = __builtin_bit_cast(half8, xa[(2 * s0 + 2 + h) ^ sw]);
+            const half8 x2 = __builtin_bit_cast(half8, xa[(2 * s0 + 4 + h) ^ sw]);
+            const half8 x3 = __builtin_bit_cast(half8, xa[(2 * s0 + 6 + h) ^ sw]);
+#pragma unroll
+            for (int tt = 0; tt < kSkTiles; ++tt) {
+                const uint8_t *row = wslot[wave] + (32 * tt + arow) * kBlockBytes;
+                const uint2 d0 = *reinterpret_cast<const uint2 *>(row + 16 + 32 * i + 8 * h);
+                const uint2 d1 = *reinterpret_cast<const uint2 *>(row + 32 + 32 * i + 8 * h);
+                const uint32_t scw = i < 2 ? rs[tt].scA : rs[tt].scB, mnw = i < 2 ? rs[tt].mnA : rs[tt].mnB;
+                const int sh = (i & 1) * 16;
+                const float a_lo = rs[tt].d * 16777216.0f * static_cast<float>((scw >> sh) & 0xFFu);
+                const float a_hi = rs[tt].d * 1048576.0f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
+                const float c_lo = rs[tt].dmin * static_cast<float>((mnw >> sh) & 0xFFu);
+                const float c_hi = rs[tt].dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
+                const WordWeights p0 = dequant_word(d0.x, a_lo, c_lo, a_hi, c_hi);
+                const WordWeights p1 = dequant_word(d0.y, a_lo, c_lo, a_hi, c_hi);
+                const WordWeights q0 = dequant_word(d1.x, a_lo, c_lo, a_hi, c_hi);
+                const WordWeights q1 = dequant_word(d1.y, a_lo, c_lo, a_hi, c_hi);
+                // slices 4i .. 4i+3: sub-block 2i (low nibbles) then 2i+1 (high), 16 k each
+                const half8 b0 = __builtin_bit_cast(half8, make_uint4(p0.lo01, p0.lo23, p1.lo01, p1.lo23));
+                const half8 b1 = __builtin_bit_cast(half8, make_uint4(q0.lo01, q0.lo23, q1.lo01, q1.lo23));
+                const half8 b2 = __builtin_bit_cast(half8, make_uint4(p0.hi01, p0.hi23, p1.hi01, p1.hi23));
+                const half8 b3 = __builtin_bit_cast(half8, make_uint4(q0.hi01, q0.hi23, q1.hi01, q1.hi23));
+                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, b0, acc[tt], 0, 0, 0);
+                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, b1, acc[tt], 0, 0, 0);
+                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x2, b2, acc[tt], 0, 0, 0);
+                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x3, b3, acc[tt], 0, 0, 0);
+            }
+        }
+    };
+    // Step b: park W(b) (its loads were requested a step earlier; parking
+    // frees the registers), publish x(b), request step b + 1 into the same
+    // registers, then multiply step b while step b + 1 is on its way.
+    u32x4s wr[kSkLoads];
+    stage_x(0, 0);
+    ldw(0, wr);
+    for (int b = 0; b < kbn; ++b) {
+        park(wr);
+        // x(b)'s global-to-LDS loads (requested before W(b)) have landed once
+        // every load of the wave is done; the barrier then publishes them, and
+        // every wave is past its multiply of step b - 1 (the other buffer).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (b + 1 < kbn) {
+            stage_x(b + 1, (b + 1) & 1);
+            ldw(b + 1, wr);
+        }
+        compute(xbuf[b & 1]);
+    }
+
+    // Store: D layout of a 32x32 MFMA tile, lane l, register r -> token
+    // 8*(r/4) + 4*(l/32) + r%4, W row (tile's first) + l%32.  x's per-row
+    // factor undone.
+    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
+    if (P.w2 && splits == 1) {
+        const int n_out = P.n_out;
+        const bool up = (lane & 16) != 0;
+#pragma unroll
+        for (int tt = 0; tt < kSkTiles; ++tt) {
+            const int n = ((n0 + 32 * tt) >> 1) + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int m0 = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const float v0 = acc[tt][r] * xfac[min(m0, M - 1)];
+                const float v1 = acc[tt][r + 1] * xfac[min(m0 + 1, M - 1)];
+                const float got = __shfl_xor(up ? v0 : v1, 16);
+                const int m = up ? m0 + 1 : m0;
+                if (m < M && n < n_out) P.y[static_cast<size_t>(m) * n_out + n] = up ? swiglu(got, v1) : swiglu(v0, got);
+            }
+        }
+        return;
+    }
+    float *dst = splits == 1 ? P.y : P.part + static_cast<size_t>(sidx) * M * N;
+#pragma unroll
+    for (int tt = 0; tt < kSkTiles; ++tt) {
+        const int n = n0 + 32 * tt + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < M && n < N) dst[static_cast<size_t>(m) * N + n] = acc[tt][r] * xfac[m];
+        }
+    }
+}
+
 // Launch plan of one tile shape: problems in order of decreasing K (the
 // longest tiles start first), their K splits, the tile space (each problem's
 // tiles back to back; the K chunks of an output tile adjacent, N tiles of
@@ -742,6 +954,8 @@ void make_plan(const Batch &b, SplitRule rule, Plan &pl) {
     pl.tiles = tiles;
 }
 
+hipError_t launch_split_sum(const Plan &pl, hipStream_t stream);
+
 // Launch one tile shape (after the binary16 copies of x are queued).
 template <class S, int WAVES_PER_EU>
 hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
@@ -762,6 +976,11 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
     hipLaunchKernelGGL((prefill_kernel<S, WAVES_PER_EU>), dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, sealed(pl.sb), ga);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.partial_floats == 0) return err;
+    return launch_split_sum(pl, stream);
+}
+
+// The second kernel of a split K: every split problem's chunks summed in order.
+hipError_t launch_split_sum(const Plan &pl, hipStream_t stream) {
     Batch red;
     red.count = 0;
     red.M = pl.sb.M;
@@ -777,6 +996,25 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
     }
     hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, sealed(red));
     return hipGetLastError();
+}
+
+// Launch the up-to-32-token kernel (after the binary16 copies of x are queued).
+hipError_t launch_skinny(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
+    if (pl.grid == 0) return hipSuccess;
+    GemmArgs ga;
+    for (int c = 0; c <= kXcds; ++c) ga.xcd_first[c] = pl.xcd_first[c];
+    for (int i = 0; i < pl.sb.count; ++i) {
+        DevProblem &d = pl.sb.p[i];
+        ga.xh[i] = xh[pl.order[i]];
+        if (d.splits > 1) {
+            d.part = part;
+            part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
+        }
+    }
+    hipLaunchKernelGGL(skinny_kernel, dim3(pl.grid), dim3(64 * kSkWaves), 0, stream, sealed(pl.sb), ga);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || pl.partial_floats == 0) return err;
+    return launch_split_sum(pl, stream);
 }
 
 }  // namespace
@@ -805,11 +1043,14 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     }
     // Few tokens: the W stream dominates, small tiles (K split as needed)
     // keep every CU busy.
-    const bool small = b.M <= kSmallTileMaxM;
+    const bool skinny = b.M <= kSkinnyMaxM;
+    const bool small = !skinny && b.M <= kSmallTileMaxM;
     Plan pl;
-    const bool mid = !small && b.M <= kMidTileMaxM;
+    const bool mid = !skinny && !small && b.M <= kMidTileMaxM;
     bool narrow = false;
-    if (small) {
+    if (skinny) {
+        make_plan<SkinnyTile>(b, kSkinnySplit, pl);
+    } else if (small) {
         make_plan<SmallTile>(b, kSmallSplit, pl);
         narrow = pl.tiles < kNarrowBelow;
         if (narrow) make_plan<NarrowTile>(b, kSmallSplit, pl);
@@ -838,11 +1079,22 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
         sg.row_begin = cblocks;
         cblocks += b.M;
     }
-    hipLaunchKernelGGL(convert_x_kernel, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
+    int max_k = 0;
+    for (int k = 0; k < nx; ++k) max_k = max(max_k, xk[k]);
+    const int regs = (max_k + 1023) / 1024;  // float4 per thread for the longest row
+    if (regs <= 4)
+        hipLaunchKernelGGL(convert_x_kernel<4>, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
+    else if (regs <= 8)
+        hipLaunchKernelGGL(convert_x_kernel<8>, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
+    else if (regs <= 12)
+        hipLaunchKernelGGL(convert_x_kernel<12>, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
+    else
+        hipLaunchKernelGGL(convert_x_kernel<18>, dim3(cblocks), dim3(kCvtThreads), 0, stream, cb);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
+    if (skinny) return launch_skinny(pl, xh, part, stream);
     if (narrow) return launch_gemm<NarrowTile, kSmallWaves>(pl, xh, part, stream);
     if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);

@@ -63,7 +63,10 @@ PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 204
                   (80, 300, 13056), (130, 70, 17408), (100, 300, 4352), (512, 64, 5120),
                   (65, 40, 768), (128, 257, 2048), (129, 64, 1024),
                   # more tokens: only rows longer than 48 blocks are cut
-                  (513, 40, 4352), (600, 33, 12544)]
+                  (513, 40, 4352), (600, 33, 12544),
+                  # up to 32 tokens: W dequantized straight into the MFMA operands, K in
+                  # chunks of four blocks (one block, a ragged last chunk, many chunks)
+                  (31, 1, 256), (20, 257, 4352), (25, 33, 8192), (18, 300, 1280), (32, 130, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)

@@ -27,12 +27,15 @@ def _inputs(M, N, K, tag):
 # One token and more than 16 tokens run the epilogue inside the product (tiles
 # of 16 gate rows and the same 16 up rows): (1, 8192, 2048) on four-wave,
 # (1, 1000, 8192) on sixteen-wave, (1, 17408, 5120) on eight-wave workgroups;
-# 32-row prefill tiles with K chunks summed by the second kernel (33, 64),
+# up to 32 tokens W straight into the MFMA operands, with K chunks summed by
+# the second kernel (20) or in one chunk (32); 32-row prefill tiles with K
+# chunks summed by the second kernel (33, 64),
 # 128x128 (100) and 256x256 tiles (300), and at 600 tokens a K of 13056 cut
 # into two chunks.  Ragged N (1000, 700, 301, 5, 1) leaves part of the last
 # tile unused.  2..16 tokens combine two products in a second kernel.
 @pytest.mark.parametrize("M,N,K", [(1, 8192, 2048), (1, 1000, 8192), (1, 17408, 5120), (1, 301, 768), (1, 1, 256),
                                    (4, 1000, 1024), (16, 3000, 512), (2, 5, 256),
+                                   (20, 301, 2304), (32, 100, 1024),
                                    (33, 700, 768), (64, 301, 2304), (100, 300, 512), (300, 1000, 1024),
                                    (600, 200, 13056)])
 def test_swiglu_against_products_and_oracle(M, N, K):
