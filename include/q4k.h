@@ -29,14 +29,25 @@
  *     enqueued.  The integer codes follow the convention of the
  *     nx_f32_llm_run_v3 source page (0 success, -1 null pointer, -2 bad
  *     dimension, -3 failure while running the forward), extended with -4..-6.
- *   - Calls are thread-safe; calls on different streams may run concurrently.
+ *   - Calls are thread-safe (the library's tables are guarded per device);
+ *     calls on different streams may run concurrently.
  *   - Workspace: the library keeps device scratch memory per (device, stream)
  *     for split-K partial sums, the binary16 copy of x (prefill) and the
  *     staged activations of 2 <= M <= 16 calls.  It grows on demand with
- *     hipMalloc, so a call whose shape needs more than any earlier call on
- *     that stream allocates; calls on one stream reuse it in stream order.
- *     Code that captures HIP graphs makes one eager call of each shape on the
- *     capture stream first.
+ *     hipMalloc (no synchronization), so a call whose shape needs more than
+ *     any earlier call on that stream allocates; calls on one stream reuse it
+ *     in stream order.  A buffer replaced by a larger one is never freed
+ *     (retired buffers stay allocated until the process ends, and sizes at
+ *     least double), so a HIP graph captured earlier on that stream keeps
+ *     valid memory.  Code that captures HIP graphs makes one eager call of
+ *     each shape on the capture stream first (no allocation inside a
+ *     capture), and does not replay such a graph concurrently with calls on
+ *     its capture stream (they share the workspace).  q4k_matmul_batched_noalloc
+ *     uses a fixed per-GPU array instead and allocates nothing.
+ *   - The stream handle is passed to the HIP runtime as given; a handle that
+ *     is not a live stream of the current device is undefined behaviour in
+ *     HIP itself and is not detected (a launch the runtime rejects returns
+ *     Q4K_ERR_LAUNCH).
  */
 #ifndef Q4K_H
 #define Q4K_H
@@ -87,8 +98,18 @@ typedef struct q4k_problem {
 
 /* `count` independent products that share M, run by one launch per kernel
  * family (for example the q, k, v, o, gate, up and down projections of one
- * layer).  `problems` is a HOST array that is only read during the call.
- * Problems may share x; no y may overlap any x, W or another y. */
+ * layer).  The rlx-qwen3 crate page ("Quick start") emits one DequantMatMul
+ * per packed projection; a layer's projections that read the same
+ * activations are independent products, batched here so that a decode step
+ * pays one launch per layer instead of seven.  `problems` is a HOST array
+ * (at most Q4K_MAX_BATCH entries) that is only read during the call.
+ * Problems may share x (also at different K: each reads its own M x K rows);
+ * no y may overlap any x, W or another y.  Each problem's result is the one
+ * q4k_matmul gives it alone (bit for bit, except that one-token problems may
+ * split their K over a different number of waves, which changes the last
+ * bits only).  Errors: as for q4k_matmul, checked for every problem before
+ * anything is enqueued; count outside [1, Q4K_MAX_BATCH] is Q4K_ERR_BAD_DIM
+ * and problems == NULL is Q4K_ERR_NULL. */
 int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_t stream);
 
 /* For callers that cannot allocate device memory: code under HIP graph
@@ -208,7 +229,10 @@ int q4k_matmul_batched_path(const q4k_problem *problems, int count, int M, int p
  * Q4K_PATH_PREFILL), or a negative error code for an invalid shape. */
 int q4k_select_path(int M, int N, int K);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL; "unknown status" for codes the
+ * library does not return).  The codes follow the integer status convention
+ * of the nx_f32_llm_run_v3 source page (0 success, -1 null pointer, -2 bad
+ * dimension, -3 failure while running), extended with -4 .. -9. */
 const char *q4k_strerror(int status);
 
 /* Library version as major*10000 + minor*100 + patch. */
