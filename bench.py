@@ -141,9 +141,11 @@ class Pass:
                 layer_events[li][1].record()
 
 
-def _capture(fn):
-    """A HIP graph of fn(stream) captured on a side stream (run once eagerly
-    there first, so the library's per-stream state exists before capture)."""
+def _capture(fn, repeat=1):
+    """A HIP graph of fn(stream), repeat times in a row, captured on a side
+    stream (run once eagerly there first, so the library's per-stream state
+    exists before capture).  Repeating short work inside one graph keeps the
+    host's per-replay launch cost out of a per-kernel figure."""
     import torch
     gs = torch.cuda.Stream()
     gs.wait_stream(torch.cuda.current_stream())
@@ -152,9 +154,22 @@ def _capture(fn):
         gs.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=gs):
-            fn(gs)
+            for _ in range(repeat):
+                fn(gs)
     torch.cuda.synchronize()
     return g
+
+
+# Launches per replay of a graph that times one kernel's average duration.
+LAUNCHES_PER_REPLAY = 128
+# Weights a timing graph cycles through before it reads one again: twice the
+# 256 MB last-level cache, so every launch reads its weights from HBM.
+ROTATE_BYTES = 512 << 20
+
+
+def _copies(nbytes):
+    """Copies of an nbytes working set that a timing graph rotates through."""
+    return max(1, -(-ROTATE_BYTES // nbytes))
 
 
 def _time_replays(g, steps, warmup):
@@ -177,8 +192,9 @@ def time_pass(ps, q4k, steps, warmup, graph=True):
 
     graph=True: both figures come from HIP-graph replays bracketed by HIP
     events on the replay stream: the whole pass, and the per-layer launches
-    alone (their time divided by the number of launches).  graph=False:
-    eager prepared calls, events around the pass and around every layer."""
+    alone, repeated in one graph to at least LAUNCHES_PER_REPLAY launches
+    (their time divided by the number of launches).  graph=False: eager
+    prepared calls, events around the pass and around every layer."""
     import torch
     ps.prepare(q4k)
     for _ in range(warmup):
@@ -187,8 +203,9 @@ def time_pass(ps, q4k, steps, warmup, graph=True):
     if graph:
         ms_step = _time_replays(_capture(lambda st: ps.run(st)), steps, warmup)
         nl = len(ps.layers)
-        layers_only = _capture(lambda st: [c(st) for c in ps.calls[:nl]])
-        ms_layer = _time_replays(layers_only, steps, warmup) / nl
+        rep = -(-LAUNCHES_PER_REPLAY // nl)
+        layers_only = _capture(lambda st: [c(st) for c in ps.calls[:nl]], rep)
+        ms_layer = _time_replays(layers_only, steps, warmup) / (nl * rep)
         return ms_step, ms_layer
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -238,9 +255,14 @@ def time_head_argmax(ps, q4k, steps, warmup):
     w, x, y = ps.head
     idx = torch.empty(ps.M, dtype=torch.int32, device=x.device)
     val = torch.empty(ps.M, dtype=torch.float32, device=x.device)
-    ms_logits = _time_replays(_capture(lambda st: q4k.matmul(w, x, y, stream=st)), steps, warmup)
-    ms_argmax = _time_replays(_capture(lambda st: q4k.matmul_argmax(w, x, index=idx, value=val, stream=st)),
-                              steps, warmup)
+    ws = [w] + [w.clone() for _ in range(_copies(w.numel()) - 1)]
+    n = len(ws) * -(-8 // len(ws))  # at least eight launches per replay, every copy as often
+    ms_logits = _time_replays(_capture(lambda st: [q4k.matmul(ws[i % len(ws)], x, y, stream=st)
+                                                   for i in range(n)]), steps, warmup) / n
+    ms_argmax = _time_replays(_capture(lambda st: [q4k.matmul_argmax(ws[i % len(ws)], x, index=idx, value=val,
+                                                                     stream=st) for i in range(n)]),
+                              steps, warmup) / n
+    del ws
     yh = y.cpu().numpy()
     first = np.argmax(yh, axis=1)
     if not (np.array_equal(idx.cpu().numpy(), first) and np.array_equal(val.cpu().numpy(), yh[np.arange(ps.M), first])):
@@ -400,6 +422,8 @@ def swiglu_figures(q4k, dev, steps, warmup):
     wg = torch.from_numpy(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 0, PROJ_ID["gate"]))).to(dev)
     wu = torch.from_numpy(qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, 0, PROJ_ID["up"]))).to(dev)
     out = {"shape": [N, K], "weight_bytes": 2 * N * K // 256 * 144}
+    # one-token timing rotates through copies of the pair (more than the last-level cache)
+    pairs = [(wg, wu)] + [(wg.clone(), wu.clone()) for _ in range(_copies(out["weight_bytes"]) - 1)]
     for M in (1, 1024):
         x = torch.from_numpy(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, wl.ident, M, 1000 + X_ROLE["gate"]))).to(dev)
         o = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -408,8 +432,12 @@ def swiglu_figures(q4k, dev, steps, warmup):
         prods = q4k.prepare_batched([(wg, x, g), (wu, x, u)])
         fused = lambda st: q4k.matmul_swiglu(wg, wu, x, out=o, stream=st)
         if M == 1:
-            ms_f = _time_replays(_capture(fused), steps, warmup)
-            ms_p = _time_replays(_capture(lambda st: prods(st)), steps, warmup)
+            n = len(pairs) * -(-32 // len(pairs))
+            ms_f = _time_replays(_capture(lambda st: [q4k.matmul_swiglu(*pairs[i % len(pairs)], x, out=o, stream=st)
+                                                      for i in range(n)]), steps, warmup) / n
+            cp = [q4k.prepare_batched([(a, x, g), (b, x, u)]) for a, b in pairs]
+            ms_p = _time_replays(_capture(lambda st: [cp[i % len(cp)](st) for i in range(n)]), steps, warmup) / n
+            del cp
         else:
             def eager(fn, reps=max(3, steps // 4)):
                 for _ in range(2):
@@ -435,6 +463,7 @@ def swiglu_figures(q4k, dev, steps, warmup):
             rec["TFLOPs"] = round(2 * M * 2 * N * K / (ms_f * 1e-3) / 1e12, 1)
         out[f"M{M}"] = rec
         del x, o, g, u, prods
+    del pairs
     return out
 
 
@@ -684,6 +713,7 @@ def main():
 
     if not args.no_prefill:
         out["prefill_m1024"], pp = prefill_pass(q4k, dev, wl, args.prefill_steps, weights_from=ps)
+        out["prefill_m1024"]["roofline"]["traffic"] = recorded_traffic("prefill_qwen3_14b_layer_m1024")
         del pp
         torch.cuda.empty_cache()
     if not args.no_others:
