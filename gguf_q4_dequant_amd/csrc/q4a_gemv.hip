@@ -3,7 +3,10 @@
 // include/q4a.h: the q4 QuantizedLinear weights of the mlx-rs pull request
 // #356 page, groups of 64).
 //
-// Decode-oriented GEMV on the vector units, fp32 throughout:
+// One token (M = 1) runs on the matrix cores when K is a multiple of 256
+// (q4a_wide_kernel below); every other case on the vector units.
+//
+// GEMV on the vector units, fp32 throughout:
 //   * A workgroup of four waves owns 8 rows of W.  Its 256 threads split the
 //     rows' K into 32-value half-groups (thread t takes half-groups t,
 //     t + 256, ...), so for K up to 8192 every thread requests all of its
@@ -137,6 +140,257 @@ __global__ __launch_bounds__(kThreads) void q4a_gemv_kernel(const uint8_t *__res
     }
 }
 
+// ---- one token on the matrix cores ----------------------------------------
+// Four groups (256 weights) of a row are 128 bytes of quants plus four scales
+// and four biases: 144 bytes, so a 32-row tile of them is parked in LDS like
+// a Q4_K super-block (q4k_decode_mma.hip), and the tile's waves split its
+// blocks as the one-token Q4_K kernel does.
+//   * B operand of v_mfma_f32_16x16x32_f16: a nibble masked into the low bits
+//     of a binary16 is the subnormal q * 2^-24 (exact, the matrix cores keep
+//     subnormals).  A word w holds elements 0..7 at bits 0, 4, ..., 28, so
+//     w & 0x000F000F is elements (0, 4), (w >> 8) & 0x000F000F elements (2, 6),
+//     and the masks 0x00F000F0 give elements (1, 5) and (3, 7) as 16q: two
+//     words make one 8-value fragment of each "plane" (order 0,4,2,6 of the
+//     first word then of the second; 1,5,3,7 likewise), and the two planes
+//     accumulate separately, the second scaled by 1/16 afterwards.
+//   * A operand: x split into binary16 hi = rn(x'), lo = rn(x' - hi), x' = x
+//     scaled by a power of two per block that puts its largest magnitude in
+//     [2^14, 2^15), staged per wave in the planes' order.
+//   * Two rows of W per MFMA: k-quarters 0, 1 carry 16 weights of row l%16
+//     of the tile, quarters 2, 3 the same weights of row 16 + l%16; A holds
+//     hi/lo in rows 0, 1 over quarters 0, 1 and in rows 4, 5 over quarters
+//     2, 3, zeros where the other row's weights sit.  Lane l < 32 then finds
+//     row l's hi and lo sums in C registers 0 and 1.
+//   * Per group: y += s * (sum_k x_k q_k) + b * (sum_k x_k), the two sums
+//     from the MFMAs and from the staged activations (factored form: its
+//     rounding scales with sum |x| (|s q| + |b|), not with sum |x w|).
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 32;                  // rows of W per tile
+constexpr int kBlkRow = 144;               // parked bytes of one row's block: 128 quants | 4 scales | 4 biases
+constexpr int kSlot = kTile * kBlkRow;     // one block of a tile
+constexpr int kWide = 16;                  // waves of the widest workgroup
+constexpr int kCus = 256;                  // MI355X compute units
+constexpr int kWideMaxGroups = 512;        // about two rounds of one workgroup per CU
+constexpr int kWideMaxK = 1 << 24;         // 32-bit offsets within a tile
+
+// Waves per tile: the power of two (at most waves) that leaves each wave two
+// blocks or fewer where possible.
+__host__ __device__ inline int tile_waves(int KB, int waves) {
+    int w = 1;
+    while (w < waves && 2 * w < KB) w *= 2;
+    return w;
+}
+
+// v of lane (lane ^ X) within each group of 32 lanes (ds_swizzle, bit mode).
+template <int X>
+__device__ __forceinline__ float swz(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (X << 10) | 0x1F));
+}
+
+// Lane col (of the 32 lanes of one block) stages word col of the block,
+// elements 8col .. 8col+7 (a, b), into the planes' fragments of block blk of
+// the wave's pair, xs[(((blk*4 + group)*4 + word pair)*2 + plane)*2 + hi/lo],
+// 8 bytes per word; sums of each group and the block's factor 2^(24-e).
+__device__ __forceinline__ void stage_block(const float4 a, const float4 b, int blk, int col, uint4 *xs,
+                                            float *sum_t, float *mul_t) {
+    const float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float mx = 0.f, sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mx = fmaxf(mx, fabsf(xv[i]));
+        sm += xv[i];
+    }
+    mx = fmaxf(mx, swz<1>(mx));
+    mx = fmaxf(mx, swz<2>(mx));
+    mx = fmaxf(mx, swz<4>(mx));
+    mx = fmaxf(mx, swz<8>(mx));
+    mx = fmaxf(mx, swz<16>(mx));
+    sm += swz<1>(sm);  // the eight words of a group
+    sm += swz<2>(sm);
+    sm += swz<4>(sm);
+    const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
+    int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
+    e = max(-103, min(127, e));
+    const float up = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    const float back = __uint_as_float(static_cast<uint32_t>(24 - e + 127) << 23);
+    _Float16 hv[8], lv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = xv[i] * up;
+        hv[i] = static_cast<_Float16>(v);
+        lv[i] = static_cast<_Float16>(v - static_cast<float>(hv[i]));
+    }
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    const int j = col >> 3, wp = (col >> 1) & 3;
+    uint8_t *base = reinterpret_cast<uint8_t *>(xs + ((blk * 4 + j) * 4 + wp) * 4) + 8 * (col & 1);
+    const half4 lh = {hv[0], hv[4], hv[2], hv[6]}, ll = {lv[0], lv[4], lv[2], lv[6]};
+    const half4 hh = {hv[1], hv[5], hv[3], hv[7]}, hl = {lv[1], lv[5], lv[3], lv[7]};
+    *reinterpret_cast<half4 *>(base) = lh;        // plane 0, hi
+    *reinterpret_cast<half4 *>(base + 16) = ll;   // plane 0, lo
+    *reinterpret_cast<half4 *>(base + 32) = hh;   // plane 1, hi
+    *reinterpret_cast<half4 *>(base + 48) = hl;   // plane 1, lo
+    if ((col & 7) == 0) sum_t[blk * 4 + j] = sm;
+    if (col == 0) mul_t[blk] = back;
+}
+
+// One parked block of 32 rows times the staged activations of block blk of
+// the pair; rb: this lane's quant bytes (its row, 16 bytes 16*(quarter & 1)
+// of each group), xa: its A fragments (staged, or the zero block).
+__device__ __forceinline__ void mma_block(const uint8_t *slot, const uint8_t *rb, const uint4 *xa, int lane, int blk,
+                                          float mul, const float *sum_t, float &acc) {
+    const uint4 sb = *reinterpret_cast<const uint4 *>(slot + (lane & 31) * kBlkRow + 128);  // lane's own row
+    const uint32_t sw[2] = {sb.x, sb.y}, bw[2] = {sb.z, sb.w};
+    float as = 0.f, ab = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(rb + 32 * j);
+        const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
+        const uint32_t s0 = v.x >> 8, s1 = v.y >> 8, s2 = v.z >> 8, s3 = v.w >> 8;
+        const uint4 bl0 = {v.x & LM, s0 & LM, v.y & LM, s1 & LM};
+        const uint4 bh0 = {v.x & HM, s0 & HM, v.y & HM, s1 & HM};
+        const uint4 bl1 = {v.z & LM, s2 & LM, v.w & LM, s3 & LM};
+        const uint4 bh1 = {v.z & HM, s2 & HM, v.w & HM, s3 & HM};
+        const uint4 *f = xa + (blk * 4 + j) * 16;
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        float4v cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f[0]),
+                                                            __builtin_bit_cast(half8, bl0), z, 0, 0, 0);
+        float4v ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f[2]),
+                                                            __builtin_bit_cast(half8, bh0), z, 0, 0, 0);
+        cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f[4]), __builtin_bit_cast(half8, bl1),
+                                                    cl, 0, 0, 0);
+        ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, f[6]), __builtin_bit_cast(half8, bh1),
+                                                    ch, 0, 0, 0);
+        const float r = __builtin_fmaf(ch[0] + ch[1], 0.0625f, cl[0] + cl[1]);  // sum x' q 2^-24
+        const int sh = 16 * (j & 1);
+        as = __builtin_fmaf(f16_bits(static_cast<uint16_t>(sw[j >> 1] >> sh)), r, as);
+        ab = __builtin_fmaf(f16_bits(static_cast<uint16_t>(bw[j >> 1] >> sh)), sum_t[blk * 4 + j], ab);
+    }
+    acc += __builtin_fmaf(mul, as, ab);
+}
+
+// WAVES = 16 (launches of about two rounds at most), 8 (longer launches of
+// long rows) or 4; each wave owns about two blocks of one 32-row tile, the
+// waves of a tile meet in LDS at the end.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(const uint8_t *__restrict__ wq,
+                                                           const uint16_t *__restrict__ sc,
+                                                           const uint16_t *__restrict__ bi,
+                                                           const float *__restrict__ x, float *__restrict__ y,
+                                                           int N, int K) {
+    __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kSlot];
+    __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][2 * 64];
+    __shared__ __attribute__((aligned(16))) uint4 xzero[2 * 64];  // the A fragments that must be zero
+    __shared__ float xsumw[WAVES][2 * 4];
+    __shared__ float xmulw[WAVES][2];
+    __shared__ float red[WAVES * 64];
+    static_assert(64 * WAVES >= 2 * 64, "one thread per zero fragment");
+    if (threadIdx.x < 2 * 64) xzero[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int KB = K >> 8, G = K >> 6;
+    const int wpt = tile_waves(KB, WAVES);
+    const int lg = __builtin_ctz(wpt);
+    const int T = WAVES >> lg;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int tl = wave >> lg, kw = wave & (wpt - 1);
+    const int n0 = (static_cast<int>(blockIdx.x) * T + tl) * kTile;
+    const bool active = n0 < N;
+
+    uint8_t *wst = wslots + wave * kSlot;
+    uint4 *xs = xsw[wave];
+    float *xsum = xsumw[wave];
+    float *xmul = xmulw[wave];
+
+    // Loads of one block: quant pieces f = lane + 64j (row f/8, 16 bytes
+    // 16*(f%8)), and 8 bytes of scales (lanes 0..31, row lane) or biases
+    // (lanes 32..63, row lane - 32).  Rows past N re-read the last row and
+    // are not stored.
+    const int nr = active ? N - 1 - n0 : 0;
+    const uint32_t qrow = static_cast<uint32_t>(K) >> 1;
+    const uint8_t *W = wq + static_cast<size_t>(active ? n0 : 0) * qrow;
+    uint32_t qoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = lane + 64 * j;
+        qoff[j] = static_cast<uint32_t>(min(f >> 3, nr)) * qrow + 16u * (f & 7);
+    }
+    const uint16_t *sbp = (half ? bi : sc) + static_cast<size_t>((active ? n0 : 0) + min(col, nr)) * G;
+    auto ldq = [&](int kb, int j) -> u32x4 {
+        const uint8_t *wb = W + static_cast<uint32_t>(kb) * 128u;  // uniform
+        return *reinterpret_cast<const u32x4 *>(wb + qoff[j]);
+    };
+    auto lds = [&](int kb) -> uint2 { return *reinterpret_cast<const uint2 *>(sbp + 4 * kb); };
+    auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, uint2 vs) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = lane + 64 * j;
+            const u32x4 v = j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3;
+            *reinterpret_cast<u32x4 *>(wst + (f >> 3) * kBlkRow + 16 * (f & 7)) = v;
+        }
+        *reinterpret_cast<uint2 *>(wst + col * kBlkRow + 128 + 8 * half) = vs;
+    };
+
+    const int c16 = lane & 15, quarter = lane >> 4;
+    const bool zero_lane = (c16 < 2 && quarter >= 2) || ((c16 == 4 || c16 == 5) && quarter < 2);
+    const uint4 *xfrag = zero_lane ? xzero : xs + 8 * (quarter & 1) + (c16 & 1);
+    const uint8_t *rb = wst + (c16 + 16 * (quarter >> 1)) * kBlkRow + 16 * (quarter & 1);
+
+    float acc = 0.f;
+    // This wave's blocks kb = kw + wpt * i, in pairs, everything of a pair
+    // requested at once (activations: lanes 0..31 the first block, 32..63
+    // the second).
+    const int nb = active && KB > kw ? (KB - kw + wpt - 1) >> lg : 0;
+    for (int i0 = 0; i0 < nb; i0 += 2) {
+        const int bi_ = min(i0 + half, nb - 1);  // a lone last block is staged twice
+        const float4 *src = reinterpret_cast<const float4 *>(x + static_cast<size_t>(kw + wpt * bi_) * 256 + 8 * col);
+        const float4 xa = src[0], xb = src[1];
+        const int kb0 = kw + wpt * i0, kb1 = kw + wpt * min(i0 + 1, nb - 1);
+        const u32x4 a0 = ldq(kb0, 0), a1 = ldq(kb0, 1), a2 = ldq(kb0, 2), a3 = ldq(kb0, 3);
+        const uint2 as = lds(kb0);
+        const u32x4 b0 = ldq(kb1, 0), b1 = ldq(kb1, 1), b2 = ldq(kb1, 2), b3 = ldq(kb1, 3);
+        const uint2 bs = lds(kb1);
+        stage_block(xa, xb, half, col, xs, xsum, xmul);
+        park(a0, a1, a2, a3, as);
+        mma_block(wst, rb, xfrag, lane, 0, xmul[0], xsum, acc);
+        if (i0 + 1 < nb) {
+            park(b0, b1, b2, b3, bs);  // after the reads above, in program order
+            mma_block(wst, rb, xfrag, lane, 1, xmul[1], xsum, acc);
+        }
+    }
+
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (active && kw == 0 && half == 0) {  // lane l < 32 owns row n0 + l
+        float v = 0.f;
+        for (int j = 0; j < wpt; ++j) v += red[(tl * wpt + j) * 64 + lane];
+        const int n = n0 + col;
+        if (n < N) y[n] = v;
+    }
+}
+
+// Workgroup size for one token: as for the one-token Q4_K launches.
+int wide_waves(int N, int KB) {
+    const int tiles = (N + kTile - 1) / kTile;
+    const int T16 = kWide / tile_waves(KB, kWide);
+    const int g16 = (tiles + T16 - 1) / T16;
+    if (g16 <= kWideMaxGroups) return g16 < kCus && tile_waves(KB, kWide) <= 4 ? 4 : kWide;
+    return KB > 8 ? 8 : 4;
+}
+
+template <int WAVES>
+void launch_wide(const uint8_t *wq, const uint16_t *sc, const uint16_t *bi, const float *x, float *y, int N, int K,
+                 hipStream_t stream) {
+    const int T = WAVES / tile_waves(K >> 8, WAVES);
+    const int tiles = (N + kTile - 1) / kTile;
+    hipLaunchKernelGGL(q4a_wide_kernel<WAVES>, dim3((tiles + T - 1) / T), dim3(64 * WAVES), 0, stream, wq, sc, bi, x,
+                       y, N, K);
+}
+
 }  // namespace
 }  // namespace q4k
 
@@ -151,11 +405,20 @@ extern "C" int q4a_matmul(const void *w_q, const void *scales, const void *biase
         return Q4K_ERR_ALIGN;
     const int dev_rc = q4k::check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
-    const int MT = M == 1 ? 1 : 2;
-    const dim3 grid((N + q4k::kRows - 1) / q4k::kRows, (M + MT - 1) / MT);
     const auto *wq = static_cast<const uint8_t *>(w_q);
     const auto *sc = static_cast<const uint16_t *>(scales);
     const auto *bi = static_cast<const uint16_t *>(biases);
+    if (M == 1 && K % 256 == 0 && K <= q4k::kWideMaxK &&
+        ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) & 7u) == 0) {
+        switch (q4k::wide_waves(N, K >> 8)) {
+            case 4: q4k::launch_wide<4>(wq, sc, bi, x, y, N, K, stream); break;
+            case 8: q4k::launch_wide<8>(wq, sc, bi, x, y, N, K, stream); break;
+            default: q4k::launch_wide<q4k::kWide>(wq, sc, bi, x, y, N, K, stream); break;
+        }
+        return hipGetLastError() == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+    }
+    const int MT = M == 1 ? 1 : 2;
+    const dim3 grid((N + q4k::kRows - 1) / q4k::kRows, (M + MT - 1) / MT);
     if (MT == 1)
         hipLaunchKernelGGL(q4k::q4a_gemv_kernel<1>, grid, dim3(q4k::kThreads), 0, stream, wq, sc, bi, x, y, M, N, K);
     else

@@ -13,9 +13,17 @@
  *   w[n, k] = s[n, k/64] * q[n, k] + b[n, k/64]
  *
  * and the product is y[m, n] = sum_k x[m, k] * w[n, k], as for Q4_K (q4k.h).
- * Each weight is formed once in fp32 by a fused multiply-add (the exact
- * weight rounded once) and the sum is accumulated in fp32, so a group whose
- * terms cancel (s*q == -b) contributes exactly zero.
+ * Two evaluations:
+ *   - one token (M == 1) with K a multiple of 256 and scales, biases 8-byte
+ *     aligned: on the matrix cores, per group s * (sum_k x_k q_k) +
+ *     b * (sum_k x_k), with x split into two binary16 values scaled by a
+ *     power of two per 256 k (the one-token Q4_K scheme: about 22
+ *     significant bits relative to the largest |x| of each 256-block); its
+ *     rounding scales with sum_k |x_k| (|s q_k| + |b|), not sum_k |x_k w_k|;
+ *   - otherwise: each weight formed once in fp32 by a fused multiply-add (the
+ *     exact weight rounded once) and the sum accumulated in fp32, so a group
+ *     whose terms cancel (s*q == -b) contributes exactly zero.
+ * One-hot activations return the weights rounded once to f32 on both.
  */
 #ifndef Q4A_H
 #define Q4A_H
@@ -34,8 +42,8 @@ extern "C" {
  *   y: DEVICE float32 [M, N], both 16-byte aligned; y is overwritten and must
  *   not overlap the inputs.  Same stream, ownership and no-sync rules as
  *   q4k_matmul.
- *   The kernel streams W once per two tokens (it is meant for decoding, where
- *   M is small); any M is accepted.
+ *   W is streamed once per token (one token) or per two tokens (it is meant
+ *   for decoding, where M is small); any M is accepted.
  *   Errors: M, N or K negative, or K not a positive multiple of 64 when M and
  *   N are positive: Q4K_ERR_BAD_DIM; a NULL pointer: Q4K_ERR_NULL; alignment:
  *   Q4K_ERR_ALIGN; no gfx950 device: Q4K_ERR_DEVICE; launch failure:

@@ -264,6 +264,20 @@ def q4a_dequant(q, scales, biases, K: int) -> np.ndarray:
     return out
 
 
+def q4a_factored_abs(q, scales, biases, K: int) -> np.ndarray:
+    """[N, K] doubles |s*q| + |b| per weight: the magnitude of the two terms whose
+    sum is the weight (>= |w|, equal where they share a sign or either is 0).  A
+    product evaluated as s*(sum x*q) + b*(sum x) rounds in proportion to
+    sum_k |x_k| * q4a_factored_abs[n, k], its error scale."""
+    qb, sc, bi = _q4a_arrays(q, scales, biases, K)
+    words = qb.view("<u4").reshape(qb.shape[0], K // 8)
+    k = np.arange(K)
+    quant = ((words[:, k // 8] >> (4 * (k % 8)).astype(np.uint32)) & 15).astype(np.float64)
+    s = sc.view("<f2").astype(np.float64)[:, k // Q4A_GROUP]
+    b = bi.view("<f2").astype(np.float64)[:, k // Q4A_GROUP]
+    return np.abs(s * quant) + np.abs(b)
+
+
 def q4a_matmul_cols(q, scales, biases, x, N: int, K: int, cols, threads: int = 0):
     """(y, s) of the q4a product restricted to the W rows in cols: [M, len(cols)]."""
     q, sc, bi = _q4a_arrays(q, scales, biases, K)

@@ -157,3 +157,47 @@ def test_generator_fields():
     nib = (q.view(np.uint8)[..., None] >> np.array([0, 4], np.uint8)) & 15
     counts = np.bincount(nib.ravel(), minlength=16)
     assert counts.min() > 0.8 * counts.mean()
+
+
+# |s*q| + |b| of the hand-derived groups, worked out by hand from their fields.
+FACTORED = {
+    "ramp": lambda k: Fraction(k % 16, 2) + 3,
+    "cancel": lambda k: Fraction(4),
+    "subnormal": lambda k: Fraction(15, 2 ** 24) + Fraction(1, 2 ** 14),
+    "wide": lambda k: Fraction(65504) + Fraction(1, 2 ** 24),
+    "alternate": lambda k: Fraction(9 * (k % 2), 64) + Fraction(1, 4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_factored_magnitude_of_hand_derived_groups(name):
+    """q4a_factored_abs (the error scale of a product evaluated as
+    s*sum(x*q) + b*sum(x)) on the hand-derived groups, exactly."""
+    words, sb, bb, _ = CASES[name]
+    q, s, b = _group(words, sb, bb)
+    got = oracle.q4a_factored_abs(q, s, b, 64)[0]
+    assert [Fraction(float(v)) for v in got] == [FACTORED[name](k) for k in range(64)]
+
+
+def test_factored_magnitude_bounds_the_weight():
+    """|s*q| + |b| >= |s*q + b| everywhere, with equality exactly where s*q and
+    b do not have opposite signs; every quant bit moves its own entry."""
+    q, s, b = qi.random_q4a(24, 512, seed=981)
+    s[3, 2] = np.float16(-0.01)  # a negative scale too
+    b[5, 1] = np.float16(0.0)
+    fa = oracle.q4a_factored_abs(q, s, b, 512)
+    w = oracle.q4a_dequant_exact(q, s, b, 512)
+    assert np.all(fa >= np.abs(w))
+    k = np.arange(512)
+    sq = w - b.astype(np.float64)[:, k // 64]  # s*q, exact in double
+    same = sq * b.astype(np.float64)[:, k // 64] >= 0
+    assert np.array_equal(fa == np.abs(w), same)
+    q0, s1, b0 = _group([0] * 8, 0x3C00, 0x0000)  # s = 1, b = 0: |s q| + |b| = q
+    for j in (0, 7):
+        for e in (0, 5):
+            for i in range(4):
+                qq = q0.copy()
+                qq[0, j] = np.uint32(1 << (4 * e + i))
+                want = np.zeros(64)
+                want[8 * j + e] = 2 ** i
+                assert np.array_equal(oracle.q4a_factored_abs(qq, s1, b0, 64)[0], want), (j, e, i)

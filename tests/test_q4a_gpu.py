@@ -1,8 +1,13 @@
 """GPU parity of the affine 4-bit group format (q4a_matmul, include/q4a.h)
-against the oracle: element by element within 1e-5 * sum|x*w| (fp32
-arithmetic on exact weights), one-hot activations returning the f32 weights
-bit for bit, groups whose terms cancel returning exactly zero, and the
-full-size Qwen3-14B-shaped layer on sampled columns."""
+against the oracle: element by element within 1e-5 * S, one-hot activations
+returning the f32 weights bit for bit, groups whose terms cancel returning
+exactly zero on the fp32 path, and the full-size Qwen3-14B-shaped layer on
+sampled columns.
+
+S is sum|x*w| for the fp32 path (each weight formed exactly and rounded once)
+and sum |x| (|s*q| + |b|) for one token with K a multiple of 256, which runs
+on the matrix cores in the factored form s*sum(x*q) + b*sum(x)
+(oracle.q4a_factored_abs)."""
 import numpy as np
 import pytest
 
@@ -19,6 +24,15 @@ def _dev(q, s, b):
     return to_dev(q), to_dev(s), to_dev(b)
 
 
+def _scale(q, s, b, x, K, S, cols=None):
+    """The error scale of the path that q4a_matmul takes for x (see above)."""
+    if x.shape[0] != 1 or K % 256 != 0:
+        return S
+    rows = slice(None) if cols is None else cols
+    fa = oracle.q4a_factored_abs(q[rows], s[rows], b[rows], K)
+    return np.abs(x.astype(np.float64)) @ fa.T
+
+
 def _run(q, s, b, x):
     import torch
     y = q4k.q4a_matmul(*_dev(q, s, b), to_dev(x))
@@ -29,8 +43,13 @@ def _run(q, s, b, x):
 # Ragged N (1, 31, 33, 257: the last 32-row workgroup partly idle), K from a
 # single group to 128 groups (lanes of a wave with and without a second and
 # third half-group), one and two tokens per grid row, odd M.
+# One token with K a multiple of 256 takes the matrix-core kernel: 32-row
+# tiles split over 4 waves (2048: 3 tiles, N=33 ragged; 1024 x 4096 with a
+# lone last block per wave), 8 waves (5120, 17408) or 16 (N=96 x 8192 fits
+# two rounds), and the rest the fp32 kernel (K = 64, 128, 192, 640; M > 1).
 SHAPES = [(1, 1, 64), (1, 31, 128), (1, 33, 2048), (1, 1000, 5120), (2, 100, 1024), (3, 70, 192),
-          (5, 257, 4096), (16, 64, 8192), (33, 40, 640), (1, 96, 17408)]
+          (5, 257, 4096), (16, 64, 8192), (33, 40, 640), (1, 96, 17408), (1, 1, 256), (1, 1024, 4096),
+          (1, 96, 8192), (1, 40, 640), (1, 200, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -39,7 +58,7 @@ def test_q4a_matches_oracle(M, N, K):
     x = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 971, M, N, K))
     y = _run(q, s, b, x)
     y_ref, S = oracle.q4a_matmul(q, s, b, x, N, K)
-    check_close(y, y_ref, S, DECODE_TOL, f"q4a M={M} N={N} K={K}")
+    check_close(y, y_ref, _scale(q, s, b, x, K, S), DECODE_TOL, f"q4a M={M} N={N} K={K}")
 
 
 @pytest.mark.parametrize("M", [1, 8])
@@ -84,7 +103,26 @@ def test_q4a_qwen3_14b_layer_shapes(name):
     y = _run(q, s, b, x)
     cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N).integers(0, N, 200)]))
     y_ref, S = oracle.q4a_matmul_cols(q, s, b, x, N, K, cols)
-    check_close(y[:, cols], y_ref, S, DECODE_TOL, f"q4a {name}")
+    check_close(y[:, cols], y_ref, _scale(q, s, b, x, K, S, cols), DECODE_TOL, f"q4a {name}")
+
+
+def test_q4a_one_token_cancelling_rows_and_wide_range():
+    """One token on the matrix cores: rows whose weights all cancel (s = 1,
+    b = -2, q = 2) land within the factored bound of zero, and activations
+    spread over 2^-20 .. 2^20 (each block scaled by its own power of two)
+    stay within 1e-5 * S_f."""
+    N, K = 96, 2048
+    q, s, b = qi.random_q4a(N, K, seed=978)
+    q[5, :] = 0x22222222
+    s[5, :] = np.float16(1.0)
+    b[5, :] = np.float16(-2.0)
+    x = qi.random_x(1, K, seed=979)
+    x *= np.float32(2.0) ** np.linspace(-20, 20, K).astype(np.int32).astype(np.float32)
+    y = _run(q, s, b, x)
+    y_ref, S = oracle.q4a_matmul(q, s, b, x, N, K)
+    sf = _scale(q, s, b, x, K, S)
+    assert y_ref[0, 5] == 0 and abs(y[0, 5]) <= DECODE_TOL * sf[0, 5]
+    check_close(y, y_ref, sf, DECODE_TOL, "one token, wide range")
 
 
 def test_q4a_errors_leave_y_untouched_and_weights_unchanged():
