@@ -685,11 +685,13 @@ __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
 //     l / 32 of each 16-deep slice.  Packed bytes through LDS are a quarter
 //     of binary16 weights.
 //   * x: the binary16 copy (scaled per row, see above), one super-block of all
-//     32 token rows per step, moved by 16-byte global-to-LDS loads with no
-//     registers held (row m's 16-byte chunk c at position 32m + (c ^ (m & 15)),
-//     so each group of 16 lanes reading one chunk of 16 rows hits distinct
-//     banks), double-buffered: step b + 1's x and W are requested before step
-//     b's MFMAs.
+//     32 token rows per step, through registers into one of two LDS buffers
+//     (row m's 16-byte chunk c at position 32m + (c ^ (m & 15)), so each
+//     group of 16 lanes reading one chunk of 16 rows hits distinct banks):
+//     step b + 1's x and W are requested before step b's MFMAs and stay in
+//     flight through them.  W requested two steps ahead (a second register
+//     set, loads past the end clamped) was slower: 38.2-38.8 against 36.9 us
+//     on the Llama-3.2-3B-shaped layer.
 //   * Partial tiles of split K are summed by split_sum_kernel, as for the other
 //     tiles.  Rows of x past M re-read row M - 1 and are never stored.
 constexpr int kSkWaves = 4;
@@ -714,7 +716,8 @@ constexpr SplitRule kSkinnySplit = {4, 0};
 
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(Batch bt, GemmArgs ga) {
+__global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(3)))  // at most 168 VGPRs
+void skinny_kernel(Batch bt, GemmArgs ga) {
     __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][kSkXBytes];
     __shared__ __attribute__((aligned(16))) uint8_t wslot[kSkWaves][kSkSlot];
     const int xcd = static_cast<int>(blockIdx.x) % kXcds;
@@ -760,18 +763,23 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(Batch bt, GemmArg
         for (int j = 0; j < kSkLoads; ++j)
             if (kSkPieces % 64 == 0 || lane + 64 * j < kSkPieces) d[lane + 64 * j] = v[j];
     };
-    // x of block b (1024 pieces of 16 bytes, 256 per wave) into buffer buf.
-    auto stage_x = [&](int b, int buf) {
+    // x of block b: 1024 pieces of 16 bytes, four per thread, through
+    // registers (position pos = 256*wave + 64*i + lane holds row m = pos/32,
+    // chunk (pos % 32) ^ (m % 16)).  (Moved by global-to-LDS loads instead,
+    // the compiler cannot tell the next step's copy from the current step's
+    // reads and waits for every load of the wave before the multiply.)
+    auto ldx = [&](int b, u32x4s (&v)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int pos0 = 256 * wave + 64 * i;  // this instruction's first position
-            const int pos = pos0 + lane;
+            const int pos = 256 * wave + 64 * i + lane;
             const int m = pos >> 5, c = (pos & 31) ^ (m & 15);
-            const _Float16 *src = XH + static_cast<size_t>(min(m, M - 1)) * K +
-                                  static_cast<size_t>(kb0 + b) * kBlockWeights + 8 * c;
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src),
-                                             reinterpret_cast<uint4 *>(xbuf[buf] + 16 * pos0), 16, 0, 0);
+            v[i] = *reinterpret_cast<const u32x4s *>(XH + static_cast<size_t>(min(m, M - 1)) * K +
+                                                     static_cast<size_t>(kb0 + b) * kBlockWeights + 8 * c);
         }
+    };
+    auto stx = [&](const u32x4s (&v)[4], int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4s *>(xbuf[buf])[256 * wave + 64 * i + lane] = v[i];
     };
 
     float16v acc[kSkTiles];
@@ -823,21 +831,21 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(Batch bt, GemmArg
             }
         }
     };
-    // Step b: park W(b) (its loads were requested a step earlier; parking
-    // frees the registers), publish x(b), request step b + 1 into the same
-    // registers, then multiply step b while step b + 1 is on its way.
+    // Step b: store x(b) and park W(b) (both requested a step earlier;
+    // storing frees their registers), publish them, request step b + 1 into
+    // the same registers, then multiply step b while step b + 1 is on its way.
+    // The barrier also means every wave is past its multiply of step b - 1,
+    // which read the other x buffer.
     u32x4s wr[kSkLoads];
-    stage_x(0, 0);
+    u32x4s xr[4];
+    ldx(0, xr);
     ldw(0, wr);
     for (int b = 0; b < kbn; ++b) {
+        stx(xr, b & 1);
         park(wr);
-        // x(b)'s global-to-LDS loads (requested before W(b)) have landed once
-        // every load of the wave is done; the barrier then publishes them, and
-        // every wave is past its multiply of step b - 1 (the other buffer).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (b + 1 < kbn) {
-            stage_x(b + 1, (b + 1) & 1);
+            ldx(b + 1, xr);
             ldw(b + 1, wr);
         }
         compute(xbuf[b & 1]);
