@@ -49,7 +49,7 @@ PATH_GEMV = 3
 
 # Exported symbols of libq4k.so, as declared in include/q4k.h.
 EXPORTED = ("q4k_matmul", "q4k_matmul_batched", "q4k_matmul_path", "q4k_matmul_batched_path",
-            "q4k_matmul_batched_noalloc", "q4a_matmul",
+            "q4k_matmul_batched_noalloc", "q4a_matmul", "q4a_matmul_batched",
             "q4k_matmul_argmax", "q4k_matmul_swiglu", "q4k_gguf_list", "q4k_select_path", "q4k_strerror",
             "q4k_version")
 
@@ -99,6 +99,8 @@ def library() -> ctypes.CDLL:
     lib.q4k_matmul_swiglu.restype = ci
     lib.q4a_matmul.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
     lib.q4a_matmul.restype = ci
+    lib.q4a_matmul_batched.argtypes = [ctypes.POINTER(_QaProblem), ci, ci, vp]
+    lib.q4a_matmul_batched.restype = ci
     lib.q4k_gguf_list.argtypes = [ctypes.c_char_p, ctypes.POINTER(GgufTensor), ci, ctypes.POINTER(ci)]
     lib.q4k_gguf_list.restype = ci
     lib.q4k_select_path.argtypes = [ci, ci, ci]
@@ -340,10 +342,9 @@ def raw_matmul_batched_noalloc(items: Iterable[Tuple[int, int, int, int, int]], 
 Q4A_GROUP = 64
 
 
-def q4a_matmul(w_q, scales, biases, x, y=None, stream=None):
-    """y[M, N] = x[M, K] . dequant(W)^T for W in the affine 4-bit group layout
-    of include/q4a.h: w_q uint32 [N, K/8] (or uint8 [N, K/2]), scales and
-    biases float16 [N, K/64], w = s * q + b per group of 64."""
+def _q4a_checked(w_q, scales, biases, x, y):
+    """Validate one q4a product's tensors (shapes, dtypes, device, contiguity);
+    returns (y, M, N, K) with y allocated if None."""
     import torch
     if x.dtype != torch.float32 or x.dim() != 2:
         raise TypeError("x must be float32 [M, K]")
@@ -367,11 +368,59 @@ def q4a_matmul(w_q, scales, biases, x, y=None, stream=None):
             raise ValueError(f"{name} must be a device tensor on {x.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    return y, M, N, K
+
+
+def q4a_matmul(w_q, scales, biases, x, y=None, stream=None):
+    """y[M, N] = x[M, K] . dequant(W)^T for W in the affine 4-bit group layout
+    of include/q4a.h: w_q uint32 [N, K/8] (or uint8 [N, K/2]), scales and
+    biases float16 [N, K/64], w = s * q + b per group of 64."""
+    y, M, N, K = _q4a_checked(w_q, scales, biases, x, y)
     rc = library().q4a_matmul(w_q.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(), y.data_ptr(),
                               M, N, K, _stream_handle(stream))
     if rc != OK:
         raise Q4KError(rc, "q4a_matmul")
     return y
+
+
+class _QaProblem(ctypes.Structure):
+    _fields_ = [("w_q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
+
+def q4a_matmul_batched(problems, stream=None):
+    """Several q4a products sharing M in one call (q4a_matmul_batched):
+    problems is a list of (w_q, scales, biases, x, y) with y preallocated
+    float32 [M, N_i]; returns the list of y."""
+    problems = list(problems)
+    if not 1 <= len(problems) <= MAX_BATCH:
+        raise Q4KError(ERR_BAD_DIM, f"{len(problems)} problems")
+    arr = (_QaProblem * len(problems))()
+    Ms = set()
+    ys = []
+    for i, (w_q, scales, biases, x, y) in enumerate(problems):
+        if y is None:
+            raise ValueError("batched q4a products need their y tensors")
+        y, M, N, K = _q4a_checked(w_q, scales, biases, x, y)
+        Ms.add(M)
+        arr[i] = _QaProblem(w_q.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(), y.data_ptr(), N, K)
+        ys.append(y)
+    if len(Ms) != 1:
+        raise ValueError("every problem of a batch has the same M")
+    rc = library().q4a_matmul_batched(arr, len(problems), Ms.pop(), _stream_handle(stream))
+    if rc != OK:
+        raise Q4KError(rc, "q4a_matmul_batched")
+    return ys
+
+
+def raw_q4a_matmul_batched(items, M: int, stream: Optional[int] = None) -> int:
+    """Direct C-ABI call of q4a_matmul_batched; items are (wq_ptr, s_ptr,
+    b_ptr, x_ptr, y_ptr, N, K); returns the status."""
+    items = list(items)
+    arr = (_QaProblem * max(len(items), 1))()
+    for i, (w, sc, bi, x, y, n, k) in enumerate(items):
+        arr[i] = _QaProblem(w, sc, bi, x, y, n, k)
+    return library().q4a_matmul_batched(arr, len(items), M, stream)
 
 
 def raw_q4a_matmul(wq_ptr: int, s_ptr: int, b_ptr: int, x_ptr: int, y_ptr: int, M: int, N: int, K: int,

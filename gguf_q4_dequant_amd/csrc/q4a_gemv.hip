@@ -19,6 +19,8 @@
 //     weight rounded once, and then multiplies up to two tokens' x.
 //   * Per row and token the 256 partial sums meet by xor shuffles within each
 //     wave and through LDS across the four waves, in a fixed order.
+#include <limits.h>
+
 #include "../../include/q4a.h"
 #include "q4k_internal.h"
 
@@ -184,6 +186,34 @@ __host__ __device__ inline int tile_waves(int KB, int waves) {
     return w;
 }
 
+// One product of a one-token launch; workgroups tile_begin .. of the launch
+// are its own.
+struct QaProblem {
+    const uint8_t *wq;
+    const uint16_t *sc;
+    const uint16_t *bi;
+    const float *x;
+    float *y;
+    int N, K;
+    int tile_begin;
+};
+// Passed by value in the kernel-argument segment; tb[] repeats tile_begin
+// (INT_MAX past count) for find_problem.
+struct QaBatch {
+    int tb[kMaxBatch];
+    QaProblem p[kMaxBatch];
+    int count;
+};
+static_assert(sizeof(QaBatch) < 4096, "kernel-argument segment");
+
+// The problem's fields, requested together, read as the fields they are (so
+// the pointers stay global-memory pointers to the compiler).
+__device__ __forceinline__ QaProblem load_qa_problem(const QaBatch &qb, int p) {
+    const QaProblem P = qb.p[p];
+    asm volatile("" ::"s"(P.wq), "s"(P.sc), "s"(P.bi), "s"(P.x), "s"(P.y), "s"(P.N), "s"(P.K), "s"(P.tile_begin));
+    return P;
+}
+
 // v of lane (lane ^ X) within each group of 32 lanes (ds_swizzle, bit mode).
 template <int X>
 __device__ __forceinline__ float swz(float v) {
@@ -275,11 +305,7 @@ __device__ __forceinline__ void mma_block(const uint8_t *slot, const uint8_t *rb
 // long rows) or 4; each wave owns about two blocks of one 32-row tile, the
 // waves of a tile meet in LDS at the end.
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(const uint8_t *__restrict__ wq,
-                                                           const uint16_t *__restrict__ sc,
-                                                           const uint16_t *__restrict__ bi,
-                                                           const float *__restrict__ x, float *__restrict__ y,
-                                                           int N, int K) {
+__global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(QaBatch qb) {
     __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kSlot];
     __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][2 * 64];
     __shared__ __attribute__((aligned(16))) uint4 xzero[2 * 64];  // the A fragments that must be zero
@@ -289,6 +315,14 @@ __global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(const uint8_t *__r
     static_assert(64 * WAVES >= 2 * 64, "one thread per zero fragment");
     if (threadIdx.x < 2 * 64) xzero[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
+    const int g = static_cast<int>(blockIdx.x);
+    const QaProblem P = load_qa_problem(qb, find_problem(qb, g));
+    const uint8_t *__restrict__ wq = P.wq;
+    const uint16_t *__restrict__ sc = P.sc;
+    const uint16_t *__restrict__ bi = P.bi;
+    const float *__restrict__ x = P.x;
+    float *__restrict__ y = P.y;
+    const int N = P.N, K = P.K;
     const int KB = K >> 8, G = K >> 6;
     const int wpt = tile_waves(KB, WAVES);
     const int lg = __builtin_ctz(wpt);
@@ -298,7 +332,7 @@ __global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(const uint8_t *__r
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int tl = wave >> lg, kw = wave & (wpt - 1);
-    const int n0 = (static_cast<int>(blockIdx.x) * T + tl) * kTile;
+    const int n0 = ((g - P.tile_begin) * T + tl) * kTile;
     const bool active = n0 < N;
 
     uint8_t *wst = wslots + wave * kSlot;
@@ -373,29 +407,62 @@ __global__ __launch_bounds__(64 * WAVES) void q4a_wide_kernel(const uint8_t *__r
     }
 }
 
-// Workgroup size for one token: as for the one-token Q4_K launches.
-int wide_waves(int N, int KB) {
-    const int tiles = (N + kTile - 1) / kTile;
-    const int T16 = kWide / tile_waves(KB, kWide);
-    const int g16 = (tiles + T16 - 1) / T16;
-    if (g16 <= kWideMaxGroups) return g16 < kCus && tile_waves(KB, kWide) <= 4 ? 4 : kWide;
-    return KB > 8 ? 8 : 4;
+// Workgroup size for one token: as for the one-token Q4_K launches (sixteen
+// waves for launches of up to about two rounds, four for less than one round
+// of short rows, else eight when some row is longer than eight blocks).
+int wide_waves(const q4a_problem *const *ps, int count) {
+    int g16 = 0, max_kb = 0;
+    bool short_rows = true;
+    for (int i = 0; i < count; ++i) {
+        const int KB = ps[i]->K >> 8;
+        const int T16 = kWide / tile_waves(KB, kWide);
+        g16 += ((ps[i]->N + kTile - 1) / kTile + T16 - 1) / T16;
+        max_kb = max(max_kb, KB);
+        if (tile_waves(KB, kWide) > 4) short_rows = false;
+    }
+    if (g16 <= kWideMaxGroups) return g16 < kCus && short_rows ? 4 : kWide;
+    return max_kb > 8 ? 8 : 4;
 }
 
 template <int WAVES>
-void launch_wide(const uint8_t *wq, const uint16_t *sc, const uint16_t *bi, const float *x, float *y, int N, int K,
-                 hipStream_t stream) {
-    const int T = WAVES / tile_waves(K >> 8, WAVES);
-    const int tiles = (N + kTile - 1) / kTile;
-    hipLaunchKernelGGL(q4a_wide_kernel<WAVES>, dim3((tiles + T - 1) / T), dim3(64 * WAVES), 0, stream, wq, sc, bi, x,
-                       y, N, K);
+hipError_t launch_wide(const q4a_problem *const *ps, int count, hipStream_t stream) {
+    QaBatch qb;
+    qb.count = count;
+    int groups = 0;
+    for (int i = 0; i < count; ++i) {
+        const q4a_problem &q = *ps[i];
+        const int T = WAVES / tile_waves(q.K >> 8, WAVES);
+        qb.p[i] = QaProblem{static_cast<const uint8_t *>(q.w_q), static_cast<const uint16_t *>(q.scales),
+                            static_cast<const uint16_t *>(q.biases), q.x, q.y, q.N, q.K, groups};
+        groups += ((q.N + kTile - 1) / kTile + T - 1) / T;
+    }
+    for (int i = 0; i < kMaxBatch; ++i) qb.tb[i] = i < count ? qb.p[i].tile_begin : INT_MAX;
+    if (groups == 0) return hipSuccess;
+    hipLaunchKernelGGL(q4a_wide_kernel<WAVES>, dim3(groups), dim3(64 * WAVES), 0, stream, qb);
+    return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace q4k
+// One launch for one token over the problems ps[0..count) (all eligible, N > 0),
+// longest rows first.
+hipError_t launch_one_token(const q4a_problem *const *ps_in, int count, hipStream_t stream) {
+    const q4a_problem *ps[kMaxBatch];
+    for (int i = 0; i < count; ++i) ps[i] = ps_in[i];
+    for (int i = 1; i < count; ++i)  // stable insertion sort by K, descending
+        for (int j = i; j > 0 && ps[j]->K > ps[j - 1]->K; --j) {
+            const q4a_problem *t = ps[j];
+            ps[j] = ps[j - 1];
+            ps[j - 1] = t;
+        }
+    switch (wide_waves(ps, count)) {
+        case 4: return launch_wide<4>(ps, count, stream);
+        case 8: return launch_wide<8>(ps, count, stream);
+        default: return launch_wide<kWide>(ps, count, stream);
+    }
+}
 
-extern "C" int q4a_matmul(const void *w_q, const void *scales, const void *biases, const float *x, float *y, int M,
-                          int N, int K, hipStream_t stream) {
+// q4a_matmul's argument checks (Q4K_OK or the error).
+int check_args(const void *w_q, const void *scales, const void *biases, const float *x, const float *y, int M,
+               int N, int K) {
     if (M < 0 || N < 0 || K < 0) return Q4K_ERR_BAD_DIM;
     if (M == 0 || N == 0) return Q4K_OK;
     if (K == 0 || K % Q4A_GROUP != 0) return Q4K_ERR_BAD_DIM;
@@ -403,25 +470,71 @@ extern "C" int q4a_matmul(const void *w_q, const void *scales, const void *biase
     if (((reinterpret_cast<uintptr_t>(w_q) | reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) != 0 ||
         ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) & 1u) != 0)
         return Q4K_ERR_ALIGN;
+    return Q4K_OK;
+}
+
+// One token on the matrix cores?
+bool one_token_eligible(const q4a_problem &q, int M) {
+    return M == 1 && q.K % 256 == 0 && q.K <= kWideMaxK &&
+           ((reinterpret_cast<uintptr_t>(q.scales) | reinterpret_cast<uintptr_t>(q.biases)) & 7u) == 0;
+}
+
+// The fp32 kernel for one problem (arguments checked, M, N > 0).
+hipError_t launch_gemv(const q4a_problem &q, int M, hipStream_t stream) {
+    const int MT = M == 1 ? 1 : 2;
+    const dim3 grid((q.N + kRows - 1) / kRows, (M + MT - 1) / MT);
+    const auto *wq = static_cast<const uint8_t *>(q.w_q);
+    const auto *sc = static_cast<const uint16_t *>(q.scales);
+    const auto *bi = static_cast<const uint16_t *>(q.biases);
+    if (MT == 1)
+        hipLaunchKernelGGL(q4a_gemv_kernel<1>, grid, dim3(kThreads), 0, stream, wq, sc, bi, q.x, q.y, M, q.N, q.K);
+    else
+        hipLaunchKernelGGL(q4a_gemv_kernel<2>, grid, dim3(kThreads), 0, stream, wq, sc, bi, q.x, q.y, M, q.N, q.K);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace q4k
+
+extern "C" int q4a_matmul(const void *w_q, const void *scales, const void *biases, const float *x, float *y, int M,
+                          int N, int K, hipStream_t stream) {
+    const int rc = q4k::check_args(w_q, scales, biases, x, y, M, N, K);
+    if (rc != Q4K_OK || M == 0 || N == 0) return rc;
     const int dev_rc = q4k::check_device();
     if (dev_rc != Q4K_OK) return dev_rc;
-    const auto *wq = static_cast<const uint8_t *>(w_q);
-    const auto *sc = static_cast<const uint16_t *>(scales);
-    const auto *bi = static_cast<const uint16_t *>(biases);
-    if (M == 1 && K % 256 == 0 && K <= q4k::kWideMaxK &&
-        ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(biases)) & 7u) == 0) {
-        switch (q4k::wide_waves(N, K >> 8)) {
-            case 4: q4k::launch_wide<4>(wq, sc, bi, x, y, N, K, stream); break;
-            case 8: q4k::launch_wide<8>(wq, sc, bi, x, y, N, K, stream); break;
-            default: q4k::launch_wide<q4k::kWide>(wq, sc, bi, x, y, N, K, stream); break;
-        }
-        return hipGetLastError() == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+    const q4a_problem q{w_q, scales, biases, x, y, N, K};
+    const q4a_problem *ps[1] = {&q};
+    const hipError_t err = q4k::one_token_eligible(q, M) ? q4k::launch_one_token(ps, 1, stream)
+                                                         : q4k::launch_gemv(q, M, stream);
+    return err == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+}
+
+extern "C" int q4a_matmul_batched(const q4a_problem *problems, int count, int M, hipStream_t stream) {
+    if (count < 1 || count > q4k::kMaxBatch || M < 0) return Q4K_ERR_BAD_DIM;
+    if (!problems) return Q4K_ERR_NULL;
+    // Every problem is checked before anything is enqueued.
+    for (int i = 0; i < count; ++i) {
+        const q4a_problem &q = problems[i];
+        const int rc = q4k::check_args(q.w_q, q.scales, q.biases, q.x, q.y, M, q.N, q.K);
+        if (rc != Q4K_OK) return rc;
     }
-    const int MT = M == 1 ? 1 : 2;
-    const dim3 grid((N + q4k::kRows - 1) / q4k::kRows, (M + MT - 1) / MT);
-    if (MT == 1)
-        hipLaunchKernelGGL(q4k::q4a_gemv_kernel<1>, grid, dim3(q4k::kThreads), 0, stream, wq, sc, bi, x, y, M, N, K);
-    else
-        hipLaunchKernelGGL(q4k::q4a_gemv_kernel<2>, grid, dim3(q4k::kThreads), 0, stream, wq, sc, bi, x, y, M, N, K);
-    return hipGetLastError() == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+    if (M == 0) return Q4K_OK;
+    const q4a_problem *work[q4k::kMaxBatch];
+    int n = 0;
+    bool all_one_token = true;
+    for (int i = 0; i < count; ++i)
+        if (problems[i].N > 0) {
+            work[n++] = &problems[i];
+            all_one_token = all_one_token && q4k::one_token_eligible(problems[i], M);
+        }
+    if (n == 0) return Q4K_OK;
+    const int dev_rc = q4k::check_device();
+    if (dev_rc != Q4K_OK) return dev_rc;
+    if (all_one_token) return q4k::launch_one_token(work, n, stream) == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH;
+    for (int i = 0; i < n; ++i) {
+        const hipError_t err = q4k::one_token_eligible(*work[i], M) ? q4k::launch_one_token(&work[i], 1, stream)
+                                                                   : q4k::launch_gemv(*work[i], M, stream);
+        if (err != hipSuccess) return Q4K_ERR_LAUNCH;
+    }
+    return Q4K_OK;
 }

@@ -80,7 +80,8 @@ inline Batch sealed(Batch b) {
 // tile_begin <= g (problems are laid out back to back, tile_begin ascending;
 // the table is INT_MAX past count; g is uniform).  Every entry is compared,
 // so the whole table is requested at once before the first weight load.
-__device__ __forceinline__ int find_problem(const Batch &bt, int g) {
+template <class B>  // any launch table with a tb[kMaxBatch] member laid out as Batch's
+__device__ __forceinline__ int find_problem(const B &bt, int g) {
     typedef int int16v __attribute__((ext_vector_type(16)));
     static_assert(kMaxBatch == 32, "table read as two 16-entry vectors");
     const int16v t0 = *reinterpret_cast<const int16v *>(bt.tb);

@@ -52,6 +52,31 @@ extern "C" {
 int q4a_matmul(const void *w_q, const void *scales, const void *biases, const float *x, float *y, int M, int N,
                int K, hipStream_t stream);
 
+/* One q4a product of a batch; the same fields, layout and alignment as the
+ * arguments of q4a_matmul. */
+typedef struct q4a_problem {
+    const void *w_q;
+    const void *scales;
+    const void *biases;
+    const float *x;
+    float *y;
+    int N;
+    int K;
+} q4a_problem;
+
+/* Several q4a products that share M (one layer's q/k/v/o/gate/up/down, as
+ * q4k_matmul_batched does for Q4_K; same passage).  problems: HOST array of
+ * count entries, 1 <= count <= Q4K_MAX_BATCH; problems may share x.  For one
+ * token, when every problem with work meets the matrix-core conditions above
+ * (K a multiple of 256, scales and biases 8-byte aligned), all of them run in
+ * one launch; otherwise each runs as q4a_matmul would.  Each y is as that
+ * problem's q4a_matmul computes it, up to the summation order of its K split
+ * (the split can differ with the batch around it).
+ *   Errors (every problem is checked before anything is enqueued): count
+ *   outside [1, Q4K_MAX_BATCH], M < 0, or any problem's error as for
+ *   q4a_matmul.  M == 0 and problems with N == 0 do nothing. */
+int q4a_matmul_batched(const q4a_problem *problems, int count, int M, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -119,3 +119,20 @@ def test_q4a_argument_errors_before_any_device_call(lib):
     assert q4k.raw_q4a_matmul(A, A, A, A + 4, A, 1, 4, 64) == q4k.ERR_ALIGN
     assert q4k.raw_q4a_matmul(0, 0, 0, 0, 0, 0, 4, 64) == q4k.OK
     assert q4k.raw_q4a_matmul(0, 0, 0, 0, 0, 3, 0, 64) == q4k.OK
+
+
+def test_q4a_batched_argument_errors_before_any_device_call(lib):
+    """Every problem of a batch is checked before anything is enqueued: a bad
+    count, M or problem is reported and M == 0 / N == 0 do nothing, all
+    without a device."""
+    A = 1 << 20
+    good = (A, A, A, A, A, 4, 256)
+    assert q4k.raw_q4a_matmul_batched([], 1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul_batched([good] * 33, 1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul_batched([good], -1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul_batched([good, (A, A, A, A, A, 4, 100)], 1) == q4k.ERR_BAD_DIM
+    assert q4k.raw_q4a_matmul_batched([good, (A, 0, A, A, A, 4, 256)], 1) == q4k.ERR_NULL
+    assert q4k.raw_q4a_matmul_batched([good, (A, A, A + 1, A, A, 4, 256)], 1) == q4k.ERR_ALIGN
+    assert q4k.raw_q4a_matmul_batched([good, (A, A, A, A, A + 8, 4, 256)], 1) == q4k.ERR_ALIGN
+    assert q4k.raw_q4a_matmul_batched([good, good], 0) == q4k.OK
+    assert q4k.raw_q4a_matmul_batched([(0, 0, 0, 0, 0, 0, 256)] * 3, 1) == q4k.OK

@@ -125,6 +125,75 @@ def test_q4a_one_token_cancelling_rows_and_wide_range():
     check_close(y, y_ref, sf, DECODE_TOL, "one token, wide range")
 
 
+def _batch_inputs(M, shapes, tag):
+    """Problems of one batch: (q, s, b) per shape, x shared by the problems of
+    equal K (as q/k/v share the attention input)."""
+    xs, probs = {}, []
+    for i, (N, K) in enumerate(shapes):
+        if K not in xs:
+            xs[K] = qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 990, M, K, tag))
+        probs.append((qi.random_q4a(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 991, i, N, K, tag)), xs[K]))
+    return probs, xs
+
+
+# One token: a layer-like batch in one launch (eight-wave workgroups: the
+# K = 4352 rows are 17 blocks), a short-row batch of sixteen- or four-wave
+# workgroups, a batch with an empty problem, a batch with one problem off the
+# matrix-core path (K = 640: each problem then runs as q4a_matmul would), and
+# two tokens (the fp32 kernel per problem).
+@pytest.mark.parametrize("M,shapes", [
+    (1, [(640, 1280), (128, 1280), (128, 1280), (640, 1280), (2176, 1280), (2176, 1280), (640, 4352)]),
+    (1, [(96, 512), (33, 256), (1, 768)]),
+    (1, [(300, 1024), (0, 1024), (70, 2048)]),
+    (1, [(200, 1024), (60, 640), (90, 2048)]),
+    (2, [(100, 1024), (37, 512), (64, 640)]),
+])
+def test_q4a_batched_matches_oracle(M, shapes):
+    import torch
+    probs, xs = _batch_inputs(M, shapes, 1)
+    xd = {K: to_dev(x) for K, x in xs.items()}
+    dev_probs = []
+    for (q, s, b), x in probs:
+        N, K = s.shape[0], x.shape[1]
+        y = torch.full((M, N), 5.0, dtype=torch.float32, device=device())
+        dev_probs.append((*_dev(q, s, b), xd[K], y))
+    ys = q4k.q4a_matmul_batched(dev_probs)
+    torch.cuda.synchronize()
+    for ((q, s, b), x), y in zip(probs, ys):
+        N, K = s.shape[0], x.shape[1]
+        if N == 0:
+            continue
+        y_ref, S = oracle.q4a_matmul(q, s, b, x, N, K)
+        check_close(y.cpu().numpy(), y_ref, _scale(q, s, b, x, K, S), DECODE_TOL, f"batched q4a N={N} K={K}")
+
+
+def test_q4a_batched_errors_enqueue_nothing():
+    """A bad problem anywhere in the batch is reported before any launch: the
+    other problems' y stay untouched."""
+    import torch
+    probs, xs = _batch_inputs(1, [(64, 512), (32, 512)], 2)
+    ys = [torch.full((1, s.shape[0]), 9.0, device=device()) for (q, s, b), _ in probs]
+    items = []
+    for ((q, s, b), x), y in zip(probs, ys):
+        qd, sd, bd = _dev(q, s, b)
+        xd = to_dev(x)
+        items.append([qd, sd, bd, xd, y])
+    keep = [t for it in items for t in it]  # device buffers alive through the raw calls
+    raw = [(it[0].data_ptr(), it[1].data_ptr(), it[2].data_ptr(), it[3].data_ptr(), it[4].data_ptr(),
+            it[1].shape[0], 512) for it in items]
+    bad = list(raw[1])
+    bad[6] = 500
+    assert q4k.raw_q4a_matmul_batched([raw[0], tuple(bad)], 1) == q4k.ERR_BAD_DIM
+    bad = list(raw[1])
+    bad[2] += 1  # biases: binary16, so an odd address is misaligned
+    assert q4k.raw_q4a_matmul_batched([raw[0], tuple(bad)], 1) == q4k.ERR_ALIGN
+    torch.cuda.synchronize()
+    assert all(torch.all(y == 9.0) for y in ys)
+    assert q4k.raw_q4a_matmul_batched(raw, 1) == q4k.OK
+    torch.cuda.synchronize()
+    assert not torch.all(ys[0] == 9.0) and len(keep) == 10
+
+
 def test_q4a_errors_leave_y_untouched_and_weights_unchanged():
     import torch
     dev = device()
