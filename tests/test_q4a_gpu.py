@@ -213,3 +213,35 @@ def test_q4a_errors_leave_y_untouched_and_weights_unchanged():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert np.array_equal(qd.cpu().numpy(), q) and np.array_equal(sd.cpu().numpy(), s)
+
+
+def test_q4a_batched_graph_replays():
+    """The one-token batched launch captured in a HIP graph (it needs no
+    workspace): three replays, with eager calls on other inputs in between,
+    each equal to the eager result bit for bit."""
+    import torch
+    probs, xs = _batch_inputs(1, [(300, 1024), (64, 1024), (130, 2048)], 3)
+    xd = {K: to_dev(x) for K, x in xs.items()}
+    dev_probs = []
+    for (q, s, b), x in probs:
+        dev_probs.append((*_dev(q, s, b), xd[x.shape[1]], torch.empty((1, s.shape[0]), device=device())))
+    eager = [y.clone() for y in q4k.q4a_matmul_batched(dev_probs)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q4k.q4a_matmul_batched(dev_probs, stream=side)
+        side.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            q4k.q4a_matmul_batched(dev_probs, stream=side)
+    torch.cuda.synchronize()
+    other = [(w, sc, bi, torch.randn_like(x), torch.empty_like(y)) for w, sc, bi, x, y in dev_probs]
+    for _ in range(3):
+        for *_, y in dev_probs:
+            y.fill_(-1.0)
+        q4k.q4a_matmul_batched(other)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (*_, y), e in zip(dev_probs, eager):
+            assert torch.equal(y, e)
