@@ -658,7 +658,7 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the Llama-3.2-1B pass, the launch groupings and the other workloads of the list")
     ap.add_argument("--only", default=None,
-                    help="run one piece only, for profiling: qwen3-14b_m1, llama1b_m1, prefill_m32, "
+                    help="run one piece only, for profiling: qwen3-14b_m1, qwen3-14b_m2, llama1b_m1, prefill_m32, "
                          "qwen3-14b_m4, qwen3-14b_m16, qwen3-14b_m1024, qwen3-8b_m1024, argmax, swiglu, q4a")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy three times (a known-size "
@@ -772,7 +772,7 @@ def run_only(args, q4k, dev):
     wl14 = WORKLOADS["qwen3-14b_sweep"]
     name = args.only
     res = {}
-    if name in ("qwen3-14b_m1", "qwen3-14b_m4", "qwen3-14b_m16"):
+    if name in ("qwen3-14b_m1", "qwen3-14b_m2", "qwen3-14b_m4", "qwen3-14b_m16"):
         ps = Pass(wl14, int(name.split("_m")[1]), dev)
         ms, ml = time_pass(ps, q4k, args.steps, args.warmup)
         res = {"us_per_step": ms * 1e3, "us_per_layer_launch": ml * 1e3}

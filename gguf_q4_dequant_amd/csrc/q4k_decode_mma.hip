@@ -36,11 +36,14 @@
 //     uses v_mfma_f32_16x16x32_f16 instead, its k-quarters split between two
 //     rows of W: two accumulating MFMAs cover a 32-weight sub-block of 32
 //     rows, and every lane finds its own row's hi and lo sums in the same two
-//     C registers (see mma_block16).
-//   * Kernels: for M = 1, workgroups of sixteen waves (four or eight for
-//     launches of more than about two rounds, four for small launches of
+//     C registers (see mma_block16).  Two to four tokens use the same split
+//     with their hi and lo rows in the A rows a single token leaves unused,
+//     so the MFMA count and the weight path stay those of one token (see
+//     mma_block_mt).
+//   * Kernels: for 1..4 tokens, workgroups of sixteen waves (four or eight
+//     for launches of more than about two rounds, four for small launches of
 //     short rows), each wave owning about two super-blocks of one 32-row tile
-//     and staging its own activations; for 2 <= M <= 16, eight-wave
+//     and staging its own activations; for 5 <= M <= 16, eight-wave
 //     workgroups on two tiles of four waves (up to 8 tokens) or four tiles of
 //     two waves (9..16), sharing one staged copy of the activations of all
 //     tokens, pass by pass over K.  In both, the waves of a tile add their
@@ -621,6 +624,7 @@ void decode_mma_kernel(Batch bt) {
 constexpr int kWideWaves = 16;
 constexpr int kCus = 256;  // MI355X compute units
 constexpr int kWideMaxGroups = 512;  // about two rounds of one workgroup per CU
+constexpr int kWideMaxTokens = 4;    // tokens of the one-token structure (decode_wide_mt_kernel)
 
 // Waves per tile: the power of two (at most the workgroup's WAVES) that
 // leaves each wave two super-blocks or fewer where possible.
@@ -791,6 +795,287 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     }
 }
 
+// ---- 2..4 tokens on the one-token structure ---------------------------------
+// The k-quarter split of mma_block16 with more A rows per row group: MT
+// tokens (2 or 4) put their hi and lo rows at 2t and 2t + 1 of a group of RG
+// rows (RG = 4 for two tokens, 8 for four); group 0 (rows 0..RG-1) carries
+// quarters 0, 1 (row l%16 of the tile), group 1 (rows RG..2RG-1) quarters
+// 2, 3 (row 16 + l%16), each zero where the other group's weights sit.  In
+// the 16x16 C layout (lane l, register r -> row 4*(l/16) + r) every lane
+// then finds two tokens of one row of W in registers 0..3:
+//   two tokens:  lanes 0..15 rows 0..15, lanes 16..31 rows 16..31 (lanes
+//                32..63 hold unused rows);
+//   four tokens: lanes 0..15 tokens 0, 1 and lanes 16..31 tokens 2, 3 of rows
+//                0..15, lanes 32..47 and 48..63 the same of rows 16..31.
+// The MFMAs, the weight loads and their parking are those of one token; each
+// wave stages its activations one super-block at a time (MT KB of LDS),
+// every token scaled by its own power of two per super-block.
+template <int MT>
+struct WideMt {
+    static_assert(MT == 2 || MT == 4, "two or four tokens");
+    static constexpr int RG = MT == 4 ? 8 : 4;  // A rows per row group
+    static constexpr int XS = 64 * MT;          // uint4 of one staged super-block
+    // Row of W (within the tile) and first token of lane l's results.
+    __device__ static int wrow(int l) { return MT == 4 ? (l & 15) + 16 * (l >> 5) : (l & 31); }
+    __device__ static int tbase(int l) { return MT == 4 ? 2 * ((l >> 4) & 1) : 0; }
+    __device__ static bool holds_row(int l) { return MT == 4 || l < 32; }
+};
+
+// Lane l of 64 stages 4*MT values of one token of one super-block: token
+// t = l / (64/MT), values 4*MT*u .. of it (u = l % (64/MT)), i.e. one
+// k-quarter of a sub-block (two tokens) or two (four tokens), into
+// xs[((jj*MT + t)*2 + hl)*4 + quarter] in the k order 0,2,1,3,4,6,5,7 of the
+// nibble operands; per token and sub-block the plain sum of x, per token the
+// factor 2^(24-e) that undoes its scaling.
+template <int MT>
+__device__ __forceinline__ void stage_block_mt(const float4 (&v)[MT], int lane, uint4 *xs, float *sum_t,
+                                               float *mul_t) {
+    constexpr int LPT = 64 / MT;  // lanes per token
+    const int t = lane / LPT, u = lane % LPT;
+    float xv[4 * MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        xv[4 * i] = v[i].x;
+        xv[4 * i + 1] = v[i].y;
+        xv[4 * i + 2] = v[i].z;
+        xv[4 * i + 3] = v[i].w;
+    }
+    // Sub-block sums in one order for every MT (and for one token): each
+    // k-quarter (8 values) in order, then quarters 0 + 1 and 2 + 3, then the
+    // two halves.
+    float mx = 0.f, sm = 0.f;
+#pragma unroll
+    for (int h = 0; h < MT / 2; ++h) {
+        float sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mx = fmaxf(mx, fabsf(xv[8 * h + i]));
+            sq += xv[8 * h + i];
+        }
+        sm = h == 0 ? sq : sm + sq;
+    }
+    // largest |x| of the token's super-block: its LPT lanes
+    mx = fmaxf(mx, xor32<1>(mx));
+    mx = fmaxf(mx, xor32<2>(mx));
+    mx = fmaxf(mx, xor32<4>(mx));
+    mx = fmaxf(mx, xor32<8>(mx));
+    if constexpr (LPT == 32) mx = fmaxf(mx, xor32<16>(mx));
+    // sum of each sub-block (32 values): 32 / (4*MT) lanes
+    if constexpr (MT == 2) sm += xor32<1>(sm);  // quarters 0 + 1, 2 + 3
+    sm += xor32<MT == 2 ? 2 : 1>(sm);           // the two halves
+    const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu);
+    int e = E == 0 ? 127 : (E == 255 ? 0 : 141 - E);
+    e = max(-103, min(127, e));
+    const float up = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    const float back = __uint_as_float(static_cast<uint32_t>(24 - e + 127) << 23);
+    constexpr int perm[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+    for (int h = 0; h < MT / 2; ++h) {  // the lane's k-quarters
+        half8 hv, lv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x2 = xv[8 * h + perm[i]] * up;
+            const _Float16 hh = static_cast<_Float16>(x2);
+            hv[i] = hh;
+            lv[i] = static_cast<_Float16>(x2 - static_cast<float>(hh));
+        }
+        const int q = MT == 2 ? (u & 3) : 2 * (u & 1) + h;  // quarter of the sub-block
+        const int jj = MT == 2 ? (u >> 2) : (u >> 1);       // sub-block
+        xs[((jj * MT + t) * 2 + 0) * 4 + q] = __builtin_bit_cast(uint4, hv);
+        xs[((jj * MT + t) * 2 + 1) * 4 + q] = __builtin_bit_cast(uint4, lv);
+    }
+    constexpr int LPS = 32 / (4 * MT);  // lanes per sub-block
+    if (u % LPS == 0) sum_t[t * 8 + u / LPS] = sm;
+    if (u == 0) mul_t[t] = back;
+}
+
+// One parked super-block of 32 rows times the staged activations of MT
+// tokens; this lane's two tokens tb, tb + 1 of its row add into acc[0..1].  rb: the lane's B bytes (as in mma_block16), xa: its A
+// fragments, fragment (sub-block jj, half p) at xa[jj*MT*8 + 2p].
+template <int MT>
+__device__ __forceinline__ void mma_block_mt(const uint8_t *slot, const uint8_t *rb, const uint4 *xa, int lane,
+                                             const float *mul_t, const float *sum_t, float (&acc)[2]) {
+    using W = WideMt<MT>;
+    const int tb = W::tbase(lane);
+    const uint4 hd = *reinterpret_cast<const uint4 *>(slot + W::wrow(lane) * kBlockBytes);
+    const uint32_t scA = hd.y & 0x3F3F3F3Fu, mnA = hd.z & 0x3F3F3F3Fu;
+    const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+    float blo[2] = {0.f, 0.f}, bhi[2] = {0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint2 q0 = *reinterpret_cast<const uint2 *>(rb + 32 * g);
+        const uint2 q1 = *reinterpret_cast<const uint2 *>(rb + 32 * g + 16);
+        const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
+        const uint32_t s00 = q0.x >> 8, s01 = q0.y >> 8, s10 = q1.x >> 8, s11 = q1.y >> 8;
+        const uint4 bl0 = {q0.x & LM, s00 & LM, q0.y & LM, s01 & LM};
+        const uint4 bh0 = {q0.x & HM, s00 & HM, q0.y & HM, s01 & HM};
+        const uint4 bl1 = {q1.x & LM, s10 & LM, q1.y & LM, s11 & LM};
+        const uint4 bh1 = {q1.x & HM, s10 & HM, q1.y & HM, s11 & HM};
+        const int jl = 2 * g, jh = jl + 1;
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        float4v cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jl * MT * 8]),
+                                                            __builtin_bit_cast(half8, bl0), z, 0, 0, 0);
+        float4v ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jh * MT * 8]),
+                                                            __builtin_bit_cast(half8, bh0), z, 0, 0, 0);
+        cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jl * MT * 8 + 2]),
+                                                    __builtin_bit_cast(half8, bl1), cl, 0, 0, 0);
+        ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jh * MT * 8 + 2]),
+                                                    __builtin_bit_cast(half8, bh1), ch, 0, 0, 0);
+        const uint32_t sw = g < 2 ? scA : scB;
+        const float sl = static_cast<float>((sw >> (16 * (g & 1))) & 0xFFu);
+        const float sh = static_cast<float>((sw >> (16 * (g & 1) + 8)) & 0xFFu);
+        blo[0] = __builtin_fmaf(sl, cl[0] + cl[1], blo[0]);
+        blo[1] = __builtin_fmaf(sl, cl[2] + cl[3], blo[1]);
+        bhi[0] = __builtin_fmaf(sh, ch[0] + ch[1], bhi[0]);
+        bhi[1] = __builtin_fmaf(sh, ch[2] + ch[3], bhi[1]);
+    }
+    const float d = half_bits_to_float(hd.x & 0xFFFFu), dmin = half_bits_to_float(hd.x >> 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float mterm = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t mw = j < 4 ? mnA : mnB;
+            mterm = __builtin_fmaf(static_cast<float>((mw >> (8 * (j & 3))) & 0xFFu), sum_t[(tb + i) * 8 + j], mterm);
+        }
+        acc[i] = __builtin_fmaf(mul_t[tb + i], d * __builtin_fmaf(bhi[i], 0.0625f, blo[i]), acc[i]);
+        acc[i] = __builtin_fmaf(-dmin, mterm, acc[i]);
+    }
+}
+
+// WAVES as for decode_wide_kernel; each wave owns about two super-blocks of
+// one 32-row tile and stages its own activations, one super-block at a time.
+template <int WAVES, int MT>
+__global__ __launch_bounds__(64 * WAVES) void decode_wide_mt_kernel(Batch bt) {
+    using Wm = WideMt<MT>;
+    __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kStage];
+    __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][Wm::XS];
+    __shared__ __attribute__((aligned(16))) uint4 xzero[Wm::XS];  // the A fragments that must be zero
+    __shared__ float xsumw[WAVES][MT * 8];
+    __shared__ float xmulw[WAVES][MT];
+    __shared__ float red[WAVES * 64 * 2];
+    for (int i = threadIdx.x; i < Wm::XS; i += 64 * WAVES) xzero[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int g = static_cast<int>(blockIdx.x);
+    const int p = find_problem(bt, g);
+    const DevProblem P = load_problem(bt, p);
+    const int N = P.N, K = P.K, M = bt.M;
+    const int KB = K >> 8;
+    const int wpt = wide_wpt(KB, WAVES);
+    const int lg = __builtin_ctz(wpt);
+    const int T = WAVES >> lg;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int tl = wave >> lg, kw = wave & (wpt - 1);
+    const int n0 = ((g - P.tile_begin) * T + tl) * kCols;
+    const bool active = n0 < N;
+
+    uint8_t *wst = wslots + wave * kStage;
+    uint4 *xs = xsw[wave];
+    float *xsum = xsumw[wave];
+    float *xmul = xmulw[wave];
+
+    const int nr = active ? N - 1 - n0 : 0;
+    const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * KB * kBlockBytes;
+    const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
+    uint32_t goff[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int f = min(lane + 64 * j, kStageChunks - 1);
+        goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
+    }
+    const bool has5 = lane + 256 < kStageChunks;
+    auto ld = [&](int kb, int j) -> u32x4 {
+        const uint8_t *wb = W + static_cast<uint32_t>(kb) * kBlockBytes;  // uniform
+        return *reinterpret_cast<const u32x4 *>(wb + goff[j]);
+    };
+    auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, u32x4 v4) {
+        u32x4 *d = reinterpret_cast<u32x4 *>(wst);
+        d[lane] = v0;
+        d[lane + 64] = v1;
+        d[lane + 128] = v2;
+        d[lane + 192] = v3;
+        if (has5) d[lane + 256] = v4;
+    };
+    // This lane's activations of a super-block: token min(t, M - 1) (tokens
+    // past M repeat the last one and are never stored), values 4*MT*u.
+    constexpr int LPT = 64 / MT;
+    const float *xrow = P.x + static_cast<size_t>(min(lane / LPT, M - 1)) * K + 4 * MT * (lane % LPT);
+    auto ldx = [&](int kb, float4 (&v)[MT]) {
+        const float4 *src = reinterpret_cast<const float4 *>(xrow + static_cast<size_t>(kb) * 256);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) v[i] = src[i];
+    };
+
+    // This lane's operands: its B bytes (as for one token), its A fragments
+    // (A row c16 of group c16 / RG: token (c16 % RG) / 2, hi or lo by parity;
+    // zeros where the row's group is not the quarter's; rows past 2 RG are
+    // never read back).
+    const int c16 = lane & 15, quarter = lane >> 4;
+    const int ga = c16 / Wm::RG;
+    const bool zero_lane = ga < 2 && ga != (quarter >> 1);
+    const int ta = ga < 2 ? (c16 % Wm::RG) >> 1 : 0;
+    const uint4 *xfrag = zero_lane ? xzero : xs + ta * 8 + (c16 & 1) * 4 + (quarter & 1);
+    const uint8_t *rb = wst + (c16 + 16 * (quarter >> 1)) * kBlockBytes + 16 + 8 * (quarter & 1);
+
+    float acc[2] = {0.f, 0.f};
+    const int nb = active && KB > kw ? (KB - kw + wpt - 1) >> lg : 0;
+    for (int i0 = 0; i0 < nb; i0 += 2) {
+        const int kb0 = kw + wpt * i0, kb1 = kw + wpt * min(i0 + 1, nb - 1);
+        float4 xa[MT], xb[MT];
+        ldx(kb0, xa);
+        ldx(kb1, xb);
+        const u32x4 a0 = ld(kb0, 0), a1 = ld(kb0, 1), a2 = ld(kb0, 2), a3 = ld(kb0, 3), a4 = ld(kb0, 4);
+        const u32x4 b0 = ld(kb1, 0), b1 = ld(kb1, 1), b2 = ld(kb1, 2), b3 = ld(kb1, 3), b4 = ld(kb1, 4);
+        stage_block_mt<MT>(xa, lane, xs, xsum, xmul);
+        park(a0, a1, a2, a3, a4);
+        mma_block_mt<MT>(wst, rb, xfrag, lane, xmul, xsum, acc);
+        if (i0 + 1 < nb) {
+            // after the reads above, in program order
+            stage_block_mt<MT>(xb, lane, xs, xsum, xmul);
+            park(b0, b1, b2, b3, b4);
+            mma_block_mt<MT>(wst, rb, xfrag, lane, xmul, xsum, acc);
+        }
+    }
+
+    red[(wave * 64 + lane) * 2] = acc[0];
+    red[(wave * 64 + lane) * 2 + 1] = acc[1];
+    __syncthreads();
+    if (active && kw == 0 && Wm::holds_row(lane)) {
+        const int n = n0 + Wm::wrow(lane), tb = Wm::tbase(lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float v = 0.f;
+            for (int j = 0; j < wpt; ++j) v += red[((tl * wpt + j) * 64 + lane) * 2 + i];
+            if (tb + i < M && n < N) P.y[static_cast<size_t>(tb + i) * N + n] = v;
+        }
+    }
+}
+
+template <int WAVES, int MT>
+hipError_t launch_wide_mt(const Batch &b, const int *order, hipStream_t stream) {
+    Batch sb;
+    sb.count = b.count;
+    sb.M = b.M;
+    int groups = 0;
+    for (int i = 0; i < b.count; ++i) {
+        sb.p[i] = b.p[order[i]];
+        const int KB = sb.p[i].K / kBlockWeights;
+        const int T = WAVES / wide_wpt(KB, WAVES);
+        const int tiles = (sb.p[i].N + kCols - 1) / kCols;
+        sb.p[i].tile_begin = groups;
+        sb.p[i].tiles = (tiles + T - 1) / T;
+        sb.p[i].splits = 1;
+        groups += sb.p[i].tiles;
+    }
+    if (groups == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_wide_mt_kernel<WAVES, MT>), dim3(groups), dim3(64 * WAVES), 0, stream, sealed(sb));
+    return hipGetLastError();
+}
+
 // Greedy selection from the tile pairs of decode_wide_kernel<., true>: one
 // workgroup, index[0] = the best pair's row, value[0] its value (an all-NaN
 // row gives index 0 and value NaN).
@@ -888,7 +1173,8 @@ hipError_t launch_wide(const Batch &b, const int *order, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The waves per workgroup of an M = 1 launch (see launch_decode_mma).
+// The waves per workgroup of a one- to four-token launch (see
+// launch_decode_mma).
 int wide_waves(const Batch &b) {
     const int g16 = wide_groups(b, kWideWaves);
     if (g16 <= kWideMaxGroups) {
@@ -900,6 +1186,24 @@ int wide_waves(const Batch &b) {
     int max_kb = 0;
     for (int i = 0; i < b.count; ++i) max_kb = max(max_kb, b.p[i].K / kBlockWeights);
     return max_kb > 8 ? 8 : 4;
+}
+
+// Two to four tokens: the one-token structure with the tokens in the spare A
+// rows, workgroup size as for one token.
+hipError_t launch_few(const Batch &b, const int *order, hipStream_t stream) {
+    const int waves = wide_waves(b);
+    if (b.M == 2) {
+        switch (waves) {
+        case 4: return launch_wide_mt<4, 2>(b, order, stream);
+        case 8: return launch_wide_mt<8, 2>(b, order, stream);
+        default: return launch_wide_mt<kWideWaves, 2>(b, order, stream);
+        }
+    }
+    switch (waves) {
+    case 4: return launch_wide_mt<4, 4>(b, order, stream);
+    case 8: return launch_wide_mt<8, 4>(b, order, stream);
+    default: return launch_wide_mt<kWideWaves, 4>(b, order, stream);
+    }
 }
 
 }  // namespace
@@ -957,6 +1261,7 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         default: return launch_wide<kWideWaves>(b, order, stream);
         }
     }
+    if (b.M <= kWideMaxTokens) return launch_few(b, order, stream);
     // At most 16 tokens per launch (32 A rows); more tokens (only when the
     // caller forces this path) are done 16 at a time.
     for (int m0 = 0; m0 < b.M; m0 += kMaxTokens) {
@@ -977,8 +1282,8 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         const int M = sb.M;
         int ident[kMaxBatch];
         for (int i = 0; i < b.count; ++i) ident[i] = i;
-        if (M <= 1) {
-            const hipError_t e = launch_wide<kWideWaves>(sb, ident, stream);
+        if (M <= kWideMaxTokens) {  // a last chunk of 1..4 tokens
+            const hipError_t e = M == 1 ? launch_wide<kWideWaves>(sb, ident, stream) : launch_few(sb, ident, stream);
             if (e != hipSuccess) return e;
             continue;
         }
@@ -1025,9 +1330,7 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             hipLaunchKernelGGL(prestage_kernel<false>, dim3(blocks), dim3(256), 0, stream, st);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = M <= 4 ? launch_np<2>(sb, M, stream)
-            : M <= 8 ? launch_np<4>(sb, M, stream)
-                     : launch_np<8>(sb, M, stream);
+        e = M <= 8 ? launch_np<4>(sb, M, stream) : launch_np<8>(sb, M, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -70,6 +70,7 @@ def test_llama32_1b_decode_layer_and_lm_head():
     _layer_case(wl, 1, 0)
     _layer_case(wl, 1, wl.layers - 1)
     _lm_head_case(wl, 1)
+    _lm_head_case(wl, 3)  # four-wave workgroups over several rounds, a fourth token row unused
 
 
 def test_llama32_3b_prefill_chunk_layer():
@@ -92,7 +93,9 @@ def test_qwen3_14b_long_prefill_layer_and_lm_head():
     _lm_head_case(wl, 1024, ncols=64)
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
+# 2..4 tokens run the one-token structure (eight-wave workgroups over several
+# rounds here), 16 the token-row layout.
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
 def test_qwen3_14b_decode_layer(M):
     wl = WORKLOADS["qwen3-14b_sweep"]
     _layer_case(wl, M, 0)

@@ -117,8 +117,8 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
 
 
 @pytest.mark.parametrize("path,M,cuts,bitwise", [
-    (DEC, 4, (2,), True),         # chunks of 2..8 tokens run one kernel and K split: identical bits
-    (DEC, 8, (3, 5), True),
+    (DEC, 4, (2,), True),         # chunks of 2..4 tokens run one kernel and K split: identical bits
+    (DEC, 8, (3, 5), False),      # 3 tokens on the one-token structure, 5 on the pair-row layout
     (DEC, 29, (13,), True),       # chunks of 9..16 tokens (16 at a time above 16): identical bits
     (DEC, 9, (5, 7), False),      # 9 tokens against chunks of 5 and 2: two layouts, same values to rounding
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
@@ -265,10 +265,11 @@ def test_split_k_workspace_reuse_across_layouts(path, Ms):
                 check_close(y.cpu().numpy()[:, cols], y_ref, s, tol, f"seq {si} M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M", [17, 20, 33])
+@pytest.mark.parametrize("M", [17, 18, 20, 33, 35])
 def test_decode_forced_above_16_tokens(M):
-    """The decode family runs more than 16 tokens 16 at a time (the last chunk of
-    33 is a single token, on the M = 1 kernel); the chunks share the workspace."""
+    """The decode family runs more than 16 tokens 16 at a time; a last chunk of
+    one token (17, 33) runs the M = 1 kernel, of 2..4 tokens (18, 20, 35) the
+    kernel of 2..4 tokens; the chunks share the workspace."""
     N, K = 150, 2560
     w, x = _inputs(M, N, K, 6)
     y = _run(w, x, N, DEC)
