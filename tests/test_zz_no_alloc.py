@@ -43,10 +43,10 @@ def _items(probs, key):
     ((600, 64), [(300, 1024), (200, 17408), (129, 1024), (64, 2304)]),
     # 32-row prefill tiles: K cut into chunks of eight blocks, partials in scratch
     ((48, 17), [(700, 4096), (300, 2816)]),
-    # small-M decode: staged activations (token rows above 8 tokens, pair rows below)
-    ((12, 3), [(500, 5120), (90, 2048), (500, 5120)]),
-    # one token: no scratch at all
-    ((1, 1), [(1000, 2048), (40, 8192)]),
+    # small-M decode: staged activations (token rows above 8 tokens, pair rows for 5..8)
+    ((12, 6), [(500, 5120), (90, 2048), (500, 5120)]),
+    # 2..4 tokens and one token: no scratch at all
+    ((3, 1), [(1000, 2048), (40, 8192)]),
 ])
 def test_noalloc_equals_batched_on_consecutive_calls(Ms, shapes):
     import torch
