@@ -25,7 +25,9 @@ def test_graph_replays_match_eager():
     q4k.library()
     # M = 1 layer-sized batch (sixteen-wave kernel), a tall M = 1 product (more
     # than two rounds of workgroups: four-wave kernel), an M = 64 prefill and
-    # long rows through the fp32 GEMV family (split-K partials in the workspace).
+    # long rows through the fp32 GEMV family (split-K partials in the workspace);
+    # three tokens (the one-token structure, no workspace), twelve (activations
+    # staged in the workspace) and 32 (binary16 x, K chunks and their sum).
     layer = []
     for i, (N, K) in enumerate([(2048, 2048), (512, 2048), (8192, 2048), (2048, 8192)]):
         w, x = _dev_inputs(1, N, K, i)
@@ -36,9 +38,17 @@ def test_graph_replays_match_eager():
     pre = [(wp, xp, torch.empty(64, 1024, device="cuda"))]
     wg, xg = _dev_inputs(1, 300, 8192, 12)
     gemv = [(wg, xg, torch.empty(1, 300, device="cuda"))]
-    calls = [q4k.prepare_batched(b) for b in (layer, tall, pre)]
+    small = []
+    for i, (N, K) in enumerate([(1000, 2048), (300, 5120)]):
+        w, x = _dev_inputs(3, N, K, 20 + i)
+        small.append((w, x, torch.empty(3, N, device="cuda")))
+    wr, xr = _dev_inputs(12, 500, 5120, 13)
+    rows = [(wr, xr, torch.empty(12, 500, device="cuda"))]
+    ws, xs = _dev_inputs(32, 700, 3072, 14)
+    skinny = [(ws, xs, torch.empty(32, 700, device="cuda"))]
+    calls = [q4k.prepare_batched(b) for b in (layer, tall, pre, small, rows, skinny)]
     calls.append(q4k.prepare_batched(gemv, path=q4k.PATH_GEMV))
-    outs = [y for b in (layer, tall, pre, gemv) for (_, _, y) in b]
+    outs = [y for b in (layer, tall, pre, small, rows, skinny, gemv) for (_, _, y) in b]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
