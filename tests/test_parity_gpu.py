@@ -44,7 +44,10 @@ DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 
                  # workgroups of two tiles (<= 8 tokens) or four (9..16 tokens) with the last
                  # tiles past N, one-block and three-block rows, long rows in passes of four
                  (6, 33, 1280), (7, 65, 256), (12, 97, 1024), (13, 161, 2304), (15, 40, 256),
-                 (10, 33, 768), (11, 50, 17408)]
+                 (10, 33, 768), (11, 50, 17408),
+                 # 2..4 tokens on the one-token structure: one-block rows (a tile per wave),
+                 # a single row, long rows split over sixteen waves
+                 (4, 33, 256), (3, 1, 512), (2, 97, 17408)]
 
 
 @pytest.mark.parametrize("path", [DEC, GEMV])
