@@ -33,12 +33,11 @@
 //     distinct banks): reading fragments straight from HBM touches twice as
 //     many cache lines per load and is much slower.
 //   * For M = 1 the single token fills only two A rows, so the wide kernel
-//     uses v_mfma_f32_16x16x32_f16 instead, its k-quarters split between two
-//     rows of W: two accumulating MFMAs cover a 32-weight sub-block of 32
-//     rows, and every lane finds its own row's hi and lo sums in the same two
-//     C registers (see mma_block16).  Two to four tokens use the same split
-//     with their hi and lo rows in the A rows a single token leaves unused,
-//     so the MFMA count and the weight path stay those of one token (see
+//     uses v_mfma_f32_16x16x32_f16 instead: one MFMA covers a whole 32-weight
+//     sub-block for 16 rows of W, with hi in the even and lo in the odd rows
+//     of A (see mma_block16).  Two to four tokens split the MFMA's k-quarters
+//     between two rows of W and put their hi and lo rows in A rows of their
+//     own, so the MFMA count and the weight path stay those of one token (see
 //     mma_block_mt).
 //   * Kernels: for 1..4 tokens, workgroups of sixteen waves (four or eight
 //     for launches of more than about two rounds, four for small launches of
@@ -361,63 +360,51 @@ __global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
 // NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8); 8 (9..16
 // tokens) runs mma_block_rows on the token-row layout instead.
 
-// M = 1 variant of mma_block on v_mfma_f32_16x16x32_f16.  The k-quarters of
-// one MFMA carry two rows of W at once: quarters 0, 1 hold 16 weights of row
-// n0 + l%16, quarters 2, 3 the same 16 weights of row n0 + 16 + l%16.  A holds
-// x' hi in row 0 and lo in row 1 over quarters 0, 1 (zeros over 2, 3), and the
-// same in rows 4, 5 over quarters 2, 3 (zeros over 0, 1), so C rows 0, 1 are
-// the first row's hi and lo sums and C rows 4, 5 the second row's.  In the C
-// layout of a 16x16 MFMA (lane l, register r -> row 4*(l/16) + r, column
-// l%16) lanes 0..15 find the first rows and lanes 16..31 the second rows in
-// registers 0 and 1: lane l (< 32) owns row l of the tile with no selection.
-// Two such MFMAs, accumulating, cover a 32-weight sub-block.  The other A
-// rows are never read back and may hold anything.
-//   rb: this lane's bytes in the slot (its row, k-half 8*(quarter & 1));
-// xa: this lane's A fragments (staged x', or the zero block for the eight
-// lanes that must be zero), fragment (sub-block jj, half p) at xa[jj*8 + 2p].
-// The 6-bit scales and mins enter as small integers; d, dmin and the factor
-// that undoes the activations' scaling are applied once per super-block.
-__device__ __forceinline__ void mma_block16(const uint8_t *slot, const uint8_t *rb, const uint4 *xa, int lane,
-                                            int jj0, float mul, const float *sum_t, float &acc) {
-    const uint4 hd = *reinterpret_cast<const uint4 *>(slot + (lane & 31) * kBlockBytes);
-    const uint32_t scA = hd.y & 0x3F3F3F3Fu, mnA = hd.z & 0x3F3F3F3Fu;
-    const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
-    const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
-    float blo = 0.f, bhi = 0.f;  // sum_j sc_j * (sub-block j's sum of x' q 2^-24), even and odd j
+// M = 1 variant of mma_block on v_mfma_f32_16x16x32_f16: K = 32 is one
+// sub-block, so no MFMA waits on another.  A holds x' hi in every even row and
+// lo in every odd row (lane l: row l%16, k-quarter l/16); B holds the quants
+// of rows n0 + l%16 (first MFMA) and n0 + 16 + l%16 (second).  Lane l < 16
+// reads its row's result in C rows 0, 1 of the first MFMA, lane 16..31 in C
+// rows 4, 5 of the second, so lane l (< 32) owns row l of the tile and decodes
+// only that row's scales.  xs holds, per staged sub-block jj, the hi then lo
+// row as four 16-byte k-quarters: xs[(jj*2 + hl)*4 + quarter].
+__device__ __forceinline__ void mma_block16(const uint8_t *slot, const uint4 *xs, int lane, int jj0,
+                                            float mul, const float *sum_t, float &acc) {
+    const int c16 = lane & 15, quarter = lane >> 4, hl = lane & 1;
+    const bool second = (lane & 16) != 0;
+    float dsc[8], dm[8];
+    block_scales(*reinterpret_cast<const uint4 *>(slot + (lane & 31) * kBlockBytes), dsc, dm);
+    const uint8_t *ra = slot + c16 * kBlockBytes + 16 + 8 * quarter;
+    const uint8_t *rc = ra + 16 * kBlockBytes;
+    float blk = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const uint2 q0 = *reinterpret_cast<const uint2 *>(rb + 32 * g);
-        const uint2 q1 = *reinterpret_cast<const uint2 *>(rb + 32 * g + 16);
+        const uint2 qa = *reinterpret_cast<const uint2 *>(ra + 32 * g);
+        const uint2 qc = *reinterpret_cast<const uint2 *>(rc + 32 * g);
         const uint32_t LM = 0x000F000Fu, HM = 0x00F000F0u;
-        const uint32_t s00 = q0.x >> 8, s01 = q0.y >> 8, s10 = q1.x >> 8, s11 = q1.y >> 8;
-        const uint4 bl0 = {q0.x & LM, s00 & LM, q0.y & LM, s01 & LM};
-        const uint4 bh0 = {q0.x & HM, s00 & HM, q0.y & HM, s01 & HM};
-        const uint4 bl1 = {q1.x & LM, s10 & LM, q1.y & LM, s11 & LM};
-        const uint4 bh1 = {q1.x & HM, s10 & HM, q1.y & HM, s11 & HM};
+        const uint32_t sa0 = qa.x >> 8, sa1 = qa.y >> 8, sc0 = qc.x >> 8, sc1 = qc.y >> 8;
+        const uint4 bla = {qa.x & LM, sa0 & LM, qa.y & LM, sa1 & LM};
+        const uint4 bha = {qa.x & HM, sa0 & HM, qa.y & HM, sa1 & HM};
+        const uint4 blc = {qc.x & LM, sc0 & LM, qc.y & LM, sc1 & LM};
+        const uint4 bhc = {qc.x & HM, sc0 & HM, qc.y & HM, sc1 & HM};
         const int jl = jj0 + 2 * g, jh = jl + 1;
+        const half8 al = __builtin_bit_cast(half8, xs[(jl * 2 + hl) * 4 + quarter]);
+        const half8 ah = __builtin_bit_cast(half8, xs[(jh * 2 + hl) * 4 + quarter]);
         const float4v z = {0.f, 0.f, 0.f, 0.f};
-        float4v cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jl * 8]),
-                                                            __builtin_bit_cast(half8, bl0), z, 0, 0, 0);
-        float4v ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jh * 8]),
-                                                            __builtin_bit_cast(half8, bh0), z, 0, 0, 0);
-        cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jl * 8 + 2]),
-                                                    __builtin_bit_cast(half8, bl1), cl, 0, 0, 0);
-        ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xa[jh * 8 + 2]),
-                                                    __builtin_bit_cast(half8, bh1), ch, 0, 0, 0);
-        const uint32_t sw = g < 2 ? scA : scB;  // sub-blocks 2g, 2g+1: bytes (2g)%4, (2g+1)%4
-        blo = __builtin_fmaf(static_cast<float>((sw >> (16 * (g & 1))) & 0xFFu), cl[0] + cl[1], blo);
-        bhi = __builtin_fmaf(static_cast<float>((sw >> (16 * (g & 1) + 8)) & 0xFFu), ch[0] + ch[1], bhi);
+        const float4v cla = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(half8, bla), z, 0, 0, 0);
+        const float4v clc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(half8, blc), z, 0, 0, 0);
+        const float4v cha = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8, bha), z, 0, 0, 0);
+        const float4v chc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(half8, bhc), z, 0, 0, 0);
+        // C layout of a 16x16 MFMA: lane l, register r -> row 4*(l/16) + r, column l%16.
+        const float lo = second ? clc[0] + clc[1] : cla[0] + cla[1];
+        const float hi = second ? chc[0] + chc[1] : cha[0] + cha[1];
+        blk = __builtin_fmaf(dsc[2 * g], lo, blk);
+        blk = __builtin_fmaf(dsc[2 * g + 1], hi, blk);
     }
     float mterm = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t mw = j < 4 ? mnA : mnB;
-        mterm = __builtin_fmaf(static_cast<float>((mw >> (8 * (j & 3))) & 0xFFu), sum_t[jj0 + j], mterm);
-    }
-    const float d = half_bits_to_float(hd.x & 0xFFFFu), dmin = half_bits_to_float(hd.x >> 16);
-    // high nibbles entered as 16q: their sums carry a factor 16
-    acc = __builtin_fmaf(mul, d * __builtin_fmaf(bhi, 0.0625f, blo), acc);
-    acc = __builtin_fmaf(-dmin, mterm, acc);
+    for (int j = 0; j < 8; ++j) mterm = __builtin_fmaf(dm[j], sum_t[jj0 + j], mterm);
+    acc = __builtin_fmaf(mul, blk, acc) - mterm;
 }
 
 // Staging for mma_block16: eight activations (values 8v..8v+7 of staged
@@ -661,13 +648,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     // super-blocks with their sub-block sums and scale factors.
     __shared__ __attribute__((aligned(16))) uint8_t wslots[WAVES * kStage];
     __shared__ __attribute__((aligned(16))) uint4 xsw[WAVES][2 * 64];
-    __shared__ __attribute__((aligned(16))) uint4 xzero[2 * 64];  // the A fragments that must be zero
     __shared__ float xsumw[WAVES][2 * 8];
     __shared__ float xmulw[WAVES][2];
     __shared__ float red[WAVES * 64];  // partial sums (own array: one barrier before the final sum)
-    static_assert(64 * WAVES >= 2 * 64, "one thread per zero fragment");
-    if (threadIdx.x < 2 * 64) xzero[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
     const int g = static_cast<int>(blockIdx.x);
     const int p = find_problem(bt, g);
     const DevProblem P = load_problem(bt, p);
@@ -679,8 +662,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
 
     const int t = threadIdx.x;
     const int lane = t & 63;
-    // wave-uniform to the compiler too: the weight loads take a scalar base
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // (Made wave-uniform to the compiler with readfirstlane, so that the
+    // weight loads take a scalar base, the layer launch was about 1% slower.)
+    const int wave = t >> 6;
     const int col = lane & 31, half = lane >> 5;
     const int tl = wave >> lg, kw = wave & (wpt - 1);  // tile within the group, K lane
     const int n0 = ((g - P.tile_begin) * T + tl) * kCols;
@@ -709,8 +693,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
     const bool has5 = lane + 256 < kStageChunks;
     auto ld = [&](int kb, int j) -> u32x4 {
         if constexpr (PAIR) return *reinterpret_cast<const u32x4 *>(pb[j] + static_cast<uint32_t>(kb) * kBlockBytes);
-        const uint8_t *wb = W + static_cast<uint32_t>(kb) * kBlockBytes;  // uniform
-        return *reinterpret_cast<const u32x4 *>(wb + goff[j]);
+        return *reinterpret_cast<const u32x4 *>(W + (static_cast<uint32_t>(kb) * kBlockBytes + goff[j]));
     };
     auto park = [&](u32x4 v0, u32x4 v1, u32x4 v2, u32x4 v3, u32x4 v4) {
         u32x4 *d = reinterpret_cast<u32x4 *>(wst);
@@ -720,13 +703,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
         d[lane + 192] = v3;
         if (has5) d[lane + 256] = v4;
     };
-
-    // This lane's operands in mma_block16: its row's bytes in the slot, its A
-    // fragments (x' of the staged blocks, or zeros).
-    const int c16 = lane & 15, quarter = lane >> 4;
-    const bool zero_lane = (c16 < 2 && quarter >= 2) || ((c16 == 4 || c16 == 5) && quarter < 2);
-    const uint4 *xfrag = zero_lane ? xzero : xs + (c16 & 1) * 4 + (quarter & 1);
-    const uint8_t *rb = wst + (c16 + 16 * (quarter >> 1)) * kBlockBytes + 16 + 8 * (quarter & 1);
 
     float acc[1] = {0.f};
 
@@ -748,10 +724,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
         // used while the second block is still arriving.
         stage_group16(xa, xb, half * 8 + (col >> 2), col & 3, xs, xsum, xmul);
         park(a0, a1, a2, a3, a4);
-        mma_block16(wst, rb, xfrag, lane, 0, xmul[0], xsum, acc[0]);
+        mma_block16(wst, xs, lane, 0, xmul[0], xsum, acc[0]);
         if (i0 + 1 < nb) {
             park(b0, b1, b2, b3, b4);  // after the reads above, in program order
-            mma_block16(wst, rb, xfrag, lane, 8, xmul[1], xsum, acc[0]);
+            mma_block16(wst, xs, lane, 8, xmul[1], xsum, acc[0]);
         }
     }
 
@@ -796,11 +772,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_wide_kernel(Batch bt) {
 }
 
 // ---- 2..4 tokens on the one-token structure ---------------------------------
-// The k-quarter split of mma_block16 with more A rows per row group: MT
-// tokens (2 or 4) put their hi and lo rows at 2t and 2t + 1 of a group of RG
-// rows (RG = 4 for two tokens, 8 for four); group 0 (rows 0..RG-1) carries
-// quarters 0, 1 (row l%16 of the tile), group 1 (rows RG..2RG-1) quarters
-// 2, 3 (row 16 + l%16), each zero where the other group's weights sit.  In
+// v_mfma_f32_16x16x32_f16 with its k-quarters split between two rows of W:
+// quarters 0, 1 carry 16 weights of tile row l%16, quarters 2, 3 the same 16
+// weights of row 16 + l%16, and two accumulating MFMAs cover a 32-weight
+// sub-block of 32 rows.  MT tokens (2 or 4) put their hi and lo rows at 2t and
+// 2t + 1 of a group of RG A rows (RG = 4 for two tokens, 8 for four); group 0
+// (rows 0..RG-1) carries quarters 0, 1, group 1 (rows RG..2RG-1) quarters
+// 2, 3, each zero where the other group's weights sit.  In
 // the 16x16 C layout (lane l, register r -> row 4*(l/16) + r) every lane
 // then finds two tokens of one row of W in registers 0..3:
 //   two tokens:  lanes 0..15 rows 0..15, lanes 16..31 rows 16..31 (lanes
@@ -890,8 +868,12 @@ __device__ __forceinline__ void stage_block_mt(const float4 (&v)[MT], int lane, 
 }
 
 // One parked super-block of 32 rows times the staged activations of MT
-// tokens; this lane's two tokens tb, tb + 1 of its row add into acc[0..1].  rb: the lane's B bytes (as in mma_block16), xa: its A
-// fragments, fragment (sub-block jj, half p) at xa[jj*MT*8 + 2p].
+// tokens; this lane's two tokens tb, tb + 1 of its row add into acc[0..1].
+// rb: the lane's B bytes in the slot (row l%16 for quarters 0, 1, row
+// 16 + l%16 for quarters 2, 3; k-half 8*(quarter & 1)), xa: its A fragments,
+// fragment (sub-block jj, half p) at xa[jj*MT*8 + 2p].  The 6-bit scales and
+// mins enter as small integers; d, dmin and the factor that undoes the
+// activations' scaling are applied once per super-block.
 template <int MT>
 __device__ __forceinline__ void mma_block_mt(const uint8_t *slot, const uint8_t *rb, const uint4 *xa, int lane,
                                              const float *mul_t, const float *sum_t, float (&acc)[2]) {
