@@ -40,6 +40,9 @@ Also reported in the same line:
     per batched launch, weight GB/s, TFLOP/s, kernel family);
   * ``cross_check_*``: agreement of the timed kernels with a second kernel
     family on the last layer (max |difference| / max |value|);
+  * ``vendor_fp16_gemm``: context for the prefill figures, the ROCm library's
+    binary16 GEMM (torch.matmul) on weights already dequantized to binary16,
+    on the same layer shapes at M = 1024 and on an 8192-cubed square;
   * ``other_workloads``: the 1024x1024 GEMV (latency), the Llama-3.2-3B-shaped
     prefill chunk at M = 32 and the Qwen3-14B-shaped pass at M = 4, 16
     (graph replays, weight GB/s against the HBM bound).
@@ -619,6 +622,58 @@ def layer_roofline(ps, ms_layer, kernel, profile):
             "kernel": kernel, "bytes_per_launch": ps.layer_bytes, "avg_launch_us": round(ms_layer * 1e3, 3)}
 
 
+def vendor_fp16_gemm(dev, reps=20):
+    """Context for the prefill figures, not a product path: the ROCm library's
+    binary16 GEMM (torch.matmul, hipBLASLt) on weights already dequantized to
+    binary16 (2 bytes per weight, no Q4_K work), at M = 1024 on the layer
+    shapes of both prefill workloads (seven launches per layer, [K, N]
+    row-major weights) and on an 8192-cubed square product."""
+    import torch
+    from q4k_inputs.workloads import WORKLOADS
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    M = 1024
+    g = torch.Generator(device=dev)
+    g.manual_seed(1024)
+    out = {"M": M, "note": "binary16 weights already dequantized, one library call per projection"}
+    for name in ("qwen3-14b_sweep", "qwen3-8b_prefill_m1024"):
+        layer = WORKLOADS[name].layer
+        xs = {K: torch.randn(M, K, device=dev, dtype=torch.float16, generator=g) for _, _, K in layer}
+        ws = [torch.randn(K, N, device=dev, dtype=torch.float16, generator=g) for _, N, K in layer]
+        ys = [torch.empty(M, N, device=dev, dtype=torch.float16) for _, N, _ in layer]
+
+        def run():
+            for (_, N, K), w, y in zip(layer, ws, ys):
+                torch.matmul(xs[K], w, out=y)
+        ms = timed(run)
+        flops = sum(2 * M * N * K for _, N, K in layer)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name + "_layer"] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                                "frac_of_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+        del xs, ws, ys
+        torch.cuda.empty_cache()
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.float16, generator=g)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.float16, generator=g)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.float16)
+    ms = timed(lambda: torch.matmul(a, b, out=c))
+    tf = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+    out["square_8192"] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / FP16_PEAK_TFLOPS, 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_pass(q4k, dev, wl, steps, weights_from=None):
     """A whole M = 1024 pass (one batched call per layer, then the lm_head),
     eager calls: TFLOP/s, and the roofline of the per-layer launch (x
@@ -741,6 +796,8 @@ def main():
         out["prefill_m1024_qwen3_8b"] = res
         del pp
         torch.cuda.empty_cache()
+        out["vendor_fp16_gemm"] = vendor_fp16_gemm(dev)
+        log(f"vendor binary16 GEMM: {out['vendor_fp16_gemm']}")
     if not args.no_others:
         out["swiglu_gate_up"] = swiglu_figures(q4k, dev, args.steps, args.warmup)
         log(f"swiglu: {out['swiglu_gate_up']}")

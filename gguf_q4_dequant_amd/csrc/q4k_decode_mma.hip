@@ -46,7 +46,9 @@
 //     workgroups on two tiles of four waves (up to 8 tokens) or four tiles of
 //     two waves (9..16), sharing one staged copy of the activations of all
 //     tokens, pass by pass over K.  In both, the waves of a tile add their
-//     partial sums through LDS (no second kernel).
+//     partial sums through LDS; at 9..16 tokens rows longer than 24
+//     super-blocks are also cut into K chunks (one workgroup each), whose
+//     partial tiles a second kernel adds in chunk order.
 #include <limits.h>
 #include <math.h>
 
@@ -80,6 +82,30 @@ __host__ __device__ inline int lds_bytes(int M, int CB, int waves) {
     // weight slots | staged x (R * CB * 1024 B) | X sums and factors (R * CB * 64 B) | padding,
     // R = stage_rows(M)
     return waves * kStage + stage_bytes(M, CB);
+}
+
+// K chunks of a 9..16-token problem.  One eight-wave workgroup per CU (its
+// LDS) walks four tiles over a whole row, so without a split the long rows
+// of a batch set the launch's length: on the Qwen3-14B-shaped layer the 40
+// workgroups of the 68-block down projection run about 3.4 times as long as
+// the 368 of 20-block rows, and most CUs idle for the last half of the
+// launch.  Rows longer than kNpChunkBlocks blocks are cut into near-equal
+// chunks on pass boundaries, one workgroup each, whose partial tiles a
+// second kernel adds in chunk order.  The rule depends on K only (not on
+// M within 9..16), so every chunk of 9..16 tokens of a call sums each output
+// in the same order.  Up to 8 tokens the workgroups are half as large and
+// twice as many, and rows stay whole.
+constexpr int kNpChunkBlocks = 24;
+constexpr int kNpSplitMinTokens = 9;
+__host__ inline int np_splits(int KB, int M) {
+    if (M < kNpSplitMinTokens) return 1;
+    const int most = KB / pass_blocks(M) > 1 ? KB / pass_blocks(M) : 1;  // chunks of at least one pass
+    const int s = (KB + kNpChunkBlocks - 1) / kNpChunkBlocks;
+    return s < 1 ? 1 : (s > most ? most : s);
+}
+// First block of chunk s of S (S: the end), a multiple of CB.
+__host__ __device__ inline int np_chunk_begin(int KB, int S, int s, int CB) {
+    return s >= S ? KB : (s * KB / S) / CB * CB;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
@@ -459,15 +485,22 @@ void decode_mma_kernel(Batch bt) {
     const int p = find_problem(bt, g);
     const DevProblem P = load_problem(bt, p);
     const int N = P.N, K = P.K, M = bt.M;
-    const int KB = K >> 8;
     const int CB = pass_blocks(M);
     const int R2 = 2 * M;  // A rows in use
+    // This workgroup's tiles and K chunk [kb_lo, kb_lo + KB) (the whole row
+    // when the problem is not split); chunks start on a pass boundary.
+    const int splits = P.splits;
+    const int grp = (g - P.tile_begin) / splits;
+    const int sidx = g - P.tile_begin - grp * splits;
+    const int KBr = K >> 8;  // blocks of a whole row
+    const int kb_lo = np_chunk_begin(KBr, splits, sidx, CB);
+    const int KB = np_chunk_begin(KBr, splits, sidx + 1, CB) - kb_lo;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
     const int kw = wave % WPT;  // K lane within the tile
-    const int n0 = ((g - P.tile_begin) * T + wave / WPT) * kCols;
+    const int n0 = (grp * T + wave / WPT) * kCols;
     const bool active = n0 < N;  // the last group of a product may be short
     const int col = lane & 31, half = lane >> 5;
 
@@ -479,8 +512,8 @@ void decode_mma_kernel(Batch bt) {
 
     // Offsets of this lane's five pieces of a super-block from the tile's
     // first row (32-bit: a tile spans 32 rows).
-    const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * KB * kBlockBytes;
-    const uint32_t row_bytes = static_cast<uint32_t>(KB) * kBlockBytes;
+    const uint32_t row_bytes = static_cast<uint32_t>(KBr) * kBlockBytes;
+    const uint8_t *W = P.w + static_cast<size_t>(active ? n0 : 0) * row_bytes + static_cast<size_t>(kb_lo) * kBlockBytes;
     const int nr = active ? N - 1 - n0 : 0;  // last row of the tile, relative
     uint32_t goff[5];
 #pragma unroll
@@ -489,9 +522,9 @@ void decode_mma_kernel(Batch bt) {
         goff[j] = static_cast<uint32_t>(min(f / 9, nr)) * row_bytes + 16u * (f % 9);
     }
     const bool has5 = lane + 256 < kStageChunks;  // fifth piece: lanes 0..31
-    // Piece j of super-block kb of the wave's rows: piece f = lane + 64 j
-    // (f < 288) is bytes 16*(f%9).. of row f/9 (lanes >= 32 re-read a valid
-    // piece for j = 4 and do not park it).
+    // Piece j of super-block kb (counted from the chunk's first) of the
+    // wave's rows: piece f = lane + 64 j (f < 288) is bytes 16*(f%9).. of row
+    // f/9 (lanes >= 32 re-read a valid piece for j = 4 and do not park it).
     auto ld = [&](int kb, int j) -> u32x4 {
         return *reinterpret_cast<const u32x4 *>(W + (static_cast<uint32_t>(kb) * kBlockBytes + goff[j]));
     };
@@ -533,8 +566,8 @@ void decode_mma_kernel(Batch bt) {
     // base), all requests in flight at once and no registers held.  The
     // barrier after the copy waits for them.
     const int n1k = stage_bytes(M, CB) / 1024;
-    auto stage = [&](int c) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c) * n1k * 64;
+    auto stage = [&](int c) {  // c: pass within the chunk
+        const uint4 *src = reinterpret_cast<const uint4 *>(P.part) + static_cast<size_t>(c + kb_lo / CB) * n1k * 64;
         uint4 *dst = reinterpret_cast<uint4 *>(lds + kWLds);
         for (int r = wave; r < n1k; r += kGroupWaves)
             __builtin_amdgcn_global_load_lds(src + r * 64 + lane, dst + r * 64, 16, 0, 0);
@@ -597,7 +630,8 @@ void decode_mma_kernel(Batch bt) {
             // token and row of acc[i]: pair rows (32x32 C layout) or token rows (16x16)
             const int tt = NP == 8 ? 4 * (lane >> 4) + (i & 3) : 4 * (i >> 1) + 2 * half + (i & 1);
             const int nn = NP == 8 ? n0 + 16 * (i >> 2) + (lane & 15) : n;
-            if (tt < M && nn < N) P.y[static_cast<size_t>(tt) * N + nn] = v;
+            // a split problem's y is its partial tiles [splits][M][N]
+            if (tt < M && nn < N) P.y[(static_cast<size_t>(sidx) * M + tt) * N + nn] = v;
         }
     }
 }
@@ -1115,7 +1149,7 @@ hipError_t launch_np(Batch &b, int M, hipStream_t stream) {
     for (int i = 0; i < b.count; ++i) {
         const int tiles = (b.p[i].N + kCols - 1) / kCols;
         b.p[i].tile_begin = groups;
-        b.p[i].tiles = (tiles + T - 1) / T;
+        b.p[i].tiles = (tiles + T - 1) / T * b.p[i].splits;  // one workgroup per (tile group, K chunk)
         groups += b.p[i].tiles;
         lds = max(lds, lds_bytes(M, pass_blocks(M), T * WPT));
     }
@@ -1292,9 +1326,26 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
             }
             which[i] = k;
         }
+        // Partial tiles of the problems whose K is split, after the images.
+        Batch sums = sb;  // real outputs; part -> the partial tiles
+        size_t part_floats = 0;
+        size_t part_at[kMaxBatch];
+        for (int i = 0; i < sb.count; ++i) {
+            sb.p[i].splits = np_splits(sb.p[i].K / kBlockWeights, M);
+            sums.p[i].splits = sb.p[i].splits;
+            part_at[i] = part_floats;
+            if (sb.p[i].splits > 1) part_floats += static_cast<size_t>(sb.p[i].splits) * M * sb.p[i].N;
+        }
+        img_bytes = (img_bytes + 255) & ~static_cast<size_t>(255);
         float *ws = nullptr;
-        hipError_t e = workspace(stream, img_bytes, &ws);
+        hipError_t e = workspace(stream, img_bytes + part_floats * sizeof(float), &ws);
         if (e != hipSuccess) return e;
+        for (int i = 0; i < sb.count; ++i)
+            if (sb.p[i].splits > 1) {
+                float *pt = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + img_bytes) + part_at[i];
+                sb.p[i].y = pt;  // the product kernel writes the chunks' partial tiles
+                sums.p[i].part = pt;
+            }
         int blocks = 0;
         for (int k = 0; k < st.count; ++k) {
             const int KB = st.s[k].K / kBlockWeights;
@@ -1314,6 +1365,10 @@ hipError_t launch_decode_mma(Batch &b, hipStream_t stream) {
         if (e != hipSuccess) return e;
         e = M <= 8 ? launch_np<4>(sb, M, stream) : launch_np<8>(sb, M, stream);
         if (e != hipSuccess) return e;
+        if (part_floats > 0) {
+            e = launch_partial_sums(sums, stream);
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -116,6 +116,10 @@ int check_device();
 hipError_t launch_decode(Batch &b, hipStream_t stream);
 hipError_t launch_prefill(Batch &b, hipStream_t stream);
 hipError_t launch_decode_mma(Batch &b, hipStream_t stream);
+// Second kernel of a split K: for every problem of b with splits > 1, y =
+// the sum of its partial tiles part[0 .. splits)[M][N], added in chunk order
+// (the SwiGLU pairing applied for a gate/up pair).
+hipError_t launch_partial_sums(const Batch &b, hipStream_t stream);
 
 // Library-owned device scratch, per (device, stream, slot), grown on demand,
 // with no guaranteed contents.  Growing never frees the buffer it replaces

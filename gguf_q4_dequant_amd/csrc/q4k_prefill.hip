@@ -988,23 +988,7 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
 }
 
 // The second kernel of a split K: every split problem's chunks summed in order.
-hipError_t launch_split_sum(const Plan &pl, hipStream_t stream) {
-    Batch red;
-    red.count = 0;
-    red.M = pl.sb.M;
-    int blocks = 0;
-    for (int i = 0; i < pl.sb.count; ++i) {
-        const DevProblem &d = pl.sb.p[i];
-        if (d.splits == 1) continue;
-        DevProblem &r = red.p[red.count++];
-        r = d;
-        r.tile_begin = blocks;
-        blocks += d.w2 ? static_cast<int>((static_cast<size_t>(pl.sb.M) * d.n_out + 255) / 256)
-                       : static_cast<int>((static_cast<size_t>(pl.sb.M) * d.N + 1023) / 1024);
-    }
-    hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, sealed(red));
-    return hipGetLastError();
-}
+hipError_t launch_split_sum(const Plan &pl, hipStream_t stream) { return launch_partial_sums(pl.sb, stream); }
 
 // Launch the up-to-32-token kernel (after the binary16 copies of x are queued).
 hipError_t launch_skinny(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
@@ -1107,6 +1091,27 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);
+}
+
+// Every problem of b with splits > 1: y = the sum of its partial tiles
+// part[0..splits)[M][N], added in chunk order (one second kernel).
+hipError_t launch_partial_sums(const Batch &b, hipStream_t stream) {
+    Batch red;
+    red.count = 0;
+    red.M = b.M;
+    int blocks = 0;
+    for (int i = 0; i < b.count; ++i) {
+        const DevProblem &d = b.p[i];
+        if (d.splits <= 1) continue;
+        DevProblem &r = red.p[red.count++];
+        r = d;
+        r.tile_begin = blocks;
+        blocks += d.w2 ? static_cast<int>((static_cast<size_t>(b.M) * d.n_out + 255) / 256)
+                       : static_cast<int>((static_cast<size_t>(b.M) * d.N + 1023) / 1024);
+    }
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, stream, sealed(red));
+    return hipGetLastError();
 }
 
 }  // namespace q4k

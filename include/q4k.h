@@ -117,14 +117,17 @@ int q4k_matmul_batched(const q4k_problem *problems, int count, int M, hipStream_
  * arguments, checks, results (bit for bit) and kernels as
  * q4k_matmul_batched; the only difference is where the kernels' scratch
  * lives (binary16 copies of x and split-K partial sums of the prefill
- * family, staged activations of 5..16-token decode, split-K partials of the
- * fp32 GEMV family): not in the library's growing per-stream workspace but
+ * family, staged activations and K-chunk partial sums of 5..16-token decode,
+ * split-K partials of the fp32 GEMV family): not in the library's growing
+ * per-stream workspace but
  * in one fixed device array of Q4K_NOALLOC_SCRATCH_BYTES per GPU, created
  * with the library's code on that GPU and held until the process ends.  The
  * call makes no hipMalloc, hipFree or other allocating call.
  *   Scratch needed, roughly: prefill (M > 16) 2*M*K bytes per distinct (x, K)
  *   plus 4*splits*M*N per problem whose K is split (K > 12288 at M > 512);
- *   5..16 tokens: about 4.3*M*K bytes per distinct (x, K); 1..4 tokens: none.
+ *   5..16 tokens: about 4.3*M*K bytes per distinct (x, K), plus at 9..16
+ *   tokens 4*splits*M*N per problem with K > 6144 (splits = ceil(K/6144));
+ *   1..4 tokens: none.
  *   128 MiB covers, for example, a Qwen3-8B-shaped layer at M = 1024 or the
  *   17408-deep down projection alone at M = 1024.
  *   Errors: as for q4k_matmul_batched, and Q4K_ERR_SCRATCH (nothing enqueued)

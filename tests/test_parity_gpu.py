@@ -45,6 +45,9 @@ DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 
                  # tiles past N, one-block and three-block rows, long rows in passes of four
                  (6, 33, 1280), (7, 65, 256), (12, 97, 1024), (13, 161, 2304), (15, 40, 256),
                  (10, 33, 768), (11, 50, 17408),
+                 # 9..16 tokens, rows longer than 24 blocks cut into K chunks on pass
+                 # boundaries: 12 + 13 blocks (a part pass), 16 + 16 + 17
+                 (14, 70, 6400), (9, 40, 12544),
                  # 2..4 tokens on the one-token structure: one-block rows (a tile per wave),
                  # a single row, long rows split over sixteen waves
                  (4, 33, 256), (3, 1, 512), (2, 97, 17408)]
@@ -146,6 +149,44 @@ def test_row_split_invariance(path, M, cuts, bitwise):
         y_ref, s = oracle.matmul(w, x, N, K)
         check_close(parts, y_ref, s, tol, "row chunks")
         check_close(y, y_ref, s, tol, "all rows")
+
+
+def test_row_split_invariance_on_k_chunks():
+    """9..16 tokens cut rows longer than 24 blocks into K chunks by K alone:
+    a forced 29-token call (16 + 13 tokens) and calls on 13 and 16 of its
+    rows sum every output in the same order (three chunks of a 68-block row)."""
+    M, N, K = 29, 140, 17408
+    w, x = _inputs(M, N, K, 7)
+    y = _run(w, x, N, DEC)
+    parts = np.concatenate([_run(w, x[:13], N, DEC), _run(w, x[13:], N, DEC)])
+    assert np.array_equal(parts, y)
+    y_ref, s = oracle.matmul_cols(w, x, N, K, np.arange(0, N, 9))
+    check_close(y[:, ::9], y_ref, s, DECODE_TOL, "29 tokens, K chunks")
+
+
+@pytest.mark.parametrize("M", [12, 16])
+def test_batch_with_k_chunks(M):
+    """A batch mixing rows cut into three, two and one K chunk (and a
+    problem of one row): each output equals its single call bit for bit, and
+    the chunked problems match the oracle on sampled columns."""
+    import torch
+    shapes = [(97, 17408), (1, 6400), (300, 6400), (130, 1024), (33, 17408)]
+    xs = {K: to_dev(qi.random_x(M, K, seed=qi.tensor_seed(qi.BASE_SEED, 720, M, K))) for K in (1024, 6400, 17408)}
+    host, probs = [], []
+    for i, (N, K) in enumerate(shapes):
+        w = qi.random_q4k(N, K, seed=qi.tensor_seed(qi.BASE_SEED, 721, M, i))
+        host.append(w)
+        probs.append((to_dev(w), xs[K], torch.empty((M, N), dtype=torch.float32, device=device())))
+    q4k.matmul_batched(probs)
+    singles = [q4k.matmul(w, x) for w, x, _ in probs]
+    torch.cuda.synchronize()
+    for i, ((_, _, y), ys) in enumerate(zip(probs, singles)):
+        assert torch.equal(y, ys), f"problem {i}"
+    for i in (0, 2, 4):
+        N, K = shapes[i]
+        cols = np.arange(0, N, 11)
+        y_ref, s = oracle.matmul_cols(host[i], xs[K].cpu().numpy(), N, K, cols)
+        check_close(probs[i][2].cpu().numpy()[:, cols], y_ref, s, DECODE_TOL, f"problem {i}")
 
 
 @pytest.mark.parametrize("path", [DEC, PRE, GEMV])
