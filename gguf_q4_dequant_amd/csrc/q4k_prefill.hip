@@ -630,6 +630,26 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
 // y = sum over chunks of the partial sums, in chunk order, for split problems
 // (four outputs per thread; gate/up pairs: silu(g) * u of the two sums, one
 // output per thread).
+// Chunk partials are requested eight at a time before any of them is added
+// (a loop of one load and one add per chunk pays a memory round trip per
+// chunk), then added in chunk order: the same sums, bit for bit, as one chunk
+// at a time.  A chunk past the last is neither loaded nor added.
+constexpr int kSumGroup = 8;
+template <class T, class Load, class Add>
+__device__ __forceinline__ T sum_chunks(int splits, Load load, Add add) {
+    T v = load(0);
+    for (int c0 = 1; c0 < splits; c0 += kSumGroup) {
+        T u[kSumGroup];
+#pragma unroll
+        for (int j = 0; j < kSumGroup; ++j)
+            if (c0 + j < splits) u[j] = load(c0 + j);
+#pragma unroll
+        for (int j = 0; j < kSumGroup; ++j)
+            if (c0 + j < splits) v = add(v, u[j]);
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
     const int p = find_problem(bt, static_cast<int>(blockIdx.x));
     const DevProblem P = load_problem(bt, p);
@@ -641,34 +661,30 @@ __global__ __launch_bounds__(256) void split_sum_kernel(Batch bt) {
         const int n = static_cast<int>(o - m * P.n_out);
         const size_t vg = m * P.N + (((n >> 4) << 5) | (n & 15));  // its gate row; up is 16 further
         const size_t total = static_cast<size_t>(bt.M) * P.N;
-        float g = P.part[vg], u = P.part[vg + 16];
-        for (int c = 1; c < P.splits; ++c) {
-            g += P.part[static_cast<size_t>(c) * total + vg];
-            u += P.part[static_cast<size_t>(c) * total + vg + 16];
-        }
-        P.y[o] = swiglu(g, u);
+        const float2 gu = sum_chunks<float2>(
+            P.splits,
+            [&](int c) {
+                const float *q = P.part + static_cast<size_t>(c) * total + vg;
+                return make_float2(q[0], q[16]);
+            },
+            [](float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); });
+        P.y[o] = swiglu(gu.x, gu.y);
         return;
     }
     const size_t e = (static_cast<size_t>(static_cast<int>(blockIdx.x) - P.tile_begin) * 256 + threadIdx.x) * 4;
     const size_t total = static_cast<size_t>(bt.M) * P.N;
     if (e >= total) return;
     if (e + 4 <= total && (total & 3) == 0) {
-        float4 v = *reinterpret_cast<const float4 *>(P.part + e);
-        for (int c = 1; c < P.splits; ++c) {
-            const float4 u = *reinterpret_cast<const float4 *>(P.part + static_cast<size_t>(c) * total + e);
-            v.x += u.x;
-            v.y += u.y;
-            v.z += u.z;
-            v.w += u.w;
-        }
-        *reinterpret_cast<float4 *>(P.y + e) = v;
+        *reinterpret_cast<float4 *>(P.y + e) = sum_chunks<float4>(
+            P.splits,
+            [&](int c) { return *reinterpret_cast<const float4 *>(P.part + static_cast<size_t>(c) * total + e); },
+            [](float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); });
         return;
     }
-    for (size_t i = e; i < min(e + 4, total); ++i) {
-        float v = P.part[i];
-        for (int c = 1; c < P.splits; ++c) v += P.part[static_cast<size_t>(c) * total + i];
-        P.y[i] = v;
-    }
+    for (size_t i = e; i < min(e + 4, total); ++i)
+        P.y[i] = sum_chunks<float>(
+            P.splits, [&](int c) { return P.part[static_cast<size_t>(c) * total + i]; },
+            [](float a, float b) { return a + b; });
 }
 
 // ---- up to 32 tokens: W dequantized straight into the MFMA operands ------
