@@ -694,7 +694,7 @@ def prefill_pass(q4k, dev, wl, steps, weights_from=None):
            "cross_check_vs_decode_family": xcheck_p,
            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / FP16_PEAK_TFLOPS, 4),
-                        "kernel": "per-layer batched launch (convert_x_kernel + prefill_kernel)",
+                        "kernel": "per-layer batched launch (convert_x_kernel + prefill_pc_kernel)",
                         "flops_per_launch": pp.layer_flops, "avg_launch_us": round(ms_pl * 1e3, 2)}}
     log(f"prefill {wl.name}: {ms_p:.2f} ms/step {tflops:.1f} TFLOP/s; layer launch {ms_pl * 1e3:.1f} us "
         f"-> {ach:.1f} TFLOP/s; cross-check {xcheck_p:.2e}")

@@ -108,6 +108,10 @@ constexpr SplitRule kMidSplit = {16, 16};
 // partial sums and the second launch cost more than they even out (a
 // K = 12288 row cut in two: +10% at M = 1024).
 constexpr SplitRule kBigSplit = {32, 48};
+// More than 128 tokens on producer/consumer tiles (prefill_pc_kernel) instead
+// of the 256x256 tiles.
+constexpr bool kProducerConsumer = true;
+constexpr int kPcBN = 256;
 
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -627,6 +631,256 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
     for_each_out([&](size_t e, int m, float v) { part[e] = v * xfac[m]; });
 }
 
+// ---- many tokens, producer and consumer waves ------------------------------
+// 256x128 tiles (256 rows of x, 128 rows of W) on twelve waves: eight consumer
+// waves (two per SIMD), each owning a 64x64 block of accumulators, do nothing
+// but fragment reads and MFMAs; four producer waves (one per SIMD) move the
+// next k-step of x into LDS and dequantize the next k-step of W into it, two
+// threads per W row, with the same rounding as prefill_kernel (each weight
+// rounded once from its exact value).  Both LDS buffers alternate by step:
+// while the consumers multiply step s from buffer s % 2, the producers fill
+// the other buffer with step s + 1 from registers and request step s + 3.
+// One barrier per step (every wave reaches the same number).  Every output
+// sums its k in the same order as prefill_kernel, so the two agree bit for
+// bit.
+template <int BN_>
+struct PcShape {
+    static constexpr int BM = 256, BN = BN_;
+    static constexpr int kLoaders = 256;        // producer threads (four waves)
+    static constexpr int kChunks = 2 * BN / kLoaders;  // 16-byte quant chunks of a step per producer thread
+    static constexpr int kConsumers = 8;        // consumer waves
+    static constexpr int kThreads = 64 * kConsumers + kLoaders;
+    static constexpr int WN = BN / 64, WM = kConsumers / WN;
+    static constexpr int TM = BM / WM, TN = 64, TA = TM / 32, TB = 2;
+    static constexpr int XC = BM * 8 / kLoaders;  // 16-byte x chunks per producer thread per step
+    static constexpr int XROWS = kLoaders / 8;
+    static constexpr size_t kLds = 2 * static_cast<size_t>(BM + BN) * 8 * 16;
+    static_assert(BN == 128 || BN == 256, "one or two quant chunks per producer thread");
+};
+
+// Workgroup barrier that orders LDS accesses only: the fence of
+// __syncthreads also waits for every outstanding global load, which would
+// cancel the producers' requests for later steps at every step.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int BN>
+__global__ __launch_bounds__(PcShape<BN>::kThreads) void prefill_pc_kernel(Batch bt, GemmArgs ga) {
+    using S = PcShape<BN>;
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
+    auto As = [&](int b) { return lds4 + b * (S::BM + S::BN) * 8; };
+    auto Bs = [&](int b) { return lds4 + b * (S::BM + S::BN) * 8 + S::BM * 8; };
+
+    const int xcd = static_cast<int>(blockIdx.x) % kXcds;
+    const int tile = ga.xcd_first[xcd] + static_cast<int>(blockIdx.x) / kXcds;
+    if (tile >= ga.xcd_first[xcd + 1]) return;
+
+    const int p = find_problem(bt, tile);
+    const DevProblem P = load_problem(bt, p);
+    const _Float16 *__restrict__ XH = ga.xh[p];
+    const uint8_t *__restrict__ W = P.w;
+    const int N = P.N;
+    const int K = P.K;
+    const int M = bt.M;
+    const int KB = K >> 8;
+    const int splits = P.splits;
+    const int local = (tile - P.tile_begin) / splits;
+    const int sidx = tile - P.tile_begin - local * splits;
+    const int kb0 = sidx * KB / splits;
+    const int kbn = (sidx + 1) * KB / splits - kb0;  // >= 1
+    const int n_tiles = (N + S::BN - 1) / S::BN;
+    const int tm0 = (local / n_tiles) * S::BM;
+    const int tn0 = (local % n_tiles) * S::BN;
+    const int steps = kbn * 4;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+
+    if (wave >= S::kConsumers) {
+        // ---- producer: thread lt moves x chunks f = lt + 256 j and
+        // dequantizes quant chunk lt % 2 of W row lt / 2 (128-row tiles) or
+        // both chunks of W row lt (256-row tiles).
+        const int lt = t - 64 * S::kConsumers;
+        const _Float16 *xcol = XH + static_cast<size_t>(kb0) * kBlockWeights + 8 * (lt & 7);
+        const int xr0 = tm0 + (lt >> 3);
+        const int wr = S::kChunks == 1 ? lt >> 1 : lt, wh = S::kChunks == 1 ? lt & 1 : 0;
+        const int vrow = min(tn0 + wr, N - 1);
+        const uint8_t *wrow =
+            P.w2 ? (pair_is_up(vrow) ? P.w2 : W) + (static_cast<size_t>(pair_row(vrow, P.n_out)) * KB + kb0) * kBlockBytes
+                 : W + (static_cast<size_t>(vrow) * KB + kb0) * kBlockBytes;
+        // Two register slots (named, of a vector type: arrays of uint4
+        // indexed by slot end up in scratch): slot 0 holds the even steps,
+        // slot 1 the odd ones; requests past the last step re-read the last
+        // step.
+        typedef uint32_t u32x4p __attribute__((ext_vector_type(4)));
+        u32x4p x0[S::XC], x1[S::XC];
+        u32x4p wq0[S::kChunks], wq1[S::kChunks], whd0;
+        RowScales rs;
+        auto load = [&](u32x4p (&xr)[S::XC], u32x4p (&wq)[S::kChunks], bool hdr, int s_req) {
+            const int s = min(s_req, steps - 1);
+#pragma unroll
+            for (int j = 0; j < S::XC; ++j) {
+                const size_t row = static_cast<size_t>(min(xr0 + S::XROWS * j, M - 1));
+                xr[j] = *reinterpret_cast<const u32x4p *>(xcol + row * K + static_cast<size_t>(s) * kBK);
+            }
+            const uint8_t *blk = wrow + static_cast<size_t>(s >> 2) * kBlockBytes;
+            if (hdr) whd0 = *reinterpret_cast<const u32x4p *>(blk);  // even steps carry group 0's header
+#pragma unroll
+            for (int h = 0; h < S::kChunks; ++h)
+                wq[h] = *reinterpret_cast<const u32x4p *>(blk + 16 + 32 * (s & 3) + 16 * (wh + h));
+        };
+        auto store = [&](const u32x4p (&xr)[S::XC], const u32x4p (&wqs)[S::kChunks], int s, uint4 *A, uint4 *B) {
+#pragma unroll
+            for (int j = 0; j < S::XC; ++j)
+                A[swz((lt >> 3) + S::XROWS * j, lt & 7)] = make_uint4(xr[j].x, xr[j].y, xr[j].z, xr[j].w);
+            const int g = s & 3;
+            if (g == 0) decode_header(make_uint4(whd0.x, whd0.y, whd0.z, whd0.w), rs);
+            const uint32_t scw = g < 2 ? rs.scA : rs.scB;
+            const uint32_t mnw = g < 2 ? rs.mnA : rs.mnB;
+            const int sh = (g & 1) * 16;
+            const float a_lo = rs.d * 16777216.0f * static_cast<float>((scw >> sh) & 0xFFu);
+            const float a_hi = rs.d * 1048576.0f * static_cast<float>((scw >> (sh + 8)) & 0xFFu);
+            const float c_lo = rs.dmin * static_cast<float>((mnw >> sh) & 0xFFu);
+            const float c_hi = rs.dmin * static_cast<float>((mnw >> (sh + 8)) & 0xFFu);
+#pragma unroll
+            for (int h = 0; h < S::kChunks; ++h) {
+                const u32x4p wq = wqs[h];
+                const int c = 2 * (wh + h);  // 16-byte B chunks c, c + 1 (low nibbles) and 4 + c, 5 + c (high)
+                const WordWeights p0 = dequant_word(wq.x, a_lo, c_lo, a_hi, c_hi);
+                const WordWeights q0 = dequant_word(wq.y, a_lo, c_lo, a_hi, c_hi);
+                B[swz(wr, c)] = make_uint4(p0.lo01, p0.lo23, q0.lo01, q0.lo23);
+                B[swz(wr, 4 + c)] = make_uint4(p0.hi01, p0.hi23, q0.hi01, q0.hi23);
+                const WordWeights p1 = dequant_word(wq.z, a_lo, c_lo, a_hi, c_hi);
+                const WordWeights q1 = dequant_word(wq.w, a_lo, c_lo, a_hi, c_hi);
+                B[swz(wr, c + 1)] = make_uint4(p1.lo01, p1.lo23, q1.lo01, q1.lo23);
+                B[swz(wr, 5 + c)] = make_uint4(p1.hi01, p1.hi23, q1.hi01, q1.hi23);
+            }
+        };
+        load(x0, wq0, true, 0);
+        store(x0, wq0, 0, As(0), Bs(0));
+        load(x1, wq1, false, 1);
+        load(x0, wq0, true, 2);
+        lds_barrier();
+        // Step s: the consumers multiply buffer s % 2; step s + 1 goes from
+        // its slot into the other buffer and the slot is refilled with step
+        // s + 3.  Unrolled by two (steps is a multiple of four).
+        for (int s = 0; s < steps; s += 2) {
+            store(x1, wq1, s + 1, As(1), Bs(1));
+            load(x1, wq1, false, s + 3);
+            lds_barrier();
+            store(x0, wq0, s + 2, As(0), Bs(0));  // past the last step: the idle buffer, never read
+            load(x0, wq0, true, s + 4);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---- consumer: a 64x64 block of the tile, rows 64 * (wave / 2).
+    const int wm = wave / S::WN, wn = wave % S::WN;
+    float16v acc[S::TA][S::TB];
+#pragma unroll
+    for (int a = 0; a < S::TA; ++a)
+#pragma unroll
+        for (int b = 0; b < S::TB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    auto read_frags = [&](int kk, const uint4 *A, const uint4 *B, half8 *af, half8 *bf) {
+        const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a)
+            af[a] = __builtin_bit_cast(half8, A[swz(S::TM * wm + 32 * a + (lane & 31), c)]);
+#pragma unroll
+        for (int b = 0; b < S::TB; ++b)
+            bf[b] = __builtin_bit_cast(half8, B[swz(S::TN * wn + 32 * b + (lane & 31), c)]);
+    };
+    lds_barrier();
+    for (int s = 0; s < steps; ++s) {
+        const uint4 *A = As(s & 1), *B = Bs(s & 1);
+        if constexpr (S::TA == 2) {
+            // 64x64 blocks: the next slice's fragments are read during this slice's MFMAs
+            half8 af[2][S::TA], bf[2][S::TB];
+            read_frags(0, A, B, af[0], bf[0]);
+#pragma unroll
+            for (int q = 0; q < kBK / 16; ++q) {
+                if (q + 1 < kBK / 16) read_frags(q + 1, A, B, af[(q + 1) & 1], bf[(q + 1) & 1]);
+#pragma unroll
+                for (int a = 0; a < S::TA; ++a)
+#pragma unroll
+                    for (int b = 0; b < S::TB; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q & 1][a], bf[q & 1][b], acc[a][b], 0, 0, 0);
+            }
+        } else {
+            // 128x64 blocks (128 accumulators): one slice's fragments at a
+            // time, so that three waves fit a SIMD; the other consumer wave
+            // of the SIMD covers the reads.  (Requesting each fragment of
+            // the next slice right after its last MFMA let the compiler keep
+            // two of them in registers and wait before nearly every MFMA.)
+#pragma unroll
+            for (int q = 0; q < kBK / 16; ++q) {
+                half8 af[S::TA], bf[S::TB];
+                read_frags(q, A, B, af, bf);
+#pragma unroll
+                for (int a = 0; a < S::TA; ++a)
+#pragma unroll
+                    for (int b = 0; b < S::TB; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lds_barrier();
+    }
+
+    // D layout of a 32x32 MFMA tile: lane l, register r ->
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    auto for_each_out = [&](auto &&f) {
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a) {
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b) {
+                const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, m, acc[a][b][r]);
+                }
+            }
+        }
+    };
+    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
+    if (P.w2 && splits == 1) {
+        const int n_out = P.n_out;
+        const bool up = (lane & 16) != 0;
+#pragma unroll
+        for (int a = 0; a < S::TA; ++a) {
+#pragma unroll
+            for (int b = 0; b < S::TB; ++b) {
+                const int n = ((tn0 + S::TN * wn + 32 * b) >> 1) + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int m0 = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const float v0 = acc[a][b][r] * xfac[min(m0, M - 1)];
+                    const float v1 = acc[a][b][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float got = __shfl_xor(up ? v0 : v1, 16);
+                    const int m = up ? m0 + 1 : m0;
+                    if (m < M && n < n_out)
+                        P.y[static_cast<size_t>(m) * n_out + n] = up ? swiglu(got, v1) : swiglu(v0, got);
+                }
+            }
+        }
+        return;
+    }
+    if (splits == 1) {
+        for_each_out([&](size_t e, int m, float v) { P.y[e] = v * xfac[m]; });
+        return;
+    }
+    float *part = P.part + static_cast<size_t>(sidx) * M * N;
+    for_each_out([&](size_t e, int m, float v) { part[e] = v * xfac[m]; });
+}
+
 // y = sum over chunks of the partial sums, in chunk order, for split problems
 // (four outputs per thread; gate/up pairs: silu(g) * u of the two sums, one
 // output per thread).
@@ -1006,6 +1260,29 @@ hipError_t launch_gemm(Plan &pl, const _Float16 *const *xh, float *part, hipStre
 // The second kernel of a split K: every split problem's chunks summed in order.
 hipError_t launch_split_sum(const Plan &pl, hipStream_t stream) { return launch_partial_sums(pl.sb, stream); }
 
+// Launch the producer/consumer tiles (after the binary16 copies of x are queued).
+template <int BN>
+hipError_t launch_pc(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
+    using S = PcShape<BN>;
+    hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(prefill_pc_kernel<BN>), static_cast<int>(S::kLds));
+    if (e != hipSuccess) return e;
+    if (pl.grid == 0) return hipSuccess;
+    GemmArgs ga;
+    for (int c = 0; c <= kXcds; ++c) ga.xcd_first[c] = pl.xcd_first[c];
+    for (int i = 0; i < pl.sb.count; ++i) {
+        DevProblem &d = pl.sb.p[i];
+        ga.xh[i] = xh[pl.order[i]];
+        if (d.splits > 1) {
+            d.part = part;
+            part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
+        }
+    }
+    hipLaunchKernelGGL(prefill_pc_kernel<BN>, dim3(pl.grid), dim3(S::kThreads), S::kLds, stream, sealed(pl.sb), ga);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || pl.partial_floats == 0) return err;
+    return launch_split_sum(pl, stream);
+}
+
 // Launch the up-to-32-token kernel (after the binary16 copies of x are queued).
 hipError_t launch_skinny(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
     if (pl.grid == 0) return hipSuccess;
@@ -1064,6 +1341,8 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
         if (narrow) make_plan<NarrowTile>(b, kSmallSplit, pl);
     } else if (mid)
         make_plan<MidTile>(b, kMidSplit, pl);
+    else if (kProducerConsumer)
+        make_plan<PcShape<kPcBN>>(b, b.M <= kMidMaxM ? kMidSplit : kBigSplit, pl);
     else
         make_plan<BigTile>(b, b.M <= kMidMaxM ? kMidSplit : kBigSplit, pl);
     // Workspace: the binary16 activations, then the split-K partial sums.
@@ -1106,6 +1385,7 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     if (narrow) return launch_gemm<NarrowTile, kSmallWaves>(pl, xh, part, stream);
     if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);
+    if (kProducerConsumer) return launch_pc<kPcBN>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);
 }
 
