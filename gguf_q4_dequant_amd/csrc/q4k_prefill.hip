@@ -975,9 +975,25 @@ constexpr int kSkPieces = kSkSlot / 16;                    // 16-byte pieces of 
 constexpr int kSkLoads = (kSkPieces + 63) / 64;            // pieces per lane
 constexpr int kSkXBytes = 32 * kBlockWeights * 2;          // one super-block of x: 32 rows of binary16
 constexpr int kSkinnyMaxM = 32;
-struct SkinnyTile {  // the plan needs the tile's extent only
-    static constexpr int BM = 32, BN = kSkWaves * kSkRows;
+// 33..64 tokens (two 32-token blocks): every dequantized weight feeds both
+// blocks' MFMAs; eight waves, one workgroup per CU (x double-buffered for 64
+// rows, 100 KB of LDS), at most 256 VGPRs.  Against 32x128 / 32x64 tiles
+// (Qwen3-14B-shaped layer at M = 33, 48, 64: 154, 158, 161 -> 120, 131, 142
+// us with K chunks of four blocks; Llama-3.2-3B-shaped layer at M = 33, 64:
+// 54 -> 46, 54 -> 52 us).
+constexpr int kSk2Waves = 8;
+constexpr int kSk2MaxM = 64;
+constexpr bool kSkinny2 = true;
+// K chunks of at most eight blocks for its 256-row workgroups (M = 40, 64:
+// Qwen3-14B-shaped layer 127, 142 us with four, 110, 120 with eight, 101,
+// 110 with twelve, 111, 121 with sixteen; Llama-3.2-3B-shaped layer 47.5,
+// 51 with four, 41, 44 with eight, 49, 50 with twelve: eight is the rule).
+constexpr SplitRule kSkinny2Split = {8, 0};
+template <int TB>
+struct SkinnyShape {  // the plan needs the tile's extent only
+    static constexpr int BM = 32 * TB, BN = (TB == 1 ? kSkWaves : kSk2Waves) * kSkRows;
 };
+using SkinnyTile = SkinnyShape<1>;
 // K chunks of at most four super-blocks (Llama-3.2-3B-shaped layer at
 // M = 32: 36.6 us, against 40.7 with six and 38.9 with eight; the larger
 // Qwen3-14B-shaped layer prefers eight, 89.2 against 93.6 us, but a rule by
@@ -986,10 +1002,14 @@ constexpr SplitRule kSkinnySplit = {4, 0};
 
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(3)))  // at most 168 VGPRs
+// TB: 32-token blocks (1: four waves, three per SIMD; 2: eight waves, two per SIMD).
+template <int TB>
+__global__ __launch_bounds__(64 * (TB == 1 ? kSkWaves : kSk2Waves))
+__attribute__((amdgpu_waves_per_eu(TB == 1 ? 3 : 2)))  // at most 168 / 256 VGPRs
 void skinny_kernel(Batch bt, GemmArgs ga) {
-    __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][kSkXBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t wslot[kSkWaves][kSkSlot];
+    constexpr int WAVES = TB == 1 ? kSkWaves : kSk2Waves;
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][TB * kSkXBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t wslot[WAVES][kSkSlot];
     const int xcd = static_cast<int>(blockIdx.x) % kXcds;
     const int tile = ga.xcd_first[xcd] + static_cast<int>(blockIdx.x) / kXcds;
     if (tile >= ga.xcd_first[xcd + 1]) return;
@@ -1007,7 +1027,7 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
     const int lane = t & 63;
     const int wave = t >> 6;
     const int h = lane >> 5;  // k-half of each slice this lane feeds
-    const int n0 = local * SkinnyTile::BN + kSkRows * wave;  // this wave's first row
+    const int n0 = local * SkinnyShape<TB>::BN + kSkRows * wave;  // this wave's first row
 
     // Piece j of this lane: piece f = lane + 64 j of the wave's rows, bytes
     // 16 * (f % 9) of row f / 9 (pieces past the slot re-read a valid piece
@@ -1033,11 +1053,12 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
         for (int j = 0; j < kSkLoads; ++j)
             if (kSkPieces % 64 == 0 || lane + 64 * j < kSkPieces) d[lane + 64 * j] = v[j];
     };
-    // x of block b: 1024 pieces of 16 bytes, four per thread, through
-    // registers (position pos = 256*wave + 64*i + lane holds row m = pos/32,
-    // chunk (pos % 32) ^ (m % 16)).  (Moved by global-to-LDS loads instead,
-    // the compiler cannot tell the next step's copy from the current step's
-    // reads and waits for every load of the wave before the multiply.)
+    // x of block b: 1024 pieces of 16 bytes per 32 token rows, four per
+    // thread, through registers (position pos = 256*wave + 64*i + lane holds
+    // row m = pos/32, chunk (pos % 32) ^ (m % 16)).  (Moved by global-to-LDS
+    // loads instead, the compiler cannot tell the next step's copy from the
+    // current step's reads and waits for every load of the wave before the
+    // multiply.)
     auto ldx = [&](int b, u32x4s (&v)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1051,17 +1072,19 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4s *>(xbuf[buf])[256 * wave + 64 * i + lane] = v[i];
     };
+    static_assert(4 * kSkWaves * 64 * TB == 64 * WAVES * 4, "x pieces: four per thread");
 
-    float16v acc[kSkTiles];
+    float16v acc[kSkTiles][TB];
 #pragma unroll
     for (int tt = 0; tt < kSkTiles; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tt][r] = 0.f;
+        for (int u = 0; u < TB; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tt][u][r] = 0.f;
     const int arow = lane & 31;  // A row (token) this lane feeds, and its W row in each tile
     // One super-block from the wave's slot and x buffer xb: every x fragment
     // is read once and multiplies the wave's tiles.
     auto compute = [&](const uint8_t *xb) {
-        const uint4 *xa = reinterpret_cast<const uint4 *>(xb) + arow * 32;
         const int sw = arow & 15;
         RowScales rs[kSkTiles];
 #pragma unroll
@@ -1070,10 +1093,15 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s0 = 4 * i;
-            const half8 x0 = __builtin_bit_cast(half8, xa[(2 * s0 + h) ^ sw]);
-            const half8 x1 = __builtin_bit_cast(half8, xa[(2 * s0 + 2 + h) ^ sw]);
-            const half8 x2 = __builtin_bit_cast(half8, xa[(2 * s0 + 4 + h) ^ sw]);
-            const half8 x3 = __builtin_bit_cast(half8, xa[(2 * s0 + 6 + h) ^ sw]);
+            half8 x0[TB], x1[TB], x2[TB], x3[TB];
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {  // token block u: rows 32u .. 32u + 31 of x
+                const uint4 *xa = reinterpret_cast<const uint4 *>(xb) + (32 * u + arow) * 32;
+                x0[u] = __builtin_bit_cast(half8, xa[(2 * s0 + h) ^ sw]);
+                x1[u] = __builtin_bit_cast(half8, xa[(2 * s0 + 2 + h) ^ sw]);
+                x2[u] = __builtin_bit_cast(half8, xa[(2 * s0 + 4 + h) ^ sw]);
+                x3[u] = __builtin_bit_cast(half8, xa[(2 * s0 + 6 + h) ^ sw]);
+            }
 #pragma unroll
             for (int tt = 0; tt < kSkTiles; ++tt) {
                 const uint8_t *row = wslot[wave] + (32 * tt + arow) * kBlockBytes;
@@ -1094,10 +1122,13 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
                 const half8 b1 = __builtin_bit_cast(half8, make_uint4(q0.lo01, q0.lo23, q1.lo01, q1.lo23));
                 const half8 b2 = __builtin_bit_cast(half8, make_uint4(p0.hi01, p0.hi23, p1.hi01, p1.hi23));
                 const half8 b3 = __builtin_bit_cast(half8, make_uint4(q0.hi01, q0.hi23, q1.hi01, q1.hi23));
-                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0, b0, acc[tt], 0, 0, 0);
-                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1, b1, acc[tt], 0, 0, 0);
-                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x2, b2, acc[tt], 0, 0, 0);
-                acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x3, b3, acc[tt], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < TB; ++u) {
+                    acc[tt][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x0[u], b0, acc[tt][u], 0, 0, 0);
+                    acc[tt][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x1[u], b1, acc[tt][u], 0, 0, 0);
+                    acc[tt][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x2[u], b2, acc[tt][u], 0, 0, 0);
+                    acc[tt][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x3[u], b3, acc[tt][u], 0, 0, 0);
+                }
             }
         }
     };
@@ -1132,13 +1163,17 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
         for (int tt = 0; tt < kSkTiles; ++tt) {
             const int n = ((n0 + 32 * tt) >> 1) + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int m0 = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const float v0 = acc[tt][r] * xfac[min(m0, M - 1)];
-                const float v1 = acc[tt][r + 1] * xfac[min(m0 + 1, M - 1)];
-                const float got = __shfl_xor(up ? v0 : v1, 16);
-                const int m = up ? m0 + 1 : m0;
-                if (m < M && n < n_out) P.y[static_cast<size_t>(m) * n_out + n] = up ? swiglu(got, v1) : swiglu(v0, got);
+            for (int u = 0; u < TB; ++u) {
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int m0 = 32 * u + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const float v0 = acc[tt][u][r] * xfac[min(m0, M - 1)];
+                    const float v1 = acc[tt][u][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float got = __shfl_xor(up ? v0 : v1, 16);
+                    const int m = up ? m0 + 1 : m0;
+                    if (m < M && n < n_out)
+                        P.y[static_cast<size_t>(m) * n_out + n] = up ? swiglu(got, v1) : swiglu(v0, got);
+                }
             }
         }
         return;
@@ -1148,9 +1183,12 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
     for (int tt = 0; tt < kSkTiles; ++tt) {
         const int n = n0 + 32 * tt + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < M && n < N) dst[static_cast<size_t>(m) * N + n] = acc[tt][r] * xfac[m];
+        for (int u = 0; u < TB; ++u) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * u + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) dst[static_cast<size_t>(m) * N + n] = acc[tt][u][r] * xfac[m];
+            }
         }
     }
 }
@@ -1283,7 +1321,9 @@ hipError_t launch_pc(Plan &pl, const _Float16 *const *xh, float *part, hipStream
     return launch_split_sum(pl, stream);
 }
 
-// Launch the up-to-32-token kernel (after the binary16 copies of x are queued).
+// Launch the up-to-32-token kernel, or the 33..64-token one (TB = 2), after
+// the binary16 copies of x are queued.
+template <int TB>
 hipError_t launch_skinny(Plan &pl, const _Float16 *const *xh, float *part, hipStream_t stream) {
     if (pl.grid == 0) return hipSuccess;
     GemmArgs ga;
@@ -1296,7 +1336,8 @@ hipError_t launch_skinny(Plan &pl, const _Float16 *const *xh, float *part, hipSt
             part += static_cast<size_t>(d.splits) * pl.sb.M * d.N;
         }
     }
-    hipLaunchKernelGGL(skinny_kernel, dim3(pl.grid), dim3(64 * kSkWaves), 0, stream, sealed(pl.sb), ga);
+    hipLaunchKernelGGL(skinny_kernel<TB>, dim3(pl.grid), dim3(64 * (TB == 1 ? kSkWaves : kSk2Waves)), 0, stream,
+                       sealed(pl.sb), ga);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.partial_floats == 0) return err;
     return launch_split_sum(pl, stream);
@@ -1329,12 +1370,15 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     // Few tokens: the W stream dominates, small tiles (K split as needed)
     // keep every CU busy.
     const bool skinny = b.M <= kSkinnyMaxM;
-    const bool small = !skinny && b.M <= kSmallTileMaxM;
+    const bool skinny2 = kSkinny2 && !skinny && b.M <= kSk2MaxM;
+    const bool small = !skinny && !skinny2 && b.M <= kSmallTileMaxM;
     Plan pl;
-    const bool mid = !skinny && !small && b.M <= kMidTileMaxM;
+    const bool mid = !skinny && !skinny2 && !small && b.M <= kMidTileMaxM;
     bool narrow = false;
     if (skinny) {
         make_plan<SkinnyTile>(b, kSkinnySplit, pl);
+    } else if (skinny2) {
+        make_plan<SkinnyShape<2>>(b, kSkinny2Split, pl);
     } else if (small) {
         make_plan<SmallTile>(b, kSmallSplit, pl);
         narrow = pl.tiles < kNarrowBelow;
@@ -1381,7 +1425,8 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     if (err != hipSuccess) return err;
 
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
-    if (skinny) return launch_skinny(pl, xh, part, stream);
+    if (skinny) return launch_skinny<1>(pl, xh, part, stream);
+    if (skinny2) return launch_skinny<2>(pl, xh, part, stream);
     if (narrow) return launch_gemm<NarrowTile, kSmallWaves>(pl, xh, part, stream);
     if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);

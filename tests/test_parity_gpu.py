@@ -72,7 +72,10 @@ PREFILL_SHAPES = [(32, 128, 1024), (33, 130, 768), (64, 257, 512), (128, 64, 204
                   (513, 40, 4352), (600, 33, 12544),
                   # up to 32 tokens: W dequantized straight into the MFMA operands, K in
                   # chunks of four blocks (one block, a ragged last chunk, many chunks)
-                  (31, 1, 256), (20, 257, 4352), (25, 33, 8192), (18, 300, 1280), (32, 130, 2048)]
+                  (31, 1, 256), (20, 257, 4352), (25, 33, 8192), (18, 300, 1280), (32, 130, 2048),
+                  # 33..64 tokens: two 32-token blocks per dequantized weight, K in chunks of
+                  # eight blocks (three chunks, a 68-block row, ragged rows and tokens)
+                  (48, 97, 4352), (63, 300, 17408), (33, 257, 2304)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
