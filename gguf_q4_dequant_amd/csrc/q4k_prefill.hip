@@ -43,7 +43,7 @@ constexpr int kXcds = 8;
 template <int BM_, int BN_, int WM_, int WN_, int R_>
 struct Shape {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int R = R_;  // register ring: k-steps requested ahead of the LDS stage
+    static constexpr int R = R_;  // k-steps of loads in flight ahead of the LDS stage
     static constexpr int kThreads = 2 * BN;
     static constexpr int kWaves = kThreads / 64;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -53,8 +53,7 @@ struct Shape {
     static constexpr size_t kLds = 2 * static_cast<size_t>(BM + BN) * 8 * 16;  // two buffers
     static_assert(WM * WN == kWaves && TA >= 1 && TB >= 1, "wave grid");
     static_assert(XC >= 1 && (BM * 8) % kThreads == 0, "x loader");
-    static_assert(R == 1 || R % 4 == 0, "ring: one step, or whole 256-deep blocks");
-    static_assert(R == 1 || (TA == 1 && TB == 1), "ring pipeline: one MFMA block per wave");
+    static_assert(R == 1, "one step of loads in flight");
 };
 // Many tokens: 256x256 tiles, eight waves of 128x64, loads one step ahead.
 using BigTile = Shape<256, 256, 2, 4, 1>;
@@ -67,22 +66,8 @@ using BigTile = Shape<256, 256, 2, 4, 1>;
 // (147 -> 184 us at M = 160, 128x256 tiles).
 using MidTile = Shape<128, 128, 2, 2, 1>;
 constexpr int kMidTileMaxM = 128;
-// Few tokens (the W stream dominates and the output tiles alone would leave
-// about one wave per SIMD): 32x128 tiles, four waves of 32x32, loads four
-// steps (one block) ahead, at most 168 VGPRs so that three waves share a
-// SIMD.  (Eight steps ahead, with the kernel rounding float32 x itself,
-// needs 233 VGPRs, two waves per SIMD: Qwen3-14B-shaped layer at M = 32 and
-// 64 109 and 197 us, against 98 and 165 us.)
-using SmallTile = Shape<32, 128, 1, 4, 4>;
-// The same with 64-row W tiles (two waves), twice the workgroups, for
-// batches whose 32x128 tiles would not fill three workgroups per CU
-// (Llama-3.2-3B-shaped pass at M = 32: 1100 -> 1050..1090 us; on the
-// Qwen3-14B layer, with enough tiles, it would lose: 98 -> 106 us).  Every output sums its
-// k in the same order on both shapes, so they agree bit for bit.
-using NarrowTile = Shape<32, 64, 1, 2, 4>;
-constexpr int kSmallTileMaxM = 64;
-constexpr int kSmallWaves = 3;  // waves per SIMD (launch bound) of both
-constexpr int kNarrowBelow = kSmallWaves * 256;  // 32x128 tiles in the batch
+// (32x128 and 32x64 tiles, four steps of loads in flight, served 33..64
+// tokens until the skinny kernel took two token blocks; see skinny_kernel.)
 
 // Split K: a problem whose K/256 exceeds `above` is cut into
 // ceil(K/256 / chunk) near-equal chunks, one workgroup each; a second kernel
@@ -92,9 +77,6 @@ constexpr int kNarrowBelow = kSmallWaves * 256;  // 32x128 tiles in the batch
 struct SplitRule {
     int chunk, above;
 };
-// Small tiles: chunks of at most 8 blocks, so that long and short K even out
-// and CUs hold several workgroups.
-constexpr SplitRule kSmallSplit = {8, 0};
 // 256x256 tiles, up to 512 tokens (at most two tile rows, so fewer output
 // tiles than twice the CUs): rows longer than 16 blocks are cut into chunks of
 // at most 16, so that no tile is much longer than a K = 4096 one (Qwen3-8B
@@ -346,14 +328,10 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
              : W + (static_cast<size_t>(vrow) * KB + kb0) * kBlockBytes;
 
     const int steps = kbn * 4;
-    // Raw data of the next step, loaded while the current one runs on the
-    // matrix cores (named registers: arrays of these end up in scratch).
-    // Register ring of R slots: slot r holds the raw data of a k-step s with
-    // s % R == r.  Slot indices are compile-time (the step loop is unrolled
-    // by R), and with R a multiple of 4 so is the quant group s % 4 of a slot.
-    // Requests past the last step re-read the last step (clamped address,
-    // never used): the loads stay unconditional, so the waits before a slot
-    // is used count only the newer requests.
+    // Raw data of the next step (one register slot), loaded while the current
+    // one runs on the matrix cores.  Requests past the last step re-read the
+    // last step (clamped address, never used): the loads stay unconditional,
+    // so the waits before the slot is used count only the newer requests.
     constexpr int R = S::R;
     uint4 xr[R][S::XC];
     uint4 wq[R], whd[R];
@@ -367,17 +345,16 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
         const int s = min(s_req, steps - 1);
         const int kb = s >> 2;
         const uint8_t *blk = wrow + static_cast<size_t>(kb) * kBlockBytes;
-        if (R == 1 || r % 4 == 0) whd[r] = *reinterpret_cast<const uint4 *>(blk);  // used when g == 0
+        whd[r] = *reinterpret_cast<const uint4 *>(blk);
         wq[r] = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * (s & 3) + 16 * wh);
     };
     auto load_stage = [&](int r, int s_req) {
         load_x(r, s_req);
         load_w(r, s_req);
     };
-    // g: quant group of the step in slot r.  With a ring (R > 1) it is
-    // compile-time and the header is decoded once per block; with one slot it
-    // is a runtime value and the header (loaded with every step) is decoded
-    // every step, so that the step has no branch.
+    // g: quant group of the step in the slot, a runtime value; the header
+    // (loaded with every step) is decoded every step, so that the step has no
+    // branch.
     auto store_x = [&](int r, uint4 *A) {
 #pragma unroll
         for (int j = 0; j < S::XC; ++j) A[swz((t >> 3) + S::XROWS * j, t & 7)] = xr[r][j];
@@ -389,7 +366,7 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
         float a_lo, a_hi, c_lo, c_hi;
     };
     auto group_scales = [&](int r, int g) {
-        if (R == 1 || g == 0) decode_header(whd[r], rs);
+        decode_header(whd[r], rs);
         const uint32_t scw = g < 2 ? rs.scA : rs.scB;
         const uint32_t mnw = g < 2 ? rs.mnA : rs.mnB;
         const int sh = (g & 1) * 16;
@@ -441,41 +418,8 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
 #pragma unroll
     for (int r = 1; r <= R; ++r) load_stage(r % R, r);
     __syncthreads();
-    // Few-token tiles (one 32x32 block per wave): every fragment of the step
-    // is requested from LDS first, the next step is dequantized while they
-    // arrive, and the MFMAs alternate between two accumulators so that
-    // consecutive ones do not wait on each other.
-    float16v acc2[S::TA][S::TB];
-    if constexpr (S::R > 1) {
-#pragma unroll
-        for (int a = 0; a < S::TA; ++a)
-#pragma unroll
-            for (int b = 0; b < S::TB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc2[a][b][r] = 0.f;
-    }
-    auto step = [&](int s, int d) {  // d = s % R, compile-time
-        const uint4 *A = As(d & 1), *B = Bs(d & 1);
-        half8 af[kBK / 16], bf[kBK / 16];
-#pragma unroll
-        for (int q = 0; q < kBK / 16; ++q) {
-            const int c = 2 * q + (lane >> 5);
-            af[q] = __builtin_bit_cast(half8, A[swz(S::TM * wm + (lane & 31), c)]);
-            bf[q] = __builtin_bit_cast(half8, B[swz(S::TN * wn + (lane & 31), c)]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the three phases in this order
-        store_stage((d + 1) % R, (d + 1) & 3, As((d + 1) & 1), Bs((d + 1) & 1));  // past the end: unused
-        load_stage((d + 1) % R, s + 1 + R);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < kBK / 16; q += 2) {
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q], bf[q], acc[0][0], 0, 0, 0);
-            acc2[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q + 1], bf[q + 1], acc2[0][0], 0, 0, 0);
-        }
-        __syncthreads();
-    };
     int s0 = 0;
-    if constexpr (R == 1) {
+    {
         // One slot, loads one step ahead.  Each step is straight-line code:
         // loads past the end re-read the last step and the store after the
         // last step fills the idle buffer (never read).
@@ -495,7 +439,7 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
             B[swz(wr, v)] = make_uint4(p.lo01, p.lo23, q.lo01, q.lo23);
             B[swz(wr, 4 + v)] = make_uint4(p.hi01, p.hi23, q.hi01, q.hi23);
         };
-        static_assert(R > 1 || ((S::TA == 4 || S::TA == 2) && S::TB == 2), "phased step: 4 or 2 x 2 blocks per wave");
+        static_assert((S::TA == 4 || S::TA == 2) && S::TB == 2, "phased step: 4 or 2 x 2 blocks per wave");
         for (; s0 < steps; ++s0) {
             const uint4 *A = As(s0 & 1), *B = Bs(s0 & 1);
             uint4 *An = As((s0 + 1) & 1), *Bn = Bs((s0 + 1) & 1);
@@ -554,25 +498,8 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
             mfma2(af1, bf1, 3);
             __syncthreads();
         }
-    } else {
-        for (; s0 + R <= steps; s0 += R) {
-#pragma unroll
-            for (int d = 0; d < R; ++d) step(s0 + d, d);
-        }
-        // Tail: whole blocks of four steps (steps is a multiple of 4).
-#pragma unroll
-        for (int d0 = 0; d0 < R; d0 += 4) {
-            if (s0 + d0 < steps) {
-#pragma unroll
-                for (int d = d0; d < d0 + 4; ++d) step(s0 + d, d);
-            }
-        }
     }
 
-    if constexpr (S::R > 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc2[0][0][r];
-    }
     // D layout of a 32x32 MFMA tile: lane l, register r ->
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
     auto for_each_out = [&](auto &&f) {
@@ -1371,18 +1298,12 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     // keep every CU busy.
     const bool skinny = b.M <= kSkinnyMaxM;
     const bool skinny2 = kSkinny2 && !skinny && b.M <= kSk2MaxM;
-    const bool small = !skinny && !skinny2 && b.M <= kSmallTileMaxM;
     Plan pl;
-    const bool mid = !skinny && !skinny2 && !small && b.M <= kMidTileMaxM;
-    bool narrow = false;
+    const bool mid = !skinny && !skinny2 && b.M <= kMidTileMaxM;
     if (skinny) {
         make_plan<SkinnyTile>(b, kSkinnySplit, pl);
     } else if (skinny2) {
         make_plan<SkinnyShape<2>>(b, kSkinny2Split, pl);
-    } else if (small) {
-        make_plan<SmallTile>(b, kSmallSplit, pl);
-        narrow = pl.tiles < kNarrowBelow;
-        if (narrow) make_plan<NarrowTile>(b, kSmallSplit, pl);
     } else if (mid)
         make_plan<MidTile>(b, kMidSplit, pl);
     else if (kProducerConsumer)
@@ -1427,8 +1348,6 @@ hipError_t launch_prefill(Batch &b, hipStream_t stream) {
     for (int i = 0; i < b.count; ++i) xh[i] = xh_base + offs[which[i]];
     if (skinny) return launch_skinny<1>(pl, xh, part, stream);
     if (skinny2) return launch_skinny<2>(pl, xh, part, stream);
-    if (narrow) return launch_gemm<NarrowTile, kSmallWaves>(pl, xh, part, stream);
-    if (small) return launch_gemm<SmallTile, kSmallWaves>(pl, xh, part, stream);
     if (mid) return launch_gemm<MidTile, 2>(pl, xh, part, stream);
     if (kProducerConsumer) return launch_pc<kPcBN>(pl, xh, part, stream);
     return launch_gemm<BigTile, 2>(pl, xh, part, stream);

@@ -132,7 +132,7 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
     (DEC, 9, (5, 7), False),      # 9 tokens against chunks of 5 and 2: two layouts, same values to rounding
     (DEC, 4, (2, 3), False),      # single-token chunks run the sixteen-wave kernel: same values to rounding
     (DEC, 9, (5, 6), False),
-    (PRE, 9, (5, 6), True),       # chunks of up to 64 tokens: small tiles, same K chunks
+    (PRE, 9, (5, 6), True),       # chunks of up to 32 tokens: one skinny kernel, same K chunks
     (PRE, 200, (66, 133), True),  # 128- and 256-row tiles: same K chunks, same k order
     (PRE, 200, (130, 131), False),  # mixes both tile shapes (different k order): same values to rounding
     (GEMV, 9, (5, 6), True),      # one K split for every token count: identical bits
@@ -140,7 +140,7 @@ def test_golden_blocks_through_gpu(golden_blocks, path):
 ])
 def test_row_split_invariance(path, M, cuts, bitwise):
     """An M-row call equals calls on row chunks (the nx runner's mixed-chunk gates)."""
-    N, K = (140, 2304) if path == PRE else (140, 1536)  # prefill: small tiles cut K in two
+    N, K = (140, 2304) if path == PRE else (140, 1536)  # prefill: K cut into chunks
     w, x = _inputs(M, N, K, 4)
     y = _run(w, x, N, path)
     bounds = (0,) + cuts + (M,)
@@ -260,13 +260,12 @@ def test_batch_of_32_problems(M):
 
 
 @pytest.mark.parametrize("M", [17, 32, 64])
-def test_small_tile_shapes_agree(M):
-    """Up to 64 tokens the prefill family uses 32x128 tiles, or 32x64 tiles
-    when a batch has fewer than 768 of the larger ones.  Three K = 4096
-    problems of about 16384 rows (ragged N: 256 large tiles each, the last one
-    short) go through one batched call (32x128) and through three single calls
-    (32x64 each): every output must agree bit for bit, and sampled columns,
-    the last ones included, match the oracle."""
+def test_skinny_large_batch_equals_single_calls(M):
+    """Up to 64 tokens (the skinny kernel, one or two 32-token blocks): three
+    K = 4096 problems of about 16384 rows (ragged N, the last tile short) go
+    through one batched call and through three single calls: every output
+    must agree bit for bit, and sampled columns, the last ones included,
+    match the oracle."""
     import torch
     K = 4096
     Ns = (16347, 16384, 16291)
