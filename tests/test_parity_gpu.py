@@ -50,7 +50,13 @@ DECODE_SHAPES = [(1, 1024, 1024), (1, 1, 256), (1, 17, 256), (1, 65, 2048), (1, 
                  (14, 70, 6400), (9, 40, 12544),
                  # 2..4 tokens on the one-token structure: one-block rows (a tile per wave),
                  # a single row, long rows split over sixteen waves
-                 (4, 33, 256), (3, 1, 512), (2, 97, 17408)]
+                 (4, 33, 256), (3, 1, 512), (2, 97, 17408),
+                 # one token, eight waves per tile with KB = 8q + r blocks, r = 1..5 (the
+                 # first r waves take a lone last block): two tiles per sixteen-wave
+                 # workgroup, and eight-wave workgroups over several rounds with q = 2
+                 # and q = 3
+                 (1, 100, 2304), (1, 97, 2816), (1, 130, 3072), (1, 33, 3328),
+                 (1, 16416, 5120), (1, 16416, 7168)]
 
 
 @pytest.mark.parametrize("path", [DEC, GEMV])
