@@ -156,17 +156,17 @@ __global__ __launch_bounds__(kCvtThreads) void convert_x_kernel(CvtBatch cb) {
     auto amax4 = [](float m, float4 v) {
         return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
     };
-    // The row's largest magnitude (NaN compares false and is ignored).
+    // The row's largest magnitude (NaN compares false and is ignored).  Every
+    // load is requested before any maximum is taken (a load past the row
+    // re-reads its last float4 and is not used): with the maximum inside the
+    // bounds test, each load waited for the one before it.
     float4 v[kCvtRegs];
     float mx = 0.f;
 #pragma unroll
-    for (int j = 0; j < kCvtRegs; ++j) {
-        const int f = t + kCvtThreads * j;
-        if (f < n4) {
-            v[j] = src[f];
-            mx = amax4(mx, v[j]);
-        }
-    }
+    for (int j = 0; j < kCvtRegs; ++j) v[j] = src[min(t + kCvtThreads * j, n4 - 1)];
+#pragma unroll
+    for (int j = 0; j < kCvtRegs; ++j)
+        if (t + kCvtThreads * j < n4) mx = amax4(mx, v[j]);
     for (int f = t + kCvtThreads * kCvtRegs; f < n4; f += kCvtThreads) mx = amax4(mx, src[f]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
