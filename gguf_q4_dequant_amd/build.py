@@ -18,6 +18,8 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-kernel resource remarks, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 # Per source file: MFMA results in ordinary VGPRs for the small-M decode
 # kernels, which scale every result with VALU instructions (results kept in
@@ -33,15 +35,29 @@ def sources():
 
 
 def _run(cmd, verbose):
+    """Run hipcc; return the kernels whose code needs scratch memory."""
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature and says so.
-    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l]
+    remarks = [l for l in lines if "[-Rpass-analysis=kernel-resource-usage]" in l]
+    out = "\n".join(l for l in lines if "-Rpass-analysis" not in l and not l.startswith(("   ", "      |")))
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
     if out.strip() and verbose:
         print(out)
+    # Every kernel must run without scratch memory: the runtime sets scratch
+    # up per queue on the first launch that needs it, which allocates device
+    # memory inside a call that promises to allocate none.
+    scratch, name = [], None
+    for l in remarks:
+        body = l.split("remark:", 1)[-1].replace("[-Rpass-analysis=kernel-resource-usage]", "").strip()
+        if body.startswith("Function Name:"):
+            name = body.split(":", 1)[1].strip()
+        elif body.startswith("ScratchSize") and name and int(body.rsplit(":", 1)[1]) > 0:
+            scratch.append(f"{name} ({body})")
+    return scratch
 
 
 def build(verbose: bool = False) -> str:
@@ -58,9 +74,12 @@ def build(verbose: bool = False) -> str:
             extra = EXTRA_FLAGS.get(os.path.basename(src), [])
             jobs.append((obj, [hipcc, *HIPCC_FLAGS, *extra, "-c", "-o", obj, src]))
         workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+        scratch = []
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
             for f in [pool.submit(_run, cmd, verbose) for _, cmd in jobs]:
-                f.result()
+                scratch += f.result()
+        if scratch:
+            raise RuntimeError("kernels that need scratch memory: " + "; ".join(scratch))
         _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in jobs]], verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY

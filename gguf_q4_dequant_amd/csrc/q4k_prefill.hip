@@ -121,6 +121,28 @@ __host__ __device__ inline size_t xh_copy_halves(int M, int K) {
     return xh_halves(M, K) + ((2 * static_cast<size_t>(M) + 127) & ~static_cast<size_t>(127));
 }
 
+// The factors of the rows that one lane's accumulators of a 32x32 MFMA tile
+// hold (register r: row r0 + 8*(r/4) + r%4, r0 = the tile's first row +
+// 4*(lane/32)): four 16-byte loads requested together.  Rows past M read
+// the copy's last whole group of four (inside its padding) and are never
+// stored.  (Read one by one next to each store, every factor cost the wave a
+// wait of its own.)
+__device__ __forceinline__ float4 row_factors4(const float *__restrict__ xfac, int M, int r) {
+    return *reinterpret_cast<const float4 *>(xfac + min(r, (M - 1) & ~3));  // r: a multiple of 4
+}
+__device__ __forceinline__ void row_factors(const float *__restrict__ xfac, int M, int r0, float (&f)[16]) {
+    float4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = row_factors4(xfac, M, r0 + 8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f[4 * q] = v[q].x;
+        f[4 * q + 1] = v[q].y;
+        f[4 * q + 2] = v[q].z;
+        f[4 * q + 3] = v[q].w;
+    }
+}
+
 struct CvtSeg {
     const float *src;  // [M, K] f32
     _Float16 *dst;     // the copy, laid out as above
@@ -501,23 +523,29 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
     }
 
     // D layout of a 32x32 MFMA tile: lane l, register r ->
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  f gets each output's
+    // index and its value with x's per-row scaling undone (a power of two:
+    // exact).
+    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
     auto for_each_out = [&](auto &&f) {
 #pragma unroll
         for (int a = 0; a < S::TA; ++a) {
 #pragma unroll
-            for (int b = 0; b < S::TB; ++b) {
-                const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+            for (int q = 0; q < 4; ++q) {  // rows r0 + 8q .. r0 + 8q + 3 (registers 4q .. 4q + 3)
+                const int r0 = tm0 + S::TM * wm + 32 * a + 8 * q + 4 * (lane >> 5);
+                const float4 fac = row_factors4(xfac, M, r0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, m, acc[a][b][r]);
+                for (int b = 0; b < S::TB; ++b) {
+                    const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+                    const float v[4] = {acc[a][b][4 * q] * fac.x, acc[a][b][4 * q + 1] * fac.y,
+                                        acc[a][b][4 * q + 2] * fac.z, acc[a][b][4 * q + 3] * fac.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r0 + i < M && n < N) f(static_cast<size_t>(r0 + i) * N + n, v[i]);
                 }
             }
         }
     };
-    // Undo the per-row scaling of x (a power of two: exact).
-    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
     if (P.w2 && splits == 1) {
         // Gate/up pairs: columns c and c ^ 16 of a 32-column block are the
         // gate and up rows of one output, held by lanes l and l ^ 16 in the
@@ -528,14 +556,16 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
         const bool up = (lane & 16) != 0;
 #pragma unroll
         for (int a = 0; a < S::TA; ++a) {
+            float fac[16];
+            row_factors(xfac, M, tm0 + S::TM * wm + 32 * a + 4 * (lane >> 5), fac);
 #pragma unroll
             for (int b = 0; b < S::TB; ++b) {
                 const int n = ((tn0 + S::TN * wn + 32 * b) >> 1) + (lane & 15);
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const int m0 = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float v0 = acc[a][b][r] * xfac[min(m0, M - 1)];
-                    const float v1 = acc[a][b][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float v0 = acc[a][b][r] * fac[r];
+                    const float v1 = acc[a][b][r + 1] * fac[r + 1];
                     const float got = __shfl_xor(up ? v0 : v1, 16);
                     const int m = up ? m0 + 1 : m0;
                     if (m < M && n < n_out)
@@ -546,7 +576,7 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
         return;
     }
     if (splits == 1) {
-        for_each_out([&](size_t e, int m, float v) { P.y[e] = v * xfac[m]; });
+        for_each_out([&](size_t e, float v) { P.y[e] = v; });
         return;
     }
     // Split K: store this chunk's partial tile ([splits][M][N] in the
@@ -555,7 +585,7 @@ __global__ __launch_bounds__(S::kThreads, WAVES_PER_EU) void prefill_kernel(Batc
     // release it needs writes back the whole L2 of its XCD each time, which
     // costs far more than the second launch.)
     float *part = P.part + static_cast<size_t>(sidx) * M * N;
-    for_each_out([&](size_t e, int m, float v) { part[e] = v * xfac[m]; });
+    for_each_out([&](size_t e, float v) { part[e] = v; });
 }
 
 // ---- many tokens, producer and consumer waves ------------------------------
@@ -762,35 +792,44 @@ __global__ __launch_bounds__(PcShape<BN>::kThreads) void prefill_pc_kernel(Batch
     }
 
     // D layout of a 32x32 MFMA tile: lane l, register r ->
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  f gets each output's
+    // index and its value with x's per-row scaling undone (a power of two:
+    // exact).
+    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
     auto for_each_out = [&](auto &&f) {
 #pragma unroll
         for (int a = 0; a < S::TA; ++a) {
 #pragma unroll
-            for (int b = 0; b < S::TB; ++b) {
-                const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+            for (int q = 0; q < 4; ++q) {  // rows r0 + 8q .. r0 + 8q + 3 (registers 4q .. 4q + 3)
+                const int r0 = tm0 + S::TM * wm + 32 * a + 8 * q + 4 * (lane >> 5);
+                const float4 fac = row_factors4(xfac, M, r0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < M && n < N) f(static_cast<size_t>(m) * N + n, m, acc[a][b][r]);
+                for (int b = 0; b < S::TB; ++b) {
+                    const int n = tn0 + S::TN * wn + 32 * b + (lane & 31);
+                    const float v[4] = {acc[a][b][4 * q] * fac.x, acc[a][b][4 * q + 1] * fac.y,
+                                        acc[a][b][4 * q + 2] * fac.z, acc[a][b][4 * q + 3] * fac.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r0 + i < M && n < N) f(static_cast<size_t>(r0 + i) * N + n, v[i]);
                 }
             }
         }
     };
-    const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
     if (P.w2 && splits == 1) {
         const int n_out = P.n_out;
         const bool up = (lane & 16) != 0;
 #pragma unroll
         for (int a = 0; a < S::TA; ++a) {
+            float fac[16];
+            row_factors(xfac, M, tm0 + S::TM * wm + 32 * a + 4 * (lane >> 5), fac);
 #pragma unroll
             for (int b = 0; b < S::TB; ++b) {
                 const int n = ((tn0 + S::TN * wn + 32 * b) >> 1) + (lane & 15);
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const int m0 = tm0 + S::TM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float v0 = acc[a][b][r] * xfac[min(m0, M - 1)];
-                    const float v1 = acc[a][b][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float v0 = acc[a][b][r] * fac[r];
+                    const float v1 = acc[a][b][r + 1] * fac[r + 1];
                     const float got = __shfl_xor(up ? v0 : v1, 16);
                     const int m = up ? m0 + 1 : m0;
                     if (m < M && n < n_out)
@@ -801,11 +840,11 @@ __global__ __launch_bounds__(PcShape<BN>::kThreads) void prefill_pc_kernel(Batch
         return;
     }
     if (splits == 1) {
-        for_each_out([&](size_t e, int m, float v) { P.y[e] = v * xfac[m]; });
+        for_each_out([&](size_t e, float v) { P.y[e] = v; });
         return;
     }
     float *part = P.part + static_cast<size_t>(sidx) * M * N;
-    for_each_out([&](size_t e, int m, float v) { part[e] = v * xfac[m]; });
+    for_each_out([&](size_t e, float v) { part[e] = v; });
 }
 
 // y = sum over chunks of the partial sums, in chunk order, for split problems
@@ -1083,6 +1122,9 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
     // 8*(r/4) + 4*(l/32) + r%4, W row (tile's first) + l%32.  x's per-row
     // factor undone.
     const float *__restrict__ xfac = reinterpret_cast<const float *>(XH + xh_halves(M, K));
+    float fac[TB][16];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) row_factors(xfac, M, 32 * u + 4 * (lane >> 5), fac[u]);
     if (P.w2 && splits == 1) {
         const int n_out = P.n_out;
         const bool up = (lane & 16) != 0;
@@ -1094,8 +1136,8 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const int m0 = 32 * u + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float v0 = acc[tt][u][r] * xfac[min(m0, M - 1)];
-                    const float v1 = acc[tt][u][r + 1] * xfac[min(m0 + 1, M - 1)];
+                    const float v0 = acc[tt][u][r] * fac[u][r];
+                    const float v1 = acc[tt][u][r + 1] * fac[u][r + 1];
                     const float got = __shfl_xor(up ? v0 : v1, 16);
                     const int m = up ? m0 + 1 : m0;
                     if (m < M && n < n_out)
@@ -1114,7 +1156,7 @@ void skinny_kernel(Batch bt, GemmArgs ga) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * u + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N) dst[static_cast<size_t>(m) * N + n] = acc[tt][u][r] * xfac[m];
+                if (m < M && n < N) dst[static_cast<size_t>(m) * N + n] = acc[tt][u][r] * fac[u][r];
             }
         }
     }
