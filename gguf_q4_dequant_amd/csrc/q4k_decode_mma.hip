@@ -140,6 +140,30 @@ __device__ __forceinline__ void block_scales(const uint4 hd, float dsc[8], float
     }
 }
 
+// The scales of one super-block for the 9..16-token kernel: dsc[j] as in
+// block_scales, ndm = -32 * dmin (see mma_block_rows), and the 6-bit mins
+// m_0..m_7 as binary16 subnormals m_j * 2^-24 (a 16-bit lane holding the
+// small integer m_j is exactly that subnormal), k order j, for a matrix-core
+// operand.
+__device__ __forceinline__ void block_scales_mins(const uint4 hd, float dsc[8], float &ndm, uint4 &mq) {
+    const float d = half_bits_to_float(hd.x & 0xFFFFu);
+    const float d16 = d * 0.0625f;
+    ndm = -32.0f * half_bits_to_float(hd.x >> 16);
+    const uint32_t scA = hd.y & 0x3F3F3F3Fu, mnA = hd.z & 0x3F3F3F3Fu;
+    const uint32_t scB = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t mnB = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dsc[j] = ((j & 1) ? d16 : d) * static_cast<float>((scA >> (8 * j)) & 0xFFu);
+        dsc[4 + j] = ((j & 1) ? d16 : d) * static_cast<float>((scB >> (8 * j)) & 0xFFu);
+    }
+    // bytes (m0, m1, m2, m3) -> 16-bit lanes (m0, m1) and (m2, m3)
+    mq.x = (mnA & 0xFFu) | ((mnA & 0xFF00u) << 8);
+    mq.y = ((mnA >> 16) & 0xFFu) | ((mnA >> 8) & 0xFF0000u);
+    mq.z = (mnB & 0xFFu) | ((mnB & 0xFF00u) << 8);
+    mq.w = ((mnB >> 16) & 0xFFu) | ((mnB >> 8) & 0xFF0000u);
+}
+
 // One parked super-block of 32 rows times the staged activations.  rb points
 // at this lane's row (col) in the staging slot; xs/xsum are the staged
 // activations with jj0 the block's first sub-block, mul_t[i][jj0/8] the factor
@@ -208,16 +232,25 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // lo; B the quants of 16 rows of W; the hi and the lo product accumulate in
 // the same C, so no per-token hi + lo sum is needed.  Lane l owns tokens
 // 4*(l/16) + r (r < 4) of rows n0 + l%16 (acc[r]) and n0 + 16 + l%16
-// (acc[4 + r]).  xs/xsum/xmul are the staged pass with jj0 the block's first
-// sub-block and CB8 = 8 * (blocks per pass) the per-token stride of the sums
-// and factors.
-__device__ __forceinline__ void mma_block_rows(const uint8_t *slot, const uint4 *xs, const float *xsum,
+// (acc[4 + r]).  xs is the staged pass with jj0 the block's first sub-block;
+// xm holds, per block of the pass, each token's eight sub-block sums scaled
+// by 2^(e-6) (2^e: the block's activation scale) as a binary16 hi and lo
+// part (xm[((bo*2 + part)*16 + token)], 8 halves in sub-block order); xmul
+// the per-token factors 2^(24-e) with CB8 = 8 * (blocks per pass) the
+// per-token stride.
+//   The min terms dmin * sum_j m_j * X_j are a product too: one more MFMA
+// per 16 rows, A = the sums (k-quarters 0 and 2 the hi parts, 1 and 3 the
+// lo parts, so each part enters twice), B = m_j * 2^-24 in every quarter.
+// Its C is 2 * 2^-24 * 2^(e-6) * sum_j m_j X_j = 2^-5 * 2^(e-24) * ..., so
+// the block adds mul * (blk - 32 * dmin * C) with mul = 2^(24-e).
+__device__ __forceinline__ void mma_block_rows(const uint8_t *slot, const uint4 *xs, const uint4 *xm,
                                                const float *xmul, int M, int CB8, int lane, int jj0,
                                                float acc[8]) {
     const int c16 = lane & 15, quarter = lane >> 4;
-    float dsc0[8], dm0[8], dsc1[8], dm1[8];
-    block_scales(*reinterpret_cast<const uint4 *>(slot + c16 * kBlockBytes), dsc0, dm0);
-    block_scales(*reinterpret_cast<const uint4 *>(slot + (16 + c16) * kBlockBytes), dsc1, dm1);
+    float dsc0[8], dsc1[8], ndm0, ndm1;
+    uint4 mq0, mq1;
+    block_scales_mins(*reinterpret_cast<const uint4 *>(slot + c16 * kBlockBytes), dsc0, ndm0, mq0);
+    block_scales_mins(*reinterpret_cast<const uint4 *>(slot + (16 + c16) * kBlockBytes), dsc1, ndm1, mq1);
     const uint8_t *ra = slot + c16 * kBlockBytes + 16 + 8 * quarter;
     const uint8_t *rc = ra + 16 * kBlockBytes;
     // this lane's A fragment of sub-block jj, part h (0 hi, 1 lo): xa[(jj*2 + h) * 64]
@@ -269,21 +302,20 @@ __device__ __forceinline__ void mma_block_rows(const uint8_t *slot, const uint4 
     issue(2, ca);
     scale(1, cb);
     issue(3, cb);
+    // the min terms (see above)
+    const int bo = jj0 >> 3;
+    const half8 am = __builtin_bit_cast(half8, xm[(bo * 2 + (quarter & 1)) * 16 + min(c16, M - 1)]);
+    const float4v zm = {0.f, 0.f, 0.f, 0.f};
+    const float4v cm0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, __builtin_bit_cast(half8, mq0), zm, 0, 0, 0);
+    const float4v cm1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, __builtin_bit_cast(half8, mq1), zm, 0, 0, 0);
     scale(2, ca);
     scale(3, cb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int tt = min(4 * quarter + r, M - 1);
-        const float *sm = xsum + tt * CB8 + jj0;
-        float m0 = 0.f, m1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            m0 = __builtin_fmaf(dm0[j], sm[j], m0);
-            m1 = __builtin_fmaf(dm1[j], sm[j], m1);
-        }
-        const float mul = xmul[tt * CB8 + (jj0 >> 3)];
-        acc[r] = __builtin_fmaf(mul, blk0[r], acc[r]) - m0;
-        acc[4 + r] = __builtin_fmaf(mul, blk1[r], acc[4 + r]) - m1;
+        const float mul = xmul[tt * CB8 + bo];
+        acc[r] = __builtin_fmaf(mul, __builtin_fmaf(ndm0, cm0[r], blk0[r]), acc[r]);
+        acc[4 + r] = __builtin_fmaf(mul, __builtin_fmaf(ndm1, cm1[r], blk1[r]), acc[4 + r]);
     }
 }
 
@@ -294,11 +326,13 @@ __device__ __forceinline__ void mma_block_rows(const uint8_t *slot, const uint4 
 // of separate hi and lo operands, xs[((jj*2 + 0|1)*16 + tt)*4 + v].
 // The 32 lanes of one super-block (32 adjacent lanes, from jj%8 == 0, v == 0)
 // call it together: the scale 2^e puts the super-block's largest magnitude in
-// [2^14, 2^15).  The first lane of each sub-block writes its plain sum, the
+// [2^14, 2^15).  The first lane of each sub-block writes its sum (pair rows:
+// the plain fp32 sum at sums[tt*CB*8 + jj]; token rows: the sum times
+// 2^(e-6) as a binary16 hi and lo part, the layout mma_block_rows reads), the
 // first lane of the super-block the factor 2^(24-e) that undoes the scaling.
 template <bool kTokenRows>
-__device__ __forceinline__ void stage_group(const float4 a, const float4 b, int jj, int v, int tt, int M,
-                                            uint4 *xs, float *sum_t, float *mul_t) {
+__device__ __forceinline__ void stage_group(const float4 a, const float4 b, int jj, int v, int tt, int M, int CB,
+                                            uint4 *xs, float *sums, float *mul_t) {
     float xv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float mx = 0.f, sm = 0.f;
 #pragma unroll
@@ -336,7 +370,19 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
         xs[((jj * 2 + s) * R2 + 2 * tt) * 2 + hh] = __builtin_bit_cast(uint4, hv);
         xs[((jj * 2 + s) * R2 + 2 * tt + 1) * 2 + hh] = __builtin_bit_cast(uint4, lv);
     }
-    if (v == 0) sum_t[jj] = sm;
+    if constexpr (kTokenRows) {
+        // the sub-block sum times 2^(e-6) (below 2^14 in magnitude), as a
+        // binary16 hi and lo part for mma_block_rows
+        if (v == 0) {
+            const float xs6 = sm * __uint_as_float(static_cast<uint32_t>(e + 121) << 23);
+            const _Float16 h = static_cast<_Float16>(xs6);
+            _Float16 *xm = reinterpret_cast<_Float16 *>(sums);
+            xm[(((jj >> 3) * 2 + 0) * 16 + tt) * 8 + (jj & 7)] = h;
+            xm[(((jj >> 3) * 2 + 1) * 16 + tt) * 8 + (jj & 7)] = static_cast<_Float16>(xs6 - static_cast<float>(h));
+        }
+    } else {
+        if (v == 0) sums[tt * CB * 8 + jj] = sm;
+    }
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
 
@@ -379,8 +425,8 @@ __global__ __launch_bounds__(256) void prestage_kernel(StageBatch sb) {
     uint8_t *img = S.img + static_cast<size_t>(c) * stage_bytes(M, CB);
     float *xsum = reinterpret_cast<float *>(img + stage_rows(M) * CB * 1024);
     float *xmul = xsum + stage_rows(M) * CB * 8;
-    stage_group<kTokenRows>(src[0], src[1], jj, v, tt, M, reinterpret_cast<uint4 *>(img), xsum + tt * CB * 8,
-                xmul + tt * CB * 8);
+    stage_group<kTokenRows>(src[0], src[1], jj, v, tt, M, CB, reinterpret_cast<uint4 *>(img), xsum,
+                            xmul + tt * CB * 8);
 }
 
 // NP: C register pairs that hold tokens (2 for M <= 4, 4 for M <= 8); 8 (9..16
@@ -554,7 +600,7 @@ void decode_mma_kernel(Batch bt) {
     // One super-block from the staging area; bo = its index within the pass.
     auto consume = [&](int bo) {
         if constexpr (NP == 8)
-            mma_block_rows(wst, xs, xsum, xmul, M, CB * 8, lane, bo * 8, acc);
+            mma_block_rows(wst, xs, reinterpret_cast<const uint4 *>(xsum), xmul, M, CB * 8, lane, bo * 8, acc);
         else
             mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
     };
