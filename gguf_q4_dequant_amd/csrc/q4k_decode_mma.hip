@@ -165,16 +165,22 @@ __device__ __forceinline__ void block_scales_mins(const uint4 hd, float dsc[8], 
 }
 
 // One parked super-block of 32 rows times the staged activations.  rb points
-// at this lane's row (col) in the staging slot; xs/xsum are the staged
-// activations with jj0 the block's first sub-block, mul_t[i][jj0/8] the factor
-// that undoes token tok[i]'s scaling of this block; token tok[i]'s result for
-// row col is added to acc[i] (i < NP; see the C-register layout below).
+// at this lane's row (col) in the staging slot; xs is the staged pass with
+// jj0 the block's first sub-block, mul_t[i][jj0/8] the factor that undoes
+// token tok[i]'s scaling of this block; token tok[i]'s result for row col is
+// added to acc[i] (i < NP; see the C-register layout below).  xm holds, per
+// block of the pass, each token's eight sub-block sums times 2^(e-6) as a
+// binary16 hi part (A row 2t) and lo part (A row 2t + 1), xm[bo*R2 + row], 8
+// halves in sub-block order; the min terms are one more MFMA with these rows
+// as A (both k-halves, so each part enters twice) and the mins m_j * 2^-24
+// as B, whose C rows 2t and 2t + 1 add up to 2^-23 * 2^(e-6) * sum_j m_j X_j
+// (see mma_block_rows).
 template <int NP>
 __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, int R2, int arow, int half,
-                                          int jj0, const float *const mul_t[NP], const float *const sum_t[NP],
-                                          float acc[NP]) {
-    float dsc[8], dm[8];
-    block_scales(*reinterpret_cast<const uint4 *>(rb), dsc, dm);
+                                          int jj0, const float *const mul_t[NP], const uint4 *xm, float acc[NP]) {
+    float dsc[8], ndm;
+    uint4 mq;
+    block_scales_mins(*reinterpret_cast<const uint4 *>(rb), dsc, ndm, mq);
     float blk[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) blk[i] = 0.f;
@@ -215,13 +221,15 @@ __device__ __forceinline__ void mma_block(const uint8_t *rb, const uint4 *xs, in
             blk[i] = __builtin_fmaf(dsc[2 * g + 1], chi[g][2 * i] + chi[g][2 * i + 1], blk[i]);
         }
     }
+    float16v zm;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        float mterm = 0.f;
+    for (int i = 0; i < 16; ++i) zm[i] = 0.f;
+    const int bo = jj0 >> 3;
+    const float16v cm = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, xm[bo * R2 + arow]),
+                                                              __builtin_bit_cast(half8, mq), zm, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mterm = __builtin_fmaf(dm[j], sum_t[i][jj0 + j], mterm);
-        acc[i] = __builtin_fmaf(mul_t[i][jj0 >> 3], blk[i], acc[i]) - mterm;
-    }
+    for (int i = 0; i < NP; ++i)
+        acc[i] = __builtin_fmaf(mul_t[i][bo], __builtin_fmaf(ndm, cm[2 * i] + cm[2 * i + 1], blk[i]), acc[i]);
 }
 
 typedef float float4v __attribute__((ext_vector_type(4)));
@@ -381,7 +389,15 @@ __device__ __forceinline__ void stage_group(const float4 a, const float4 b, int 
             xm[(((jj >> 3) * 2 + 1) * 16 + tt) * 8 + (jj & 7)] = static_cast<_Float16>(xs6 - static_cast<float>(h));
         }
     } else {
-        if (v == 0) sums[tt * CB * 8 + jj] = sm;
+        // pair rows: hi part in row 2tt, lo part in row 2tt + 1 of the block's
+        // 2M rows (mma_block)
+        if (v == 0) {
+            const float xs6 = sm * __uint_as_float(static_cast<uint32_t>(e + 121) << 23);
+            const _Float16 h = static_cast<_Float16>(xs6);
+            _Float16 *xm = reinterpret_cast<_Float16 *>(sums);
+            xm[((jj >> 3) * 2 * M + 2 * tt) * 8 + (jj & 7)] = h;
+            xm[((jj >> 3) * 2 * M + 2 * tt + 1) * 8 + (jj & 7)] = static_cast<_Float16>(xs6 - static_cast<float>(h));
+        }
     }
     if (v == 0 && (jj & 7) == 0) mul_t[jj >> 3] = back;
 }
@@ -591,18 +607,16 @@ void decode_mma_kernel(Batch bt) {
     for (int i = 0; i < NP; ++i) tok[i] = min(4 * (i >> 1) + 2 * half + (i & 1), M - 1);
     const int arow = min(col, R2 - 1);
 
-    const float *mul_t[NP], *sum_t[NP];
+    const float *mul_t[NP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        mul_t[i] = xmul + tok[i] * CB * 8;
-        sum_t[i] = xsum + tok[i] * CB * 8;
-    }
+    for (int i = 0; i < NP; ++i) mul_t[i] = xmul + tok[i] * CB * 8;
     // One super-block from the staging area; bo = its index within the pass.
     auto consume = [&](int bo) {
         if constexpr (NP == 8)
             mma_block_rows(wst, xs, reinterpret_cast<const uint4 *>(xsum), xmul, M, CB * 8, lane, bo * 8, acc);
         else
-            mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t, sum_t, acc);
+            mma_block<NP>(wst + col * kBlockBytes, xs, R2, arow, half, bo * 8, mul_t,
+                          reinterpret_cast<const uint4 *>(xsum), acc);
     };
 
     // Pass c of the activations (super-blocks [c*CB, c*CB + CB) of every
