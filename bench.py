@@ -436,11 +436,17 @@ def swiglu_figures(q4k, dev, steps, warmup):
         fused = lambda st: q4k.matmul_swiglu(wg, wu, x, out=o, stream=st)
         if M == 1:
             n = len(pairs) * -(-32 // len(pairs))
-            ms_f = _time_replays(_capture(lambda st: [q4k.matmul_swiglu(*pairs[i % len(pairs)], x, out=o, stream=st)
-                                                      for i in range(n)]), steps, warmup) / n
+            gf = _capture(lambda st: [q4k.matmul_swiglu(*pairs[i % len(pairs)], x, out=o, stream=st) for i in range(n)])
             cp = [q4k.prepare_batched([(a, x, g), (b, x, u)]) for a, b in pairs]
-            ms_p = _time_replays(_capture(lambda st: [cp[i % len(cp)](st) for i in range(n)]), steps, warmup) / n
-            del cp
+            gp = _capture(lambda st: [cp[i % len(cp)](st) for i in range(n)])
+            # Timed twice in turn, the better of each kept: the first graph
+            # timed after the host has built the weights otherwise runs on a
+            # clock that is still rising (about 10% on one launch).
+            ms_f, ms_p = float("inf"), float("inf")
+            for _ in range(2):
+                ms_f = min(ms_f, _time_replays(gf, steps, warmup) / n)
+                ms_p = min(ms_p, _time_replays(gp, steps, warmup) / n)
+            del cp, gf, gp
         else:
             def eager(fn, reps=max(3, steps // 4)):
                 for _ in range(2):
